@@ -1,0 +1,379 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+Each check_* function raises AssertionError on a mismatch; the test_* functions
+run them on the oracle as written, and the mutation tests run them on an
+oracle with a planted mistake to show that the pins catch it.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle.mla_oracle as O
+from synth import CONFIGS, generate, hidden_recipe, sequence_rows, small
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TINY = CONFIGS["tiny_f32"]
+RNG = np.random.default_rng(1234)
+
+
+def rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300)
+
+
+def rand_case(n_h=3, d_h=8, d_c=24, d_r=4, L=5, seed=0):
+    r = np.random.default_rng(seed)
+    return dict(c=r.standard_normal((L, d_c)), k_rope=r.standard_normal((L, d_r)),
+                q_nope=r.standard_normal((n_h, d_h)), q_pe=r.standard_normal((n_h, d_r)),
+                w_uk=r.standard_normal((n_h * d_h, d_c)) / np.sqrt(d_c),
+                w_uv=r.standard_normal((n_h * d_h, d_c)) / np.sqrt(d_c))
+
+
+# ---------------------------------------------------------------------------
+# cache-size closed forms (the pages' own numbers)
+# ---------------------------------------------------------------------------
+def test_cache_size_closed_forms():
+    g = json.load(open(os.path.join(GOLDEN, "cache_size.json")))
+    for name in ("v2lite_b32_l4096", "v2_b64_l8192", "v2_varlen_b128", "v2_b8_l131072"):
+        cfg = CONFIGS[name]
+        assert cfg.d_latent == g["d_latent_over_d_head"] * cfg.d_head
+        assert cfg.d_rope == g["d_rope_over_d_head"] * cfg.d_head
+        assert cfg.d_latent + cfg.d_rope == g["per_token_elements_over_d_head"] * cfg.d_head == 576
+        # GQA with n_g groups caches 2 n_g d_h; equal to MLA's 4.5 d_h at n_g = 2.25
+        assert (cfg.d_latent + cfg.d_rope) / (2 * cfg.d_head) == g["gqa_equivalent_groups"]
+        assert (cfg.d_latent + cfg.d_rope) * 2 == 1152          # bytes per bf16 row
+    v2 = CONFIGS["v2_b64_l8192"]
+    assert 2 * v2.n_heads * v2.d_head == 32768                   # MHA per token per layer
+    assert TINY.d_latent + TINY.d_rope == 4.5 * TINY.d_head == 72
+    # one oracle row is exactly d_c + d_h^R wide
+    wl = generate(small(v2, "s", 1, 70))
+    assert O.gather_rows(wl.cache, wl.block_table[0], 70, 64).shape == (70, 576)
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+def check_rope_planar():
+    # d = 2: theta_0 = 1, so position m rotates by m radians, counter-clockwise
+    x = np.array([0.3, -1.7])
+    for m in (0, 1, 5, 131071):
+        R = np.array([[np.cos(m), -np.sin(m)], [np.sin(m), np.cos(m)]])
+        assert rel(O.rope(x, m, 10000.0), R @ x) < 1e-14
+
+
+def check_rope_pairing():
+    # d = 4, base 1e4: pairs (0,1) at theta 1 and (2,3) at theta 1e4^(-1/2) = 0.01
+    m = 7.0
+    e2 = np.array([0.0, 0.0, 1.0, 0.0])
+    assert rel(O.rope(e2, m, 1e4), [0, 0, np.cos(0.01 * m), np.sin(0.01 * m)]) < 1e-14
+    e1 = np.array([0.0, 1.0, 0.0, 0.0])
+    assert rel(O.rope(e1, m, 1e4), [-np.sin(m), np.cos(m), 0, 0]) < 1e-14
+    assert np.allclose(O.rope_theta(64, 1e4)[[0, 1, 31]], [1.0, 1e4 ** (-2 / 64), 1e4 ** (-62 / 64)],
+                       rtol=1e-15)
+
+
+def check_rope_identities():
+    d = 64
+    x, y = RNG.standard_normal(d), RNG.standard_normal(d)
+    assert np.array_equal(O.rope(x, 0, 1e4), x)                          # R_0 = I
+    for m, n in ((3, 11), (100, 7), (131071, 65536)):
+        Rm = O.rope_matrix(m, d, 1e4)
+        assert np.allclose(Rm @ Rm.T, np.eye(d), atol=1e-14)             # orthogonal
+        assert rel(Rm @ x, O.rope(x, m, 1e4)) < 1e-13
+        assert abs(np.linalg.norm(O.rope(x, m, 1e4)) - np.linalg.norm(x)) < 1e-12
+        # S = Q^T R_m^T R_n K depends only on n - m
+        lhs = O.rope(x, m, 1e4) @ O.rope(y, n, 1e4)
+        rhs = x @ O.rope(y, n - m, 1e4)
+        assert abs(lhs - rhs) < 1e-11 * np.linalg.norm(x) * np.linalg.norm(y)
+
+
+def test_rope_planar():
+    check_rope_planar()
+
+
+def test_rope_pairing():
+    check_rope_pairing()
+
+
+def test_rope_identities():
+    check_rope_identities()
+
+
+# ---------------------------------------------------------------------------
+# closed forms of the decode step
+# ---------------------------------------------------------------------------
+def check_single_token():
+    # L = 1: softmax weight 1, o_i = W^UV_i c_0, lse = s_00 (query at position 0: R_0 = I)
+    k = rand_case(L=1)
+    r = O.naive_decode_seq(**k, pos=0, scale=0.25, rope_base=1e4)
+    n_h, d_h = k["q_nope"].shape
+    for i in range(n_h):
+        wv = k["w_uv"][i * d_h:(i + 1) * d_h]
+        wk = k["w_uk"][i * d_h:(i + 1) * d_h]
+        assert rel(r["o"][i], wv @ k["c"][0]) < 1e-14
+        assert rel(r["o_latent"][i], k["c"][0]) < 1e-15
+        s = 0.25 * (k["q_nope"][i] @ (wk @ k["c"][0]) + k["q_pe"][i] @ k["k_rope"][0])
+        assert abs(r["lse"][i] - s) < 1e-13
+
+
+def check_equal_scores():
+    # zero query: every score is 0, weights 1/L, o_i = W^UV_i mean_j c_j, lse = ln L
+    k = rand_case(L=9)
+    k["q_nope"][:] = 0
+    k["q_pe"][:] = 0
+    r = O.naive_decode_seq(**k, pos=4, scale=0.3, rope_base=1e4)
+    d_h = k["q_nope"].shape[1]
+    mean_c = k["c"].mean(axis=0)
+    for i in range(k["q_nope"].shape[0]):
+        assert rel(r["o"][i], k["w_uv"][i * d_h:(i + 1) * d_h] @ mean_c) < 1e-13
+        assert rel(r["o_latent"][i], mean_c) < 1e-14
+        assert abs(r["lse"][i] - np.log(9)) < 1e-14
+
+
+def check_identical_tokens():
+    # all tokens equal (c_j = c, k^R_j = 0): o_i = W^UV_i c whatever the query
+    k = rand_case(L=6)
+    k["c"][:] = k["c"][0]
+    k["k_rope"][:] = 0
+    r = O.naive_decode_seq(**k, pos=5, scale=0.2, rope_base=1e4)
+    d_h = k["q_nope"].shape[1]
+    for i in range(k["q_nope"].shape[0]):
+        assert rel(r["o"][i], k["w_uv"][i * d_h:(i + 1) * d_h] @ k["c"][0]) < 1e-13
+
+
+def check_two_token_rope_part():
+    # q^C = 0, query at position 0, q^R = t e_0, k^R_0 = e_0, k^R_1 = 0:
+    # s_0 = t / sqrt(d_h + d_h^R), s_1 = 0 -> a_0 = logistic(s_0)
+    n_h, d_h, d_c, d_r = 2, 8, 24, 4
+    k = rand_case(n_h, d_h, d_c, d_r, L=2)
+    k["q_nope"][:] = 0
+    k["q_pe"][:] = 0
+    k["q_pe"][:, 0] = [1.5, -2.0]
+    k["k_rope"][:] = 0
+    k["k_rope"][0, 0] = 1.0
+    scale = 1 / np.sqrt(d_h + d_r)
+    r = O.naive_decode_seq(**k, pos=0, scale=O.softmax_scale(d_h, d_r), rope_base=1e4)
+    for i, t in enumerate([1.5, -2.0]):
+        s0 = scale * t
+        a0 = 1 / (1 + np.exp(-s0))
+        wv = k["w_uv"][i * d_h:(i + 1) * d_h]
+        assert rel(r["o"][i], a0 * (wv @ k["c"][0]) + (1 - a0) * (wv @ k["c"][1])) < 1e-13
+        assert abs(r["lse"][i] - np.log(np.exp(s0) + 1)) < 1e-13
+
+
+def check_head_rows():
+    # head i owns rows i*d_h .. i*d_h+d_h-1 of W^UK and W^UV.  With selection rows
+    # W^UK[i d_h + r] = e_{(r + 3i) % d_c} and W^UV[i d_h + r] = e_{(r + 5i) % d_c},
+    # q^C_i = t_i e_0 and no RoPE part: s_ij = scale t_i c_j[3i % d_c] and
+    # o_i[r] = sum_j a_ij c_j[(r + 5i) % d_c].
+    n_h, d_h, d_c, d_r, L = 4, 6, 20, 2, 5
+    k = rand_case(n_h, d_h, d_c, d_r, L=L)
+    k["w_uk"][:] = 0
+    k["w_uv"][:] = 0
+    for i in range(n_h):
+        for r_ in range(d_h):
+            k["w_uk"][i * d_h + r_, (r_ + 3 * i) % d_c] = 1
+            k["w_uv"][i * d_h + r_, (r_ + 5 * i) % d_c] = 1
+    t = np.array([0.7, -1.1, 2.3, 0.4])
+    k["q_nope"][:] = 0
+    k["q_nope"][:, 0] = t
+    k["q_pe"][:] = 0
+    scale = 0.5
+    res = O.naive_decode_seq(**k, pos=3, scale=scale, rope_base=1e4)
+    for i in range(n_h):
+        s = scale * t[i] * k["c"][:, (3 * i) % d_c]
+        a = np.exp(s - s.max())
+        a /= a.sum()
+        expect = np.array([a @ k["c"][:, (r_ + 5 * i) % d_c] for r_ in range(d_h)])
+        assert rel(res["o"][i], expect) < 1e-13
+        # q~_i = (W^UK_i)^T q^C_i = t_i e_{3i % d_c}
+        qt = np.zeros(d_c)
+        qt[(3 * i) % d_c] = t[i]
+        assert rel(res["q_abs"][i, :d_c], qt) < 1e-15
+
+
+def test_single_token():
+    check_single_token()
+
+
+def test_equal_scores():
+    check_equal_scores()
+
+
+def test_identical_tokens():
+    check_identical_tokens()
+
+
+def test_two_token_rope_part():
+    check_two_token_rope_part()
+
+
+def test_head_rows():
+    check_head_rows()
+
+
+# ---------------------------------------------------------------------------
+# library attention and the absorbed form
+# ---------------------------------------------------------------------------
+def check_matches_sdpa():
+    torch = pytest.importorskip("torch")
+    n_h, d_h, d_c, d_r, L = 5, 16, 40, 8, 33
+    k = rand_case(n_h, d_h, d_c, d_r, L=L, seed=7)
+    pos = 32
+    scale = O.softmax_scale(d_h, d_r)
+    r = O.naive_decode_seq(**k, pos=pos, scale=scale, rope_base=1e4)
+    # keys/values by the pages' definitions, attention by torch's routine (float64, CPU)
+    K = np.stack([np.concatenate([k["c"] @ k["w_uk"][i * d_h:(i + 1) * d_h].T, k["k_rope"]], 1)
+                  for i in range(n_h)])
+    V = np.stack([k["c"] @ k["w_uv"][i * d_h:(i + 1) * d_h].T for i in range(n_h)])
+    q = np.concatenate([k["q_nope"], O.rope(k["q_pe"], pos, 1e4)], 1)[:, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+        scale=scale)[0, :, 0].numpy()
+    assert rel(r["o"], ref) < 1e-13
+
+
+def test_matches_sdpa():
+    check_matches_sdpa()
+
+
+def check_absorbed_equals_naive_full_recipe(cfg=TINY, delta=0):
+    # Tiny workload from hidden states: cache and query derived by the oracle.
+    L = cfg.seq_len
+    raw = hidden_recipe(cfg, L)
+    pos = np.arange(L) + delta
+    rows = O.cache_rows_from_hidden(raw["h"], raw["w_dkv"], raw["w_kr"], pos, cfg.rope_base,
+                                    rms_norm=cfg.rms_norm_latent)
+    qn, qp = O.query_from_hidden(raw["h"][L - 1], raw["w_q"], raw["w_qr"], cfg.n_heads)
+    scale = O.softmax_scale(cfg.d_head, cfg.d_rope)
+    args = (rows[:, :cfg.d_latent], rows[:, cfg.d_latent:], qn, qp, L - 1 + delta,
+            raw["w_uk"], raw["w_uv"], scale, cfg.rope_base)
+    nv = O.naive_decode_seq(*args)
+    ab = O.absorbed_decode_seq(*args)
+    for key in ("o", "o_latent", "lse", "q_abs"):
+        assert rel(nv[key], ab[key]) < 1e-12, key
+    # o_i = W^UV_i o~_i
+    d_h = cfg.d_head
+    for i in range(cfg.n_heads):
+        assert rel(nv["o"][i], raw["w_uv"][i * d_h:(i + 1) * d_h] @ nv["o_latent"][i]) < 1e-12
+    return nv
+
+
+def test_absorbed_equals_naive_tiny():
+    check_absorbed_equals_naive_full_recipe()
+
+
+def test_absorbed_equals_naive_v2_shape():
+    cfg = small(CONFIGS["v2_b64_l8192"], "v2s", 1, 130)
+    wl = generate(cfg)
+    rows = O.to_f64(O.gather_rows(wl.cache, wl.block_table[0], 130, 64), True)
+    args = (rows[:, :512], rows[:, 512:], O.to_f64(wl.q_nope[0], True), O.to_f64(wl.q_pe[0], True),
+            129, O.to_f64(wl.w_uk, True), O.to_f64(wl.w_uv, True), O.softmax_scale(128, 64), 1e4)
+    nv, ab = O.naive_decode_seq(*args), O.absorbed_decode_seq(*args)
+    for key in ("o", "o_latent", "lse", "q_abs"):
+        assert rel(nv[key], ab[key]) < 1e-12, key
+
+
+def test_position_shift_invariance():
+    # encoding every key at j + delta and the query at p + delta leaves o unchanged
+    a = check_absorbed_equals_naive_full_recipe(delta=0)
+    b = check_absorbed_equals_naive_full_recipe(delta=100000)
+    for key in ("o", "o_latent", "lse"):
+        assert rel(b[key], a[key]) < 1e-10, key
+
+
+# ---------------------------------------------------------------------------
+# merging subsets
+# ---------------------------------------------------------------------------
+def check_lse_merge_partition():
+    k = rand_case(n_h=3, L=40, seed=3)
+    full = O.naive_decode_seq(**k, pos=39, scale=0.3, rope_base=1e4)
+    r = np.random.default_rng(5)
+    for cuts in ([40], [1, 39], [13, 13, 14], list(r.multinomial(40 - 6, [1 / 6] * 6) + 1)):
+        bounds = np.cumsum([0] + list(cuts))
+        parts = [O.naive_decode_seq(k["c"][a:b], k["k_rope"][a:b], k["q_nope"], k["q_pe"], 39,
+                                    k["w_uk"], k["w_uv"], 0.3, 1e4)
+                 for a, b in zip(bounds[:-1], bounds[1:])]
+        ol, lse = O.lse_merge([p["o_latent"] for p in parts], [p["lse"] for p in parts])
+        assert rel(ol, full["o_latent"]) < 1e-12
+        assert np.max(np.abs(lse - full["lse"])) < 1e-12
+
+
+def test_lse_merge_partition():
+    check_lse_merge_partition()
+
+
+# ---------------------------------------------------------------------------
+# paging
+# ---------------------------------------------------------------------------
+def test_gather_matches_generator_order():
+    cfg = small(CONFIGS["v2_varlen_b128"], "vs", 5, (1, 300))
+    wl = generate(cfg)
+    assert cfg.permute_pages
+    for b in range(cfg.batch):
+        L = int(wl.seq_lens[b])
+        got = O.gather_rows(wl.cache, wl.block_table[b], L, 64)
+        assert np.array_equal(got, sequence_rows(cfg, b, L))
+
+
+def test_permuted_vs_contiguous_and_poison():
+    base = small(CONFIGS["v2_varlen_b128"], "vs", 3, (1, 200))
+    contiguous = generate(small(base, "vs", 3, (1, 200), permute_pages=False))
+    permuted = generate(base, pad_value=float("nan"))
+    assert np.isnan(O.to_f64(permuted.cache, True)).any()   # poison present in unused slots
+    a = O.decode_workload(contiguous, heads=range(0, 128, 37))
+    b = O.decode_workload(permuted, heads=range(0, 128, 37))
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: every pin above must catch at least the mistakes aimed at it
+# ---------------------------------------------------------------------------
+def _wrong_sign_rope(x, pos, base):
+    x = np.asarray(x, np.float64)
+    ang = np.asarray(pos, np.float64)[..., None] * O.rope_theta(x.shape[-1], base)
+    y = np.empty_like(x * np.ones(ang.shape[:-1] + (1,)))
+    y[..., 0::2] = x[..., 0::2] * np.cos(ang) + x[..., 1::2] * np.sin(ang)
+    y[..., 1::2] = -x[..., 0::2] * np.sin(ang) + x[..., 1::2] * np.cos(ang)
+    return y
+
+
+def _half_split_theta(d, base):
+    return base ** (-np.arange(d // 2, dtype=np.float64) / d)
+
+
+def _naive_without_rope_term(c, k_rope, *a, **kw):
+    return _ORIG_NAIVE(c, np.zeros_like(np.asarray(k_rope, np.float64)), *a, **kw)
+
+
+def _naive_wrong_scale(c, k_rope, q_nope, q_pe, pos, w_uk, w_uv, scale, rope_base, **kw):
+    return _ORIG_NAIVE(c, k_rope, q_nope, q_pe, pos, w_uk, w_uv, scale * np.sqrt(1.5), rope_base, **kw)
+
+
+_ORIG_NAIVE = O.naive_decode_seq
+
+
+def _head_rows_interleaved(w, i, d_head):
+    n_h = w.shape[0] // d_head
+    return w[i::n_h]
+
+
+def _lse_merge_unweighted(o_parts, lse_parts):
+    return np.mean(o_parts, axis=0), np.max(lse_parts, axis=0)
+
+
+@pytest.mark.parametrize("target,replacement,check", [
+    ("rope", _wrong_sign_rope, check_rope_planar),
+    ("rope_theta", _half_split_theta, check_rope_pairing),
+    ("naive_decode_seq", _naive_without_rope_term, check_two_token_rope_part),
+    ("naive_decode_seq", _naive_wrong_scale, check_two_token_rope_part),
+    ("_head_rows", _head_rows_interleaved, check_head_rows),
+    ("lse_merge", _lse_merge_unweighted, check_lse_merge_partition),
+])
+def test_planted_mistake_is_caught(monkeypatch, target, replacement, check):
+    monkeypatch.setattr(O, target, replacement)
+    with pytest.raises(AssertionError):
+        check()
