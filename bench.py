@@ -1,0 +1,248 @@
+"""Benchmark of one MLA decode step on one MI355X.
+
+A step is one pass of the whole path over a batch: mla_absorb_q ->
+mla_decode_splitkv -> mla_combine -> mla_out_proj, on synthetic inputs already
+resident in HBM (the split plan is made once per batch shape, before timing).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-flush]
+                    [--no-cpu-baseline] [--copy-probe]
+
+Prints ONE JSON line on stdout; progress goes to stderr.  Between timed steps a
+512 MiB buffer is written (untimed) so the 256 MB last-level cache holds none
+of the cache rows.  Step and kernel times come from HIP events recorded on the
+stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+METRIC = "MLA decode TFLOP/s + latent-cache GB/s (% roofline), B=64 S=8192 H=128, 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(cfg, lens):
+    """Algorithmic work of one step and of one decode launch."""
+    L = lens.astype(np.int64)
+    B, H = cfg.batch, cfg.n_heads
+    D = cfg.d_latent + cfg.d_rope
+    pages = int(((L + cfg.page_size - 1) // cfg.page_size).sum())
+    decode_flop = int(L.sum()) * H * 2 * (D + cfg.d_latent)
+    dense_flop = 2 * B * H * cfg.d_head * cfg.d_latent * 2   # absorb + out_proj
+    cache_bytes = int(L.sum()) * D * 2
+    decode_bytes = cache_bytes + B * H * D * 2 + B * H * (cfg.d_latent + 1) * 4 + 4 * pages
+    return dict(decode_flop=decode_flop, step_flop=decode_flop + dense_flop,
+                cache_bytes=cache_bytes, decode_bytes=decode_bytes, pages=pages)
+
+
+def decode_source_hash() -> str:
+    p = os.path.join(ROOT, "mla_latent_kv_16_amd", "csrc", "decode_fast.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed counter summary, if it was
+    taken on the current decode kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"decode_{workload}_counters.md")
+    if not os.path.exists(p):
+        return None
+    txt = open(p).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    h = re.search(r"decode_source_sha256_16:\s*([0-9a-f]+)", txt)
+    if not m or not h or h.group(1) != decode_source_hash():
+        return None
+    return float(m.group(1))
+
+
+def cpu_baseline(wl, budget_s: float = 20.0):
+    """The fp64 oracle, untuned, on a bounded sample of the same workload."""
+    from oracle import decode_workload
+    cfg = wl.cfg
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    order = list(range(cfg.batch))
+    done, flop, t_total = [], 0, 0.0
+    for b in order:
+        t0 = time.perf_counter()
+        decode_workload(wl, seqs=[b])
+        t_total += time.perf_counter() - t0
+        done.append(b)
+        flop += int(wl.seq_lens[b]) * cfg.n_heads * 2 * (cfg.d_latent + cfg.d_rope + cfg.d_latent)
+        if t_total >= budget_s * 0.5 or len(done) == cfg.batch:
+            break
+    toks = int(sum(int(wl.seq_lens[b]) for b in done))
+    return {"value": flop / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(done)} of {cfg.batch} sequences ({toks} cached tokens, all "
+                      f"{cfg.n_heads} heads), naive fp64 path, {t_total:.1f} s wall",
+            "seq_per_s": len(done) / t_total}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v2_b64_l8192")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path does not shard across GPUs in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mla_latent_kv_16_amd as mla
+    from synth import CONFIGS, generate
+
+    cfg = CONFIGS[args.workload]
+    t0 = time.perf_counter()
+    wl = generate(cfg)
+    log(f"[bench] generated {cfg.name} in {time.perf_counter() - t0:.1f} s "
+        f"({wl.num_pages} pages, {wl.cache.nbytes / 1e9:.2f} GB cache)")
+
+    def dev(a, bf):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if bf:
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.cuda()
+
+    bf = cfg.dtype == "bf16"
+    q_nope, q_pe = dev(wl.q_nope, bf), dev(wl.q_pe, bf)
+    positions = dev(wl.positions, False)
+    w_uk, w_uv = dev(wl.w_uk, bf), dev(wl.w_uv, bf)
+    cache = dev(wl.cache, bf)
+    block_table, seq_lens = dev(wl.block_table, False), dev(wl.seq_lens, False)
+    dims = mla.Dims(cfg.n_heads, cfg.d_head, cfg.d_latent, cfg.d_rope, cfg.page_size,
+                    rope_base=cfg.rope_base, dtype=mla.BF16 if bf else mla.F32)
+    props = torch.cuda.get_device_properties(0)
+    slots = int(props.multi_processor_count)
+    items_h, offs_h = mla.plan_splits(dims, wl.seq_lens, slots)
+    items, offs = torch.from_numpy(items_h).cuda(), torch.from_numpy(offs_h).cuda()
+    log(f"[bench] {props.name} {getattr(props, 'gcnArchName', '')}, {slots} CUs; "
+        f"{len(items_h)} work items")
+
+    B, H = cfg.batch, cfg.n_heads
+    bufs = {
+        "q_abs": torch.empty((B, H, dims.row), dtype=q_nope.dtype, device="cuda"),
+        "o_part": torch.empty((len(items_h), H, cfg.d_latent), dtype=torch.float32, device="cuda"),
+        "lse_part": torch.empty((len(items_h), H), dtype=torch.float32, device="cuda"),
+        "o_latent": torch.empty((B, H, cfg.d_latent), dtype=torch.float32, device="cuda"),
+        "lse": torch.empty((B, H), dtype=torch.float32, device="cuda"),
+        "out": torch.empty((B, H, cfg.d_head), dtype=torch.float32, device="cuda"),
+    }
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mla.absorb_q(dims, q_nope, q_pe, positions, w_uk, bufs["q_abs"], stream)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.decode_splitkv(dims, bufs["q_abs"], cache, block_table, seq_lens, items,
+                           bufs["o_part"], bufs["lse_part"], stream)
+        if ev is not None:
+            ev[2].record(stream)
+        mla.combine(dims, offs, bufs["o_part"], bufs["lse_part"], B, bufs["o_latent"],
+                    bufs["lse"], stream)
+        if ev is not None:
+            ev[3].record(stream)
+        mla.out_proj(dims, bufs["o_latent"], w_uv, bufs["out"], stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.fill_(1)
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for k in range(args.steps):
+        if flush is not None:
+            flush.fill_(k & 0xff)
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    t = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])  # ms
+    step_ms = t.sum(axis=1)
+    ms = float(step_ms.mean())
+    k_ms = t.mean(axis=0)
+    names = ["absorb_q", "decode_splitkv", "combine", "out_proj"]
+    log("[bench] per-kernel mean ms: " + ", ".join(f"{n} {v:.4f}" for n, v in zip(names, k_ms)))
+    log(f"[bench] step ms: mean {ms:.4f}  p10 {np.percentile(step_ms, 10):.4f}  "
+        f"p90 {np.percentile(step_ms, 90):.4f}; wall incl. flushes {wall * 1e3 / args.steps:.3f} ms/step")
+    assert torch.isfinite(bufs["out"]).all().item(), "non-finite output"
+
+    work = algorithmic(cfg, wl.seq_lens)
+    dec_s = float(k_ms[1]) * 1e-3
+    achieved = work["decode_bytes"] / dec_s / 1e9
+    traffic = measured_traffic(cfg.name)
+    result = {
+        "metric": METRIC,
+        "value": round(work["step_flop"] / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": B, "seq_len": int(wl.seq_lens.max()),
+                   "total_tokens": int(wl.seq_lens.sum()), "n_heads": H, "d_head": cfg.d_head,
+                   "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "page_size": cfg.page_size,
+                   "work_items": int(len(items_h)), "mall_flushed": flush is not None},
+        "latent_cache_GBps": round(work["cache_bytes"] / (ms * 1e-3) / 1e9, 1),
+        "tokens_per_s": round(B / (ms * 1e-3), 1),
+        "kernel_ms": {n: round(float(v), 5) for n, v in zip(names, k_ms)},
+        "decode_TFLOPs": round(work["decode_flop"] / dec_s / 1e12, 2),
+        "decode_mfma_frac": round(work["decode_flop"] / dec_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"kernel": "mla_decode_splitkv", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": work["decode_bytes"]},
+    }
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(3)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy probe: 1 GiB device-to-device copy done")
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

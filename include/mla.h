@@ -1,0 +1,189 @@
+/*
+ * libmla -- Multi-head Latent Attention (MLA) decode in its weight-absorbed form,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of one attention layer, for a batch of sequences whose keys
+ * and values are kept only as the cached joint latent c^KV (d_c values) and the
+ * head-shared, already position-encoded RoPE key k^R (d_h^R values) per token:
+ *
+ *   mla_absorb_q        q~_i = (W^UK_i)^T q^C_i, and RoPE_p(q^R_i)           (per head i)
+ *   mla_plan_splits     cut every sequence's pages into work items (host)
+ *   mla_decode_splitkv  per work item: scores against [c^KV | k^R], online
+ *                       softmax, latent-space weighted sum, partial LSE
+ *   mla_combine         log-sum-exp merge of the work items of a sequence
+ *   mla_out_proj        o_i = W^UV_i o~_i                                    (per head i)
+ *
+ * Pages describing the method (titles as published):
+ *   "DeepSeek V2 技术解析：多头潜在注意力（MLA）与混合专家模型（MoE）的创新实践",
+ *       part 2, sections 2.2.1.1 (joint KV compression, absorption remark) and
+ *       2.2.2 (decoupled RoPE, what is cached);
+ *   "DeepSeek-V2/V3：大模型的两张账，为什么 MLA 与 MoE 要一起看", section
+ *       "第一张账" (scores read the cached latent through the transformed query,
+ *       aggregation happens in latent space) and the RoPE section (content and
+ *       position channels, per-head q^R, one shared k^R, concatenated inner product).
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * Memory: every pointer argument, unless its name ends in _host, is a device
+ *   pointer on the current HIP device.  The caller allocates and owns all
+ *   buffers; the library allocates nothing, frees nothing and keeps no pointer
+ *   after a call returns.  Calls keep no state between them.
+ * Streams: `stream` is a hipStream_t (NULL = the default stream).  Kernels are
+ *   enqueued on it and the call returns without synchronising.
+ * Errors: arguments are checked on the host before any HIP call; a failed check
+ *   returns a negative status and enqueues nothing.  A failed launch returns
+ *   MLA_ERR_HIP.  Device data is not checked: a block-table entry outside
+ *   [0, num_pages) or a length outside [1, max_pages_per_seq * page_size] is
+ *   undefined behaviour.  No C++ exception crosses this interface.
+ * Layouts (row-major, innermost last; "dtype" is mla_dims.dtype):
+ *   q_nope      [batch][n_heads][d_head]                 dtype
+ *   q_pe        [batch][n_heads][d_rope]                 dtype (not yet encoded)
+ *   positions   [batch]                                  int32 (RoPE position of the query)
+ *   w_uk, w_uv  [n_heads * d_head][d_latent]             dtype; head i owns rows
+ *               i*d_head .. i*d_head + d_head - 1 (k^C = W^UK c^KV, v^C = W^UV c^KV)
+ *   q_abs       [batch][n_heads][d_latent + d_rope]      dtype: [q~_i | RoPE_p(q^R_i)]
+ *   kv_cache    [num_pages][page_size][d_latent + d_rope] dtype: one row per token,
+ *               [c^KV_j | k^R_j], k^R_j already encoded at its own position
+ *   block_table [batch][max_pages_per_seq]               int32: token j of sequence b
+ *               is row (j % page_size) of page block_table[b][j / page_size]
+ *   seq_lens    [batch]                                  int32: tokens 0..seq_lens[b]-1
+ *               are attended (seq_lens[b] >= 1)
+ *   items       [num_items][4]                           int32: (b, split, page_begin, page_end)
+ *   split_offsets [batch + 1]                            int32: items of sequence b are
+ *               split_offsets[b] .. split_offsets[b+1]-1, in token order
+ *   o_part      [num_items][n_heads][d_latent]           float32
+ *   lse_part    [num_items][n_heads]                     float32 (natural log)
+ *   o_latent    [batch][n_heads][d_latent]               float32: o~_i
+ *   lse         [batch][n_heads]                         float32 (natural log)
+ *   out         [batch][n_heads][d_head]                 float32: o_i
+ * Alignment: device pointers of dtype or float32 arrays must be 16-byte aligned.
+ * Numerics: bf16 operands with float32 accumulation; softmax in float32; RoPE
+ *   angles p * theta_k and their sine/cosine in float64, the rotation in float32.
+ *   The fast decode kernel weighs tokens against each work item's first-slice
+ *   score maximum; if a later maximum exceeds it by more than 2^20 it recomputes
+ *   the item against exact maxima.  The environment variable
+ *   MLA_DECODE_MAX_JUMP (log2 units, in (0, 30]) lowers that threshold.
+ *
+ * Supported shapes: the gfx950 fast path needs dtype MLA_BF16, d_latent 512,
+ * d_rope 64, d_head 128, page_size 64 and n_heads 16 or 128; any other shape
+ * with d_latent <= 1024, d_rope even and <= 128, d_head <= 256, page_size in
+ * [1, 1024] and n_heads <= 1024 runs on straightforward kernels; larger ones
+ * return MLA_ERR_UNSUPPORTED.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_VERSION 100 /* major * 100 + minor */
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, L_b < 1 */
+  MLA_ERR_UNSUPPORTED = -2, /* shape or dtype this library does not handle */
+  MLA_ERR_WORKSPACE = -3,   /* caller-provided capacity too small */
+  MLA_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} mla_status;
+
+typedef enum { MLA_BF16 = 0, MLA_F32 = 1 } mla_dtype;
+
+typedef struct {
+  int32_t n_heads;     /* n_h */
+  int32_t d_head;      /* d_h: width of q^C and of the output o_i */
+  int32_t d_latent;    /* d_c: width of the cached latent c^KV */
+  int32_t d_rope;      /* d_h^R: width of q^R and of the shared key k^R (even) */
+  int32_t page_size;   /* tokens per cache page */
+  float softmax_scale; /* multiplies q . k; the usual value is 1/sqrt(d_head + d_rope) */
+  double rope_base;    /* theta_k = rope_base^(-2k/d_rope), pairs (2k, 2k+1) */
+  mla_dtype dtype;     /* storage type of q_nope, q_pe, q_abs, kv_cache, w_uk, w_uv */
+} mla_dims;
+
+/* Absorb W^UK into the query and encode the RoPE part.
+ * Page "DeepSeek V2 技术解析" 2.2.1.1 (W^UK absorbed on the query side) and 2.2.2
+ * (decoupled per-head q^R carries the position; R_m rotation).
+ * For every (b, i): q_abs[b][i][0:d_latent] = (W^UK_i)^T q_nope[b][i] rounded to dtype,
+ * q_abs[b][i][d_latent:] = RoPE_{positions[b]}(q_pe[b][i]) rounded to dtype, where RoPE
+ * rotates the pair (x_2k, x_2k+1) by positions[b] * rope_base^(-2k/d_rope) radians:
+ * (x_2k cos - x_2k+1 sin, x_2k sin + x_2k+1 cos).
+ * Errors: MLA_ERR_INVALID_ARG for null pointers, batch < 1 or misalignment. */
+mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, const void* q_nope, const void* q_pe,
+                        const int32_t* positions, const void* w_uk, void* q_abs, void* stream);
+
+/* Plan the split-KV work items (host only, no HIP call, deterministic).
+ * Each sequence's pages 0 .. ceil(L_b / page_size)-1 are cut into contiguous,
+ * non-empty page ranges; every page of every sequence lands in exactly one item.
+ * The item size is chosen so that about `num_slots` workgroups (CUs times
+ * workgroups resident per CU) stay busy with even loads.
+ * items_host [max_items][4] receives (b, split, page_begin, page_end) for items
+ * 0 .. *num_items-1, grouped by sequence in order; split_offsets_host [batch + 1]
+ * receives the CSR offsets.  Both are plain host memory owned by the caller.
+ * Errors: MLA_ERR_INVALID_ARG for null pointers, batch < 1, num_slots < 1 or a
+ * seq_lens_host entry < 1; MLA_ERR_WORKSPACE when max_items is too small, in
+ * which case *num_items is set to the capacity needed and nothing else is written. */
+mla_status mla_plan_splits(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host,
+                           int32_t num_slots, int32_t max_items, int32_t* items_host,
+                           int32_t* split_offsets_host, int32_t* num_items);
+
+/* Upper bound on the number of items mla_plan_splits can produce for this batch:
+ * sum over b of ceil(L_b / page_size).  Host only.  Returns -1 on bad arguments. */
+int64_t mla_plan_max_items(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host);
+
+/* Split-KV decode over the paged latent cache.
+ * Page "DeepSeek-V2/V3：大模型的两张账" section "第一张账" (scores from the
+ * transformed query and the cached latent; weighted sum in latent space) and RoPE
+ * section (score = inner product of [content ; position] concatenations);
+ * page "DeepSeek V2 技术解析" 2.1.1 (paged KV memory).
+ * For work item w = (b, s, p0, p1), over tokens j in [p0*page_size, min(p1*page_size, L_b)):
+ *   s_ij = softmax_scale * (q_abs[b][i] . kv_row_j)              (all d_latent + d_rope values)
+ *   lse_part[w][i] = log sum_j exp(s_ij)
+ *   o_part[w][i]   = sum_j exp(s_ij - lse_part[w][i]) * kv_row_j[0:d_latent]
+ * Rows of unused cache slots are never read.
+ * Errors: MLA_ERR_INVALID_ARG for null pointers, batch/num_items/num_pages/
+ * max_pages_per_seq < 1 or misalignment; MLA_ERR_UNSUPPORTED for shapes out of range. */
+mla_status mla_decode_splitkv(const mla_dims* dims, int32_t batch, const void* q_abs,
+                              const void* kv_cache, int32_t num_pages, const int32_t* block_table,
+                              int32_t max_pages_per_seq, const int32_t* seq_lens,
+                              const int32_t* items, int32_t num_items, float* o_part,
+                              float* lse_part, void* stream);
+
+/* Merge the work items of every sequence (exact softmax algebra over disjoint
+ * token sets): M = max_s lse_s, w_s = exp(lse_s - M),
+ * o_latent = sum_s w_s o_s / sum_s w_s, lse = M + log sum_s w_s.
+ * `lse` may be NULL.  split_offsets is a device copy of the planner's array.
+ * Errors: MLA_ERR_INVALID_ARG for null pointers, batch < 1 or misalignment. */
+mla_status mla_combine(const mla_dims* dims, int32_t batch, const int32_t* split_offsets,
+                       const float* o_part, const float* lse_part, float* o_latent, float* lse,
+                       void* stream);
+
+/* Map the latent-space result out through W^UV: out[b][i] = W^UV_i o_latent[b][i].
+ * Page "DeepSeek V2 技术解析" 2.2.1.1 (W^UV absorbed on the output side) and page
+ * "DeepSeek-V2/V3：大模型的两张账" "第一张账" (latent-space result mapped out).
+ * float32 o_latent is split into two bf16 terms (hi + lo) on the fast path, so
+ * the product carries about 16 significant bits of o_latent.
+ * Errors: MLA_ERR_INVALID_ARG for null pointers, batch < 1 or misalignment. */
+mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const float* o_latent,
+                        const void* w_uv, float* out, void* stream);
+
+/* Text of the last HIP error that made a libmla call on this thread return
+ * MLA_ERR_HIP ("" if none).  Valid until the next libmla call on the thread. */
+const char* mla_last_hip_error(void);
+
+/* Static description of a status code (never NULL). */
+const char* mla_status_string(mla_status status);
+
+/* MLA_VERSION of the built library. */
+int32_t mla_version(void);
+
+/* 1 when the shape takes the gfx950 fast path, 0 when it takes the
+ * straightforward kernels, negative status when it is rejected. */
+int32_t mla_fast_path(const mla_dims* dims);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

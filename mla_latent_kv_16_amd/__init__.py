@@ -1,0 +1,266 @@
+"""Python binding of libmla (MLA decode, weight-absorbed form, gfx950).
+
+Argument marshalling only: every step runs in libmla's HIP kernels.  torch
+provides device memory and the current HIP stream; tensors are passed to the
+C ABI as raw device pointers.  The binding fails loudly when libmla.so has not
+been built -- there is no fallback.
+
+Entry points mirror include/mla.h:
+    absorb_q, plan_splits, decode_splitkv, combine, out_proj
+plus `decode_step`, which runs the four device steps in order.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+
+__all__ = ["MlaError", "Dims", "load", "lib_path", "absorb_q", "plan_splits", "decode_splitkv",
+           "combine", "out_proj", "decode_step", "fast_path", "version", "BF16", "F32"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+BF16, F32 = 0, 1
+_STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "capacity too small",
+           -4: "HIP runtime error"}
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: libmla status {status} ({_STATUS.get(status, '?')})")
+        self.status = status
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("d_head", ctypes.c_int32),
+                ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("rope_base", ctypes.c_double), ("dtype", ctypes.c_int)]
+
+
+@dataclass(frozen=True)
+class Dims:
+    n_heads: int
+    d_head: int
+    d_latent: int
+    d_rope: int
+    page_size: int = 64
+    softmax_scale: Optional[float] = None   # default 1/sqrt(d_head + d_rope)
+    rope_base: float = 10000.0
+    dtype: int = BF16
+
+    def c(self) -> _Dims:
+        s = self.softmax_scale
+        if s is None:
+            s = 1.0 / float(np.sqrt(self.d_head + self.d_rope))
+        return _Dims(self.n_heads, self.d_head, self.d_latent, self.d_rope, self.page_size,
+                     float(s), float(self.rope_base), int(self.dtype))
+
+    @property
+    def row(self) -> int:
+        return self.d_latent + self.d_rope
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libmla.so")
+
+
+def load():
+    """Load libmla.so (built in the package directory); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = lib_path()
+    if not os.path.exists(p):
+        raise RuntimeError(f"libmla.so not found at {p}; build it with "
+                           "`python -m mla_latent_kv_16_amd.build`")
+    # torch ships its own HIP runtime under the same soname (libamdhip64.so.7).
+    # Load it first so that libmla binds to that one instance: two HIP runtimes
+    # in one process do not share the device.
+    import torch  # noqa: F401
+    L = ctypes.CDLL(p)
+    vp, i32, pi32 = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)
+    pd = ctypes.POINTER(_Dims)
+    sig = {
+        "mla_absorb_q": (i32, [pd, i32, vp, vp, vp, vp, vp, vp]),
+        "mla_plan_splits": (i32, [pd, i32, pi32, i32, i32, pi32, pi32, pi32]),
+        "mla_plan_max_items": (ctypes.c_int64, [pd, i32, pi32]),
+        "mla_decode_splitkv": (i32, [pd, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp]),
+        "mla_combine": (i32, [pd, i32, vp, vp, vp, vp, vp, vp]),
+        "mla_out_proj": (i32, [pd, i32, vp, vp, vp, vp]),
+        "mla_status_string": (ctypes.c_char_p, [i32]),
+        "mla_version": (i32, []),
+        "mla_fast_path": (i32, [pd]),
+        "mla_last_hip_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype, f.argtypes = res, args
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        detail = ""
+        if status == -4 and _lib is not None:
+            detail = " [" + (_lib.mla_last_hip_error() or b"").decode(errors="replace") + "]"
+        raise MlaError(status, where + detail)
+
+
+def version() -> int:
+    return load().mla_version()
+
+
+def fast_path(dims: Dims) -> int:
+    return load().mla_fast_path(ctypes.byref(dims.c()))
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+def _store_dtype(dims: Dims):
+    torch = _torch()
+    return torch.bfloat16 if dims.dtype == BF16 else torch.float32
+
+
+def _ptr(t, dtype=None, shape=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def absorb_q(dims: Dims, q_nope, q_pe, positions, w_uk, q_abs=None, stream=None):
+    """q_abs[b][i] = [(W^UK_i)^T q_nope[b][i] ; RoPE_{positions[b]}(q_pe[b][i])]."""
+    torch = _torch()
+    B = q_nope.shape[0]
+    dt = _store_dtype(dims)
+    H = dims.n_heads
+    if q_abs is None:
+        q_abs = torch.empty((B, H, dims.row), dtype=dt, device=q_nope.device)
+    _check(load().mla_absorb_q(
+        ctypes.byref(dims.c()), B,
+        _ptr(q_nope, dt, (B, H, dims.d_head), "q_nope"), _ptr(q_pe, dt, (B, H, dims.d_rope), "q_pe"),
+        _ptr(positions, torch.int32, (B,), "positions"),
+        _ptr(w_uk, dt, (H * dims.d_head, dims.d_latent), "w_uk"),
+        _ptr(q_abs, dt, (B, H, dims.row), "q_abs"), _stream(stream)), "mla_absorb_q")
+    return q_abs
+
+
+def plan_splits(dims: Dims, seq_lens_host, num_slots: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Host planner: (items [W, 4] int32, split_offsets [B + 1] int32)."""
+    L = load()
+    lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
+    B = int(lens.shape[0])
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    d = dims.c()
+    cap = L.mla_plan_max_items(ctypes.byref(d), B, lens.ctypes.data_as(pi32))
+    if cap < 0:
+        raise MlaError(-1, "mla_plan_max_items")
+    items = np.zeros((max(int(cap), 1), 4), dtype=np.int32)
+    offs = np.zeros(B + 1, dtype=np.int32)
+    n = ctypes.c_int32(0)
+    _check(L.mla_plan_splits(ctypes.byref(d), B, lens.ctypes.data_as(pi32), int(num_slots),
+                             items.shape[0], items.ctypes.data_as(pi32),
+                             offs.ctypes.data_as(pi32), ctypes.byref(n)), "mla_plan_splits")
+    return items[:n.value].copy(), offs
+
+
+def decode_splitkv(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items,
+                   o_part=None, lse_part=None, stream=None):
+    """Per work item: (o_part [W, H, d_c] float32, lse_part [W, H] float32)."""
+    torch = _torch()
+    dt = _store_dtype(dims)
+    B, H = q_abs.shape[0], dims.n_heads
+    W = items.shape[0]
+    dev = q_abs.device
+    if o_part is None:
+        o_part = torch.empty((W, H, dims.d_latent), dtype=torch.float32, device=dev)
+    if lse_part is None:
+        lse_part = torch.empty((W, H), dtype=torch.float32, device=dev)
+    num_pages = kv_cache.shape[0]
+    _check(load().mla_decode_splitkv(
+        ctypes.byref(dims.c()), B, _ptr(q_abs, dt, (B, H, dims.row), "q_abs"),
+        _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
+        _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
+        _ptr(seq_lens, torch.int32, (B,), "seq_lens"), _ptr(items, torch.int32, (W, 4), "items"), W,
+        _ptr(o_part, torch.float32, (W, H, dims.d_latent), "o_part"),
+        _ptr(lse_part, torch.float32, (W, H), "lse_part"), _stream(stream)), "mla_decode_splitkv")
+    return o_part, lse_part
+
+
+def combine(dims: Dims, split_offsets, o_part, lse_part, batch: int, o_latent=None, lse=None,
+            stream=None, want_lse: bool = True):
+    """LSE merge: (o_latent [B, H, d_c] float32, lse [B, H] float32 or None)."""
+    torch = _torch()
+    H = dims.n_heads
+    dev = o_part.device
+    if o_latent is None:
+        o_latent = torch.empty((batch, H, dims.d_latent), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((batch, H), dtype=torch.float32, device=dev)
+    W = o_part.shape[0]
+    _check(load().mla_combine(
+        ctypes.byref(dims.c()), batch, _ptr(split_offsets, torch.int32, (batch + 1,), "split_offsets"),
+        _ptr(o_part, torch.float32, (W, H, dims.d_latent), "o_part"),
+        _ptr(lse_part, torch.float32, (W, H), "lse_part"),
+        _ptr(o_latent, torch.float32, (batch, H, dims.d_latent), "o_latent"),
+        _ptr(lse, torch.float32, (batch, H), "lse"), _stream(stream)), "mla_combine")
+    return o_latent, lse
+
+
+def out_proj(dims: Dims, o_latent, w_uv, out=None, stream=None):
+    """out[b][i] = W^UV_i o_latent[b][i], float32 [B, H, d_h]."""
+    torch = _torch()
+    B, H = o_latent.shape[0], dims.n_heads
+    dt = _store_dtype(dims)
+    if out is None:
+        out = torch.empty((B, H, dims.d_head), dtype=torch.float32, device=o_latent.device)
+    _check(load().mla_out_proj(
+        ctypes.byref(dims.c()), B, _ptr(o_latent, torch.float32, (B, H, dims.d_latent), "o_latent"),
+        _ptr(w_uv, dt, (H * dims.d_head, dims.d_latent), "w_uv"),
+        _ptr(out, torch.float32, (B, H, dims.d_head), "out"), _stream(stream)), "mla_out_proj")
+    return out
+
+
+def decode_step(dims: Dims, q_nope, q_pe, positions, w_uk, w_uv, kv_cache, block_table, seq_lens,
+                items, split_offsets, bufs: Optional[dict] = None, stream=None) -> dict:
+    """absorb_q -> decode_splitkv -> combine -> out_proj on one stream.
+
+    `items`/`split_offsets` are device copies of plan_splits' output.  `bufs` may
+    hold preallocated q_abs, o_part, lse_part, o_latent, lse, out tensors.
+    """
+    b = {} if bufs is None else bufs
+    B = q_nope.shape[0]
+    b["q_abs"] = absorb_q(dims, q_nope, q_pe, positions, w_uk, b.get("q_abs"), stream)
+    b["o_part"], b["lse_part"] = decode_splitkv(dims, b["q_abs"], kv_cache, block_table, seq_lens,
+                                                items, b.get("o_part"), b.get("lse_part"), stream)
+    b["o_latent"], b["lse"] = combine(dims, split_offsets, b["o_part"], b["lse_part"], B,
+                                      b.get("o_latent"), b.get("lse"), stream)
+    b["out"] = out_proj(dims, b["o_latent"], w_uv, b.get("out"), stream)
+    return b

@@ -1,0 +1,39 @@
+// Device helpers shared by the libmla kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short short4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float float4_t;
+
+// float32 -> bfloat16 bits, round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Element `i` of an array stored as bf16 (is_bf16) or float32.
+__device__ __forceinline__ float load_elem(const void* p, int64_t i, bool is_bf16) {
+  return is_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i])
+                 : static_cast<const float*>(p)[i];
+}
+
+__device__ __forceinline__ void store_elem(void* p, int64_t i, float v, bool is_bf16) {
+  if (is_bf16)
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
+  else
+    static_cast<float*>(p)[i] = v;
+}
+
+}  // namespace mla

@@ -1,0 +1,153 @@
+// C-ABI entry points of libmla: argument checks (host, before any HIP call)
+// and dispatch to the gfx950 fast path or the straightforward kernels.
+#include <math.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+
+bool is_fast_shape(const mla_dims& d) {
+  return d.dtype == MLA_BF16 && d.d_latent == kDc && d.d_rope == kDr && d.d_head == kDh &&
+         d.page_size == kPage && (d.n_heads == 16 || d.n_heads == 128);
+}
+
+namespace {
+
+mla_status check_dims(const mla_dims* d) {
+  if (!d) return MLA_ERR_INVALID_ARG;
+  if (d->dtype != MLA_BF16 && d->dtype != MLA_F32) return MLA_ERR_UNSUPPORTED;
+  if (d->n_heads < 1 || d->d_head < 1 || d->d_latent < 1 || d->d_rope < 0 ||
+      (d->d_rope & 1) != 0 || d->page_size < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (!isfinite(d->softmax_scale) || !isfinite(d->rope_base) || !(d->rope_base > 0.0))
+    return MLA_ERR_INVALID_ARG;
+  if (d->n_heads > 1024 || d->d_head > 256 || d->d_latent > 1024 || d->d_rope > 128 ||
+      d->page_size > 1024)
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+thread_local const char* t_last_hip_error = "";
+
+inline mla_status launched(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  t_last_hip_error = hipGetErrorString(e);
+  return MLA_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MLA_ERR_WORKSPACE: return "capacity too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t mla_version(void) { return MLA_VERSION; }
+
+const char* mla_last_hip_error(void) { return t_last_hip_error; }
+
+int32_t mla_fast_path(const mla_dims* d) {
+  const mla_status s = check_dims(d);
+  if (s != MLA_OK) return s;
+  return is_fast_shape(*d) ? 1 : 0;
+}
+
+mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, const void* q_nope, const void* q_pe,
+                        const int32_t* positions, const void* w_uk, void* q_abs, void* stream) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  if (batch < 1 || !q_nope || !q_pe || !positions || !w_uk || !q_abs) return MLA_ERR_INVALID_ARG;
+  if (!al16(q_nope) || !al16(q_pe) || !al16(w_uk) || !al16(q_abs) || !al4(positions))
+    return MLA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(batch) * dims->n_heads > (int64_t{1} << 31)) return MLA_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+  if (is_fast_shape(*dims))
+    return launched(absorb_fast(*dims, batch, q_nope, q_pe, positions, w_uk, q_abs, st));
+  if (batch > 65535) return MLA_ERR_UNSUPPORTED;
+  return launched(absorb_generic(*dims, batch, q_nope, q_pe, positions, w_uk, q_abs, st));
+}
+
+int64_t mla_plan_max_items(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host) {
+  if (check_dims(dims) != MLA_OK) return -1;
+  return plan_max_items(dims->page_size, batch, seq_lens_host);
+}
+
+mla_status mla_plan_splits(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host,
+                           int32_t num_slots, int32_t max_items, int32_t* items_host,
+                           int32_t* split_offsets_host, int32_t* num_items) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  return plan_splits(dims->page_size, batch, seq_lens_host, num_slots, max_items, items_host,
+                     split_offsets_host, num_items, dims->n_heads);
+}
+
+mla_status mla_decode_splitkv(const mla_dims* dims, int32_t batch, const void* q_abs,
+                              const void* kv_cache, int32_t num_pages, const int32_t* block_table,
+                              int32_t max_pages_per_seq, const int32_t* seq_lens,
+                              const int32_t* items, int32_t num_items, float* o_part,
+                              float* lse_part, void* stream) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  if (batch < 1 || num_pages < 1 || max_pages_per_seq < 1 || num_items < 1) return MLA_ERR_INVALID_ARG;
+  if (!q_abs || !kv_cache || !block_table || !seq_lens || !items || !o_part || !lse_part)
+    return MLA_ERR_INVALID_ARG;
+  if (!al16(q_abs) || !al16(kv_cache) || !al16(o_part) || !al4(lse_part) || !al4(block_table) ||
+      !al4(seq_lens) || !al4(items))
+    return MLA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+  if (is_fast_shape(*dims))
+    return launched(decode_fast(*dims, q_abs, kv_cache, block_table, max_pages_per_seq, seq_lens,
+                                items, num_items, o_part, lse_part, st));
+  return launched(decode_generic(*dims, q_abs, kv_cache, block_table, max_pages_per_seq, seq_lens,
+                                 items, num_items, o_part, lse_part, st));
+}
+
+mla_status mla_combine(const mla_dims* dims, int32_t batch, const int32_t* split_offsets,
+                       const float* o_part, const float* lse_part, float* o_latent, float* lse,
+                       void* stream) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  if (batch < 1 || !split_offsets || !o_part || !lse_part || !o_latent) return MLA_ERR_INVALID_ARG;
+  if (!al16(o_part) || !al16(o_latent) || !al4(lse_part) || !al4(split_offsets) ||
+      (lse && !al4(lse)))
+    return MLA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+  if (is_fast_shape(*dims))
+    return launched(combine_fast(*dims, batch, split_offsets, o_part, lse_part, o_latent, lse, st));
+  if (batch > 65535) return MLA_ERR_UNSUPPORTED;
+  return launched(combine_generic(*dims, batch, split_offsets, o_part, lse_part, o_latent, lse, st));
+}
+
+mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const float* o_latent,
+                        const void* w_uv, float* out, void* stream) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  if (batch < 1 || !o_latent || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  if (!al16(o_latent) || !al16(w_uv) || !al16(out)) return MLA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+  if (is_fast_shape(*dims))
+    return launched(out_proj_fast(*dims, batch, o_latent, w_uv, out, st));
+  if (batch > 65535) return MLA_ERR_UNSUPPORTED;
+  return launched(out_proj_generic(*dims, batch, o_latent, w_uv, out, st));
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal declarations shared by the libmla translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla.h"
+
+namespace mla {
+
+// Fast-path shape: bf16, d_c 512, d_h^R 64, d_h 128, 64-token pages.
+constexpr int kDc = 512;
+constexpr int kDr = 64;
+constexpr int kDq = kDc + kDr;  // 576 values per cached row / absorbed query
+constexpr int kDh = 128;
+constexpr int kPage = 64;
+
+bool is_fast_shape(const mla_dims& d);
+
+// Launchers: enqueue on `stream`, return the launch status.
+hipError_t absorb_generic(const mla_dims& d, int batch, const void* q_nope, const void* q_pe,
+                          const int32_t* positions, const void* w_uk, void* q_abs,
+                          hipStream_t stream);
+hipError_t decode_generic(const mla_dims& d, const void* q_abs, const void* kv_cache,
+                          const int32_t* block_table, int max_pages, const int32_t* seq_lens,
+                          const int32_t* items, int num_items, float* o_part, float* lse_part,
+                          hipStream_t stream);
+hipError_t combine_generic(const mla_dims& d, int batch, const int32_t* split_offsets,
+                           const float* o_part, const float* lse_part, float* o_latent, float* lse,
+                           hipStream_t stream);
+hipError_t out_proj_generic(const mla_dims& d, int batch, const float* o_latent, const void* w_uv,
+                            float* out, hipStream_t stream);
+
+hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const void* q_pe,
+                       const int32_t* positions, const void* w_uk, void* q_abs,
+                       hipStream_t stream);
+hipError_t decode_fast(const mla_dims& d, const void* q_abs, const void* kv_cache,
+                       const int32_t* block_table, int max_pages, const int32_t* seq_lens,
+                       const int32_t* items, int num_items, float* o_part, float* lse_part,
+                       hipStream_t stream);
+hipError_t combine_fast(const mla_dims& d, int batch, const int32_t* split_offsets,
+                        const float* o_part, const float* lse_part, float* o_latent, float* lse,
+                        hipStream_t stream);
+hipError_t out_proj_fast(const mla_dims& d, int batch, const float* o_latent, const void* w_uv,
+                         float* out, hipStream_t stream);
+
+// Host planner (plan.cpp).
+mla_status plan_splits(int page_size, int batch, const int32_t* seq_lens, int num_slots,
+                       int max_items, int32_t* items, int32_t* split_offsets, int32_t* num_items,
+                       int n_heads);
+int64_t plan_max_items(int page_size, int batch, const int32_t* seq_lens);
+
+}  // namespace mla

@@ -1,0 +1,125 @@
+// Split-KV work planner (host only, integer arithmetic, deterministic).
+//
+// Every sequence's pages 0 .. ceil(L_b / page_size) - 1 are cut into contiguous,
+// near-equal page ranges ("work items"); one workgroup decodes one item and
+// writes one partial (o, lse) that the combine step merges.  More items fill
+// more of the machine but each one adds a fixed cost (pipeline start-up and the
+// partial's write + re-read), so the item size is picked by simulating the
+// in-order dispatch of the items onto `num_slots` workgroup slots and keeping
+// the size with the shortest simulated makespan.
+#include <algorithm>
+#include <cstdint>
+#include <functional>
+#include <queue>
+#include <vector>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+// Cost unit: 1/16 of one page's streaming time.
+constexpr int64_t kUnit = 16;
+
+struct Layout {
+  int64_t chunk;  // max pages per item
+  int64_t items;
+  int64_t makespan;
+};
+
+// Number of items a sequence of `pages` pages is cut into at chunk size `chunk`.
+inline int64_t parts_of(int64_t pages, int64_t chunk) { return (pages + chunk - 1) / chunk; }
+
+// Pages of part `k` when `pages` are cut into `n` near-equal parts (the first
+// pages % n parts get one page more).
+inline int64_t part_pages(int64_t pages, int64_t n, int64_t k) {
+  return pages / n + (k < pages % n ? 1 : 0);
+}
+
+Layout simulate(const std::vector<int64_t>& pages, int64_t chunk, int num_slots,
+                int64_t overhead) {
+  Layout r{chunk, 0, 0};
+  std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
+  for (int i = 0; i < num_slots; ++i) free_at.push(0);
+  for (int64_t p : pages) {
+    const int64_t n = parts_of(p, chunk);
+    for (int64_t k = 0; k < n; ++k) {
+      const int64_t t = free_at.top();
+      free_at.pop();
+      const int64_t end = t + part_pages(p, n, k) * kUnit + overhead;
+      r.makespan = std::max(r.makespan, end);
+      free_at.push(end);
+      ++r.items;
+    }
+  }
+  return r;
+}
+
+}  // namespace
+
+int64_t plan_max_items(int page_size, int batch, const int32_t* seq_lens) {
+  if (page_size < 1 || batch < 1 || !seq_lens) return -1;
+  int64_t n = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens[b] < 1) return -1;
+    n += (static_cast<int64_t>(seq_lens[b]) + page_size - 1) / page_size;
+  }
+  return n;
+}
+
+mla_status plan_splits(int page_size, int batch, const int32_t* seq_lens, int num_slots,
+                       int max_items, int32_t* items, int32_t* split_offsets, int32_t* num_items,
+                       int n_heads) {
+  if (!seq_lens || !items || !split_offsets || !num_items) return MLA_ERR_INVALID_ARG;
+  if (page_size < 1 || batch < 1 || num_slots < 1 || max_items < 0 || n_heads < 1)
+    return MLA_ERR_INVALID_ARG;
+  std::vector<int64_t> pages(batch);
+  int64_t total = 0, longest = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens[b] < 1) return MLA_ERR_INVALID_ARG;
+    pages[b] = (static_cast<int64_t>(seq_lens[b]) + page_size - 1) / page_size;
+    total += pages[b];
+    longest = std::max(longest, pages[b]);
+  }
+  if (total > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  // Fixed per-item cost: about one page of pipeline start-up plus the partial
+  // (n_heads x (d_latent + 1) float32 written and read back) measured in pages
+  // of 64 rows x 1152 bytes.
+  const int64_t partial_bytes = static_cast<int64_t>(n_heads) * 513 * 4 * 2;
+  const int64_t overhead = kUnit + (partial_bytes * kUnit) / (64 * 1152);
+
+  Layout best{longest, 0, INT64_MAX};
+  std::vector<int64_t> cands;
+  for (int k = 1; k <= 8; ++k) cands.push_back(std::max<int64_t>(1, (total + int64_t(k) * num_slots - 1) / (int64_t(k) * num_slots)));
+  cands.push_back(longest);
+  std::sort(cands.begin(), cands.end());
+  cands.erase(std::unique(cands.begin(), cands.end()), cands.end());
+  for (int64_t c : cands) {
+    Layout l = simulate(pages, c, num_slots, overhead);
+    if (l.makespan < best.makespan || (l.makespan == best.makespan && l.items < best.items)) best = l;
+  }
+  if (best.items > max_items) {
+    *num_items = static_cast<int32_t>(best.items);
+    return MLA_ERR_WORKSPACE;
+  }
+  int32_t w = 0;
+  for (int b = 0; b < batch; ++b) {
+    split_offsets[b] = w;
+    const int64_t n = parts_of(pages[b], best.chunk);
+    int64_t p0 = 0;
+    for (int64_t k = 0; k < n; ++k) {
+      const int64_t np = part_pages(pages[b], n, k);
+      items[4 * w + 0] = b;
+      items[4 * w + 1] = static_cast<int32_t>(k);
+      items[4 * w + 2] = static_cast<int32_t>(p0);
+      items[4 * w + 3] = static_cast<int32_t>(p0 + np);
+      p0 += np;
+      ++w;
+    }
+  }
+  split_offsets[batch] = w;
+  *num_items = w;
+  return MLA_OK;
+}
+
+}  // namespace mla

@@ -1,0 +1,125 @@
+"""The C ABI: exported symbols and host-side argument checks (no GPU needed).
+
+Every call here fails validation before any HIP call, so it runs on a CPU-only
+host; misaligned "device pointers" are plain integers that are never touched.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mla_latent_kv_16_amd as mla
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "mla.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mla.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"mla_absorb_q", "mla_plan_splits", "mla_decode_splitkv", "mla_combine",
+            "mla_out_proj"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mla_version() == 100
+    for s in (0, -1, -2, -3, -4):
+        assert lib.mla_status_string(s)
+    assert lib.mla_status_string(7) == b"unknown status"
+
+
+V2 = mla.Dims(128, 128, 512, 64)
+
+
+def test_fast_path_shapes(lib):
+    assert mla.fast_path(V2) == 1
+    assert mla.fast_path(mla.Dims(16, 128, 512, 64)) == 1
+    assert mla.fast_path(mla.Dims(4, 16, 64, 8, dtype=mla.F32)) == 0
+    assert mla.fast_path(mla.Dims(64, 128, 512, 64)) == 0       # straightforward kernels
+    assert mla.fast_path(mla.Dims(128, 128, 512, 64, page_size=32)) == 0
+    assert mla.fast_path(mla.Dims(4, 16, 64, 7)) == INVALID     # odd RoPE width
+    assert mla.fast_path(mla.Dims(4, 16, 2048, 8)) == UNSUPPORTED
+    assert mla.fast_path(mla.Dims(4, 16, 64, 8, dtype=5)) == UNSUPPORTED
+    assert mla.fast_path(mla.Dims(4, 16, 64, 8, softmax_scale=float("nan"))) == INVALID
+    assert mla.fast_path(mla.Dims(4, 16, 64, 8, rope_base=0.0)) == INVALID
+
+
+A = 0x7f0000000000          # 16-byte aligned stand-in address (never dereferenced)
+MIS = A + 8                 # misaligned
+
+
+def _d(dims=V2):
+    return ctypes.byref(dims.c())
+
+
+def test_absorb_rejects_bad_arguments(lib):
+    f = lib.mla_absorb_q
+    assert f(None, 1, A, A, A, A, A, None) == INVALID
+    assert f(_d(), 0, A, A, A, A, A, None) == INVALID
+    assert f(_d(), 1, None, A, A, A, A, None) == INVALID
+    assert f(_d(), 1, A, A, A, A, None, None) == INVALID
+    assert f(_d(), 1, MIS, A, A, A, A, None) == INVALID
+    assert f(_d(), 1, A, A, A + 2, A, A, None) == INVALID       # positions not 4-aligned
+    assert f(_d(mla.Dims(4, 16, 4096, 8)), 1, A, A, A, A, A, None) == UNSUPPORTED
+
+
+def test_decode_rejects_bad_arguments(lib):
+    f = lib.mla_decode_splitkv
+    good = [A, A, 10, A, 4, A, A, 3, A, A, None]
+    assert f(_d(), 0, *good) == INVALID
+    for i in (0, 1, 3, 5, 6, 8, 9):                # each pointer argument set to NULL
+        args = list(good)
+        args[i] = None
+        assert f(_d(), 2, *args) == INVALID, i
+    for i, bad in ((2, 0), (4, 0), (7, 0)):        # num_pages, max_pages, num_items < 1
+        args = list(good)
+        args[i] = bad
+        assert f(_d(), 2, *args) == INVALID, i
+    args = list(good)
+    args[1] = MIS                                  # kv_cache misaligned
+    assert f(_d(), 2, *args) == INVALID
+    args = list(good)
+    args[8] = A + 4                                # o_part misaligned
+    assert f(_d(), 2, *args) == INVALID
+
+
+def test_combine_and_out_proj_reject_bad_arguments(lib):
+    assert lib.mla_combine(_d(), 0, A, A, A, A, A, None) == INVALID
+    assert lib.mla_combine(_d(), 2, None, A, A, A, A, None) == INVALID
+    assert lib.mla_combine(_d(), 2, A, MIS, A, A, A, None) == INVALID
+    assert lib.mla_combine(_d(), 2, A, A, A, A, A + 2, None) == INVALID   # lse misaligned
+    assert lib.mla_out_proj(_d(), 0, A, A, A, None) == INVALID
+    assert lib.mla_out_proj(_d(), 2, A, None, A, None) == INVALID
+    assert lib.mla_out_proj(_d(), 2, A, A, MIS, None) == INVALID
+
+
+def test_plan_rejects_bad_arguments(lib):
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    lens = np.array([5, 0, 7], dtype=np.int32)
+    items = np.zeros((16, 4), np.int32)
+    offs = np.zeros(4, np.int32)
+    n = ctypes.c_int32(-1)
+    args = (lens.ctypes.data_as(pi32), 256, 16, items.ctypes.data_as(pi32),
+            offs.ctypes.data_as(pi32), ctypes.byref(n))
+    assert lib.mla_plan_splits(_d(), 3, *args) == INVALID               # L_b = 0
+    lens[1] = 3
+    assert lib.mla_plan_splits(_d(), 3, lens.ctypes.data_as(pi32), 0, 16, items.ctypes.data_as(pi32),
+                               offs.ctypes.data_as(pi32), ctypes.byref(n)) == INVALID  # no slots
+    assert lib.mla_plan_splits(_d(), 0, *args) == INVALID
+    assert lib.mla_plan_max_items(_d(), 3, lens.ctypes.data_as(pi32)) == 3
+    lens[1] = -1
+    assert lib.mla_plan_max_items(_d(), 3, lens.ctypes.data_as(pi32)) == -1

@@ -1,0 +1,77 @@
+"""The split-KV planner (host, integer): every page exactly once, balanced items."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import mla_latent_kv_16_amd as mla
+from synth import CONFIGS, seq_lens
+
+V2 = mla.Dims(128, 128, 512, 64)
+LITE = mla.Dims(16, 128, 512, 64)
+
+
+def check_plan(lens, items, offs, page=64):
+    lens = np.asarray(lens)
+    B = len(lens)
+    pages = (lens + page - 1) // page
+    assert offs[0] == 0 and offs[-1] == len(items)
+    assert np.all(np.diff(offs) >= 1)
+    for b in range(B):
+        its = items[offs[b]:offs[b + 1]]
+        assert np.all(its[:, 0] == b)
+        assert np.array_equal(its[:, 1], np.arange(len(its)))      # split index
+        assert its[0, 2] == 0 and its[-1, 3] == pages[b]            # first/last page
+        assert np.all(its[1:, 2] == its[:-1, 3])                    # contiguous, no overlap
+        assert np.all(its[:, 3] > its[:, 2])                        # non-empty
+        sizes = its[:, 3] - its[:, 2]
+        assert sizes.max() - sizes.min() <= 1                       # near-equal parts
+
+
+@pytest.mark.parametrize("lens", [[1], [64], [65], [32768], [1, 64, 65, 32768], [4096] * 32,
+                                  [8192] * 64, [131072] * 8])
+def test_plan_edges(lens):
+    items, offs = mla.plan_splits(V2, lens, 256)
+    check_plan(lens, items, offs)
+
+
+def test_plan_headline_shapes():
+    # uniform lengths that divide evenly fill the machine with equal items
+    items, offs = mla.plan_splits(V2, [8192] * 64, 256)
+    assert len(items) == 256 and np.all(items[:, 3] - items[:, 2] == 32)
+    items, offs = mla.plan_splits(V2, [131072] * 8, 256)
+    assert len(items) == 256 and np.all(items[:, 3] - items[:, 2] == 64)
+    L = seq_lens(CONFIGS["v2_varlen_b128"])
+    items, offs = mla.plan_splits(V2, L, 256)
+    check_plan(L, items, offs)
+    sizes = items[:, 3] - items[:, 2]
+    assert sizes.max() <= 133 and len(items) >= 256
+
+
+def test_plan_is_deterministic():
+    L = np.random.default_rng(3).integers(1, 20000, 77)
+    a = mla.plan_splits(V2, L, 256)
+    b = mla.plan_splits(V2, L, 256)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_plan_capacity_error_reports_need():
+    lib = mla.load()
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    lens = np.array([8192] * 64, np.int32)
+    items = np.zeros((10, 4), np.int32)
+    offs = np.zeros(65, np.int32)
+    n = ctypes.c_int32(0)
+    st = lib.mla_plan_splits(ctypes.byref(V2.c()), 64, lens.ctypes.data_as(pi32), 256, 10,
+                             items.ctypes.data_as(pi32), offs.ctypes.data_as(pi32), ctypes.byref(n))
+    assert st == -3 and n.value == 256
+    assert not items.any() and not offs.any()
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_plan_random(seed):
+    r = np.random.default_rng(seed)
+    L = r.integers(1, 70000, r.integers(1, 300))
+    for dims in (V2, LITE):
+        items, offs = mla.plan_splits(dims, L, int(r.integers(1, 600)))
+        check_plan(L, items, offs)
