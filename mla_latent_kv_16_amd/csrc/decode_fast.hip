@@ -12,28 +12,35 @@
 //
 // Data movement
 //  * Rows stream HBM -> LDS with global_load_lds_dwordx4 (16 bytes per lane,
-//    no VGPR round trip) into a ring of 32-token slots (36,864 bytes each).
-//    The 16-byte chunk `ch` of token row `t` sits at chunk position
-//    ch ^ swz(t) of that row in LDS, which keeps both read patterns below free
-//    of bank conflicts.  Each lane picks which global chunk it fetches, so the
-//    swizzle costs nothing at load time.
+//    no VGPR round trip) into a ring of 32-token slots (36,864 bytes each),
+//    three slices ahead of the one being consumed.  The 16-byte chunk `ch` of
+//    token row `t` sits at chunk position ch ^ swz(t) of that row in LDS (see
+//    swz).  Each lane picks which global chunk it fetches, so the swizzle
+//    costs nothing at load time.
 //  * QK^T operands: a lane reads 16 contiguous bytes (8 latent values of one
 //    token) with ds_read_b128.
 //  * PV operands: C^T needs 8 tokens of one latent column per lane; two
 //    ds_read_b64_tr_b16 (4 tokens x 16 columns per 16-lane group, transposed
 //    in the LDS crossbar) deliver them.  The MFMA's reduction index k is
-//    permuted (k -> token sigma(g, k)) so that P^T comes straight out of the
-//    S^T accumulators of the same lanes with no shuffle.
-//  * One workgroup barrier per slice protects the ring.
+//    permuted (k -> token sigma(g, k), see below) so that the QK^T
+//    accumulators of a lane already hold the P^T operand of the same lane.
 //
-// Work split inside a workgroup (4 waves, one per SIMD):
-//  * H = 128: wave w owns heads 32w .. 32w+31 over every token of the item
-//    (Q fragments: 144 VGPRs; O^T accumulators: 256 registers).
+// Work split inside a workgroup (4 waves, one per SIMD), H = 128:
+//  * scores: wave w owns heads 32w .. 32w+31 over every token (its Q
+//    fragments stay in 144 VGPRs); it turns them into bf16 weights and puts
+//    them in an 8 KiB LDS exchange buffer;
+//  * latent PV: wave w owns latent columns 128w .. 128w+127 for all 128 heads
+//    (256 accumulator registers), so each transposed C^T fragment feeds 8
+//    MFMAs.  LDS transposed reads cost as much issue time as 16-byte reads but
+//    move half the bytes; this split issues a quarter of them compared with
+//    giving each wave its heads' full 512 columns.
+//  Two workgroup barriers per slice: ring hand-over and weight exchange.
+//
 // Softmax in base 2 against a fixed reference per head: the maximum of the
 // item's first slice.  Weights 2^(x - m_ref) may exceed 1 by up to 2^20, which
 // float32 accumulators and bf16 weights carry without loss of relative
 // precision, so the 256 accumulators are never rescaled in registers.  If a
-// later slice exceeds the reference by more than 2^20, the workgroup agrees on
+// later slice exceeds the reference by more than that, the workgroup agrees on
 // it through an LDS flag at the next barrier, takes the exact per-head maxima in
 // a scores-only pass and redoes the item against them; the result is the same
 // softmax either way.
@@ -55,18 +62,52 @@ constexpr int kSlotBytes = kSliceTok * kRowBytes;  // 36,864
 constexpr int kStages = 4;
 constexpr int kWaves = 4;
 constexpr int kLoadsPerWave = kSlotBytes / 1024 / kWaves;  // 9 instructions of 1 KiB
+constexpr int kHeadBlocks = 8;                              // 128 heads / 16
+constexpr int kPBytes = kHeadBlocks * 64 * 16;              // weight exchange, 8 KiB
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kMaxJumpDefault = 20.0f;  // log2 units; see the softmax note above
 
+// Pipelining depths (steps of LDS reads issued ahead of their MFMAs).
+#ifndef MLA_QK_AHEAD
+#define MLA_QK_AHEAD 8
+#endif
+#ifndef MLA_PV_AHEAD
+#define MLA_PV_AHEAD 2
+#endif
+
 static_assert(kSlotBytes % (1024 * kWaves) == 0, "slot must split evenly over the waves");
+static_assert(kStages * kSlotBytes + kPBytes + 16 <= 163840, "LDS budget");
 
 #define MLA_VMCNT(n) (((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-// Row swizzle: chunk position of logical chunk `ch` in LDS row `t` is ch ^ swz(t).
-// For 8 consecutive rows (QK^T reads) and for 4 consecutive rows x 2 adjacent
-// chunks (PV transposed reads) the positions land in distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+// Row swizzle: chunk position of logical chunk `ch` in LDS row `t` is
+// ch ^ swz(t), which permutes only within aligned groups of 8 chunks (a row is
+// 72 chunks).  LDS has 64 banks (256 bytes); a 1152-byte row advances the bank
+// position by half a period, so row parity picks the half.  With
+// swz(t) = j'(t >> 1), j'(j) = 2 (j % 4) + (j / 4) % 2:
+//  * 16 consecutive rows, one chunk (a ds_read_b128 quarter-wave of the QK^T
+//    reads): rows of equal parity get 8 distinct positions;
+//  * 8 consecutive rows x 2 adjacent chunks (a half-wave of the transposed PV
+//    reads): the 4 rows of equal parity give distinct chunk pairs.
+// Both patterns therefore touch 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int t) { return (((t >> 1) & 3) << 1) | ((t >> 3) & 1); }
+
+// Maximum / sum over the four lanes q, q+16, q+32, q+48 (the 16-lane rows of
+// a wave) with the gfx950 row-swap permutes: v_permlane16_swap exchanges rows
+// 0<->1 and 2<->3 between its two operands, v_permlane32_swap the two halves.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // 16 bytes per lane from `base + voff` into LDS at m0 + 16 * lane.
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
@@ -84,13 +125,16 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* lds, uint32_t off) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16_bits(a)) |
-         (static_cast<uint32_t>(f32_to_bf16_bits(b)) << 16);
-}
-
 // ---------------------------------------------------------------------------
-// H = 128: head split.
+// H = 128.
+// MFMA operand layouts (v_mfma_f32_16x16x32_bf16, lane l, g = l / 16, q = l % 16):
+//   A[m][k]: lane holds m = q, k = 8g .. 8g+7;  B[k][n]: k = 8g .. 8g+7, n = q;
+//   C[m][n]: lane holds m = 4g + i (i = 0..3), n = q.
+// Scores: S^T[token][head], A = rows (token q of a 16-block, 8 latent values),
+// B = Q^T.  C leaves lane l with tokens 4g+i of token block tb, head q.
+// PV: O^T[latent][head] += C^T[latent][token] . P^T[token][head] with the
+// reduction index k = 8g + j standing for token sigma(g, j) = 4g + j (j < 4) or
+// 16 + 4g + (j - 4) (j >= 4): exactly the tokens whose weights lane l holds.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
@@ -98,7 +142,9 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
     const int32_t* __restrict__ items, float scale, float max_jump, float* __restrict__ o_part,
     float* __restrict__ lse_part) {
   constexpr int H = 128;
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes + kPBytes];
+  __shared__ int restart_flag;
+  char* const pbuf = lds + kStages * kSlotBytes;
   const uint32_t lds_base =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
 
@@ -117,8 +163,8 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
   const int n_slices = (t_end - t_begin + kSliceTok - 1) / kSliceTok;
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
 
-  // --- Q fragments (B operand of S^T = Rows . Q^T): lane holds head q of
-  // block hb, values 32ks + 8g .. +8.
+  // --- Q fragments (B operand of the scores): lane holds head 32w + 16hb + q,
+  // values 32ks + 8g .. +8.
   bf16x8 qf[2][18];
   {
     const uint16_t* qrow0 = q_abs + (static_cast<int64_t>(b) * H + 32 * w + q) * kDq + 8 * g;
@@ -128,16 +174,21 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
       for (int ks = 0; ks < 18; ++ks)
         qf[hb][ks] = *reinterpret_cast<const bf16x8*>(qrow0 + hb * 16 * kDq + 32 * ks);
   }
+  if (threadIdx.x == 0) restart_flag = 0;
   __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
 
   // --- per-lane DMA source: LDS chunk p = (9w + i) * 64 + lane of a slot holds
-  // logical chunk ch = (p % 72) ^ swz(t) of token t = p / 72.
-  auto dma_token = [&](int i) { return ((kLoadsPerWave * w + i) * 64 + lane) / kChunksPerRow; };
-  auto dma_off = [&](int i) -> uint32_t {
+  // logical chunk ch = (p % 72) ^ swz(t) of token t = p / 72.  The 9 byte
+  // offsets (< 36864) are kept two to a register.
+  uint32_t dma_pk[(kLoadsPerWave + 1) / 2] = {};
+#pragma unroll
+  for (int i = 0; i < kLoadsPerWave; ++i) {
     const int p = (kLoadsPerWave * w + i) * 64 + lane;
     const int t = p / kChunksPerRow;
-    return static_cast<uint32_t>(t * kRowBytes + ((p % kChunksPerRow) ^ swz(t)) * 16);
-  };
+    const uint32_t off = static_cast<uint32_t>(t * kRowBytes + ((p % kChunksPerRow) ^ swz(t)) * 16);
+    dma_pk[i / 2] |= off << (16 * (i & 1));
+  }
+  auto dma_off = [&](int i) -> uint32_t { return (dma_pk[i / 2] >> (16 * (i & 1))) & 0xffffu; };
 
   auto issue = [&](int n) {
     const int tok0 = t_begin + n * kSliceTok;
@@ -154,16 +205,16 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
       // (finite data, weight 0), so empty cache slots are never read.
 #pragma unroll
       for (int i = 0; i < kLoadsPerWave; ++i) {
-        const int t = dma_token(i);
         const uint32_t off = dma_off(i);
-        dma16(src, t < nv ? off : off - t * kRowBytes, dst + i * 1024);
+        const uint32_t t = off / kRowBytes;
+        dma16(src, static_cast<int>(t) < nv ? off : off - t * kRowBytes, dst + i * 1024);
       }
     }
   };
 
   // --- per-lane LDS read offsets (within a slot)
   const int sw = swz(q);  // rows q and q + 16 share it
-  // QK^T A operand: token tb*16 + q, logical chunk 4ks + g
+  // scores A operand: token tb*16 + q, logical chunk 4ks + g
   const uint32_t qk_off0 = q * kRowBytes + 16 * ((g) ^ sw);       // even ks
   const uint32_t qk_off1 = q * kRowBytes + 16 * ((4 + g) ^ sw);   // odd ks
   // PV A operand (transposed read): token 4g + q/4 (+16), column 16cb + 4(q%4)
@@ -171,11 +222,11 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
   const int vsw = swz(vrow);
   const uint32_t pv_base = vrow * kRowBytes + 8 * (q & 1);
   const int pv_hc = (q & 3) >> 1;
+  auto pv_off = [&](int cb) -> uint32_t {  // cb: global 16-column block 0..31
+    return pv_base + 128 * (cb >> 2) + 16 * ((2 * (cb & 3) + pv_hc) ^ vsw);
+  };
 
-  __shared__ int restart_flag;
-  if (threadIdx.x == 0) restart_flag = 0;
-
-  float4_t oacc[32][2];
+  float4_t oacc[8][kHeadBlocks];  // [latent block of this wave][head block]
   float m_ref[2], l_run[2];
   const float c2 = scale * kLog2e;
 
@@ -187,7 +238,7 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) sacc[tb][hb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    constexpr int kSteps = 36, kAhead = 4;
+    constexpr int kSteps = 36, kAhead = MLA_QK_AHEAD;
     auto off_of = [&](int st) -> uint32_t {
       const int ks = st >> 1, tb = st & 1;
       return tb * 16 * kRowBytes + 128 * (ks >> 1) + ((ks & 1) ? qk_off1 : qk_off0);
@@ -206,31 +257,32 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
     }
   };
 
-  // Scaled scores (log2 units, masked) and their per-head maximum over the slice.
-  auto scaled_max = [&](const float4_t (&sacc)[2][2], int nv, float (&x)[2][2][4], float (&mx)[2]) {
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float m = -INFINITY;
+  // Per-head maximum of the slice's scores in log2 units (scale folded in);
+  // tokens past the end of the item (tail slice only) are set to -inf.
+  auto slice_max = [&](float4_t (&sacc)[2][2], int nv, float (&mx)[2]) {
+    if (nv < kSliceTok) {
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = tb * 16 + 4 * g + i;
-          const float v = t < nv ? sacc[tb][hb][i] * c2 : -INFINITY;
-          x[tb][hb][i] = v;
-          m = fmaxf(m, v);
-        }
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      mx[hb] = m;
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tb * 16 + 4 * g + i >= nv) sacc[tb][hb][i] = -INFINITY;
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float m = fmaxf(fmaxf(fmaxf(sacc[0][hb][0], sacc[0][hb][1]), fmaxf(sacc[0][hb][2], sacc[0][hb][3])),
+                      fmaxf(fmaxf(sacc[1][hb][0], sacc[1][hb][1]), fmaxf(sacc[1][hb][2], sacc[1][hb][3])));
+      mx[hb] = rows_max(m) * c2;
     }
   };
 
   // One pass over the item's slices through the LDS ring.
-  //  kFull = true:  scores, weights p = 2^(x - m_ref), O += C^T P^T.  With
+  //  kFull = true:  scores, weights p = 2^(s c2 - m_ref), O += C^T P^T.  With
   //                 `first` the reference m_ref is the first slice's maximum and
   //                 a jump beyond max_jump aborts the pass (returns false).
   //  kFull = false: scores only, m_ref = exact per-head maximum.
+  // Every wave executes the same barriers in every case.
   auto run_pass = [&](auto full_tag, bool first) -> bool {
     constexpr bool kFull = decltype(full_tag)::value;
     for (int n = 0; n < kStages - 1 && n < n_slices; ++n) issue(n);
@@ -243,7 +295,7 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
         __builtin_amdgcn_s_waitcnt(MLA_VMCNT(kLoadsPerWave));
       else
         __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
-      __syncthreads();
+      __syncthreads();  // (A) slice n landed; slot of n-1 and the weight buffer are free
       if (kFull && first && restart_flag) {  // same value in every wave after the barrier
         aborted = true;
         break;
@@ -254,8 +306,8 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
       const int nv = min(kSliceTok, t_end - (t_begin + n * kSliceTok));
       float4_t sacc[2][2];
       scores(slot, sacc);
-      float x[2][2][4], mx[2];
-      scaled_max(sacc, nv, x, mx);
+      float mx[2];
+      slice_max(sacc, nv, mx);
       if (!kFull) {
         m_ref[0] = fmaxf(m_ref[0], mx[0]);
         m_ref[1] = fmaxf(m_ref[1], mx[1]);
@@ -266,50 +318,55 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
           m_ref[0] = mx[0];
           m_ref[1] = mx[1];
         }
-        if (__any(mx[0] > m_ref[0] + max_jump || mx[1] > m_ref[1] + max_jump)) {
-          if (lane == 0) restart_flag = 1;
-          continue;  // this pass will be discarded
-        }
+        if (__any(mx[0] > m_ref[0] + max_jump || mx[1] > m_ref[1] + max_jump) && lane == 0)
+          restart_flag = 1;  // this pass will be discarded at the next barrier (A)
       }
-      bf16x8 pf[2];
+      // weights p = 2^(s c2 - m_ref) (masked tokens: 2^-inf = 0), packed to bf16
+      // in the token order sigma(g, .) and handed over through LDS
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         uint32_t pk[4];
         float sum = 0.f;
+        const float neg_m = -m_ref[hb];
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
           float p[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            p[i] = bf16_bits_to_f32(f32_to_bf16_bits(exp2f(x[tb][hb][i] - m_ref[hb])));
+            p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[tb][hb][i], c2, neg_m));
             sum += p[i];
           }
           pk[2 * tb] = pack_bf16x2(p[0], p[1]);
           pk[2 * tb + 1] = pack_bf16x2(p[2], p[3]);
         }
         l_run[hb] += sum;
-        pf[hb] = __builtin_bit_cast(bf16x8, pk);
+        *reinterpret_cast<bf16x8*>(pbuf + ((2 * w + hb) * 64 + lane) * 16) =
+            __builtin_bit_cast(bf16x8, pk);
       }
-      // O^T[512 x 32 heads] += C^T . P^T, 32 steps of 16 latent columns
-      constexpr int kSteps = 32, kAhead = 3;
+      __syncthreads();  // (B) every head block's weights are in the buffer
+
+      // O^T[128 columns of this wave x 128 heads] += C^T . P^T
+      bf16x8 pf[kHeadBlocks];
+#pragma unroll
+      for (int hb = 0; hb < kHeadBlocks; ++hb)
+        pf[hb] = *reinterpret_cast<const bf16x8*>(pbuf + (hb * 64 + lane) * 16);
+      constexpr int kAhead = MLA_PV_AHEAD;
       bf16x4 f0[kAhead], f1[kAhead];
-      auto pv_off = [&](int cb) -> uint32_t {
-        return pv_base + 128 * (cb >> 2) + 16 * ((2 * (cb & 3) + pv_hc) ^ vsw);
-      };
 #pragma unroll
-      for (int cb = 0; cb < kAhead; ++cb) {
-        f0[cb] = lds_read_tr(slot, pv_off(cb));
-        f1[cb] = lds_read_tr(slot, pv_off(cb) + 16 * kRowBytes);
+      for (int c = 0; c < kAhead; ++c) {
+        f0[c] = lds_read_tr(slot, pv_off(8 * w + c));
+        f1[c] = lds_read_tr(slot, pv_off(8 * w + c) + 16 * kRowBytes);
       }
 #pragma unroll
-      for (int cb = 0; cb < kSteps; ++cb) {
-        const bf16x8 a = __builtin_shufflevector(f0[cb % kAhead], f1[cb % kAhead], 0, 1, 2, 3, 4, 5, 6, 7);
-        if (cb + kAhead < kSteps) {
-          f0[cb % kAhead] = lds_read_tr(slot, pv_off(cb + kAhead));
-          f1[cb % kAhead] = lds_read_tr(slot, pv_off(cb + kAhead) + 16 * kRowBytes);
+      for (int c = 0; c < 8; ++c) {
+        const bf16x8 a = __builtin_shufflevector(f0[c % kAhead], f1[c % kAhead], 0, 1, 2, 3, 4, 5, 6, 7);
+        if (c + kAhead < 8) {
+          f0[c % kAhead] = lds_read_tr(slot, pv_off(8 * w + c + kAhead));
+          f1[c % kAhead] = lds_read_tr(slot, pv_off(8 * w + c + kAhead) + 16 * kRowBytes);
         }
-        oacc[cb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[0], oacc[cb][0], 0, 0, 0);
-        oacc[cb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[1], oacc[cb][1], 0, 0, 0);
+#pragma unroll
+        for (int hb = 0; hb < kHeadBlocks; ++hb)
+          oacc[c][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[hb], oacc[c][hb], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -320,9 +377,9 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
 
   auto zero_state = [&]() {
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb)
+    for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) oacc[cb][hb] = float4_t{0.f, 0.f, 0.f, 0.f};
+      for (int hb = 0; hb < kHeadBlocks; ++hb) oacc[c][hb] = float4_t{0.f, 0.f, 0.f, 0.f};
     l_run[0] = l_run[1] = 0.f;
   };
 
@@ -336,25 +393,33 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
     run_pass(std::integral_constant<bool, true>{}, false);
   }
 
-  // ---- epilogue: normalise, write the partial
+  // ---- epilogue: row sums of the wave's own heads to LDS, then every wave
+  // normalises its 128 columns for all heads and writes the partial.
+  float* lsum = reinterpret_cast<float*>(pbuf);  // [128], reuses the weight buffer
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    float l = l_run[hb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const float inv = 1.f / l;
+    const float l = rows_sum(l_run[hb]);
     const int head = 32 * w + 16 * hb + q;
-    float* orow = o_part + (static_cast<int64_t>(it) * H + head) * kDc + 4 * g;
+    if (g == 0) {
+      lsum[head] = l;
+      lse_part[static_cast<int64_t>(it) * H + head] = m_ref[hb] * kLn2 + logf(l);
+    }
+  }
+  __syncthreads();
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb) {
-      float4_t v = oacc[cb][hb];
+  for (int hb = 0; hb < kHeadBlocks; ++hb) {
+    const int head = 16 * hb + q;
+    const float inv = 1.f / lsum[head];
+    float* orow = o_part + (static_cast<int64_t>(it) * H + head) * kDc + 128 * w + 4 * g;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float4_t v = oacc[c][hb];
       v[0] *= inv;
       v[1] *= inv;
       v[2] *= inv;
       v[3] *= inv;
-      *reinterpret_cast<float4_t*>(orow + 16 * cb) = v;
+      *reinterpret_cast<float4_t*>(orow + 16 * c) = v;
     }
-    if (g == 0) lse_part[static_cast<int64_t>(it) * H + head] = m_ref[hb] * kLn2 + logf(l);
   }
 }
 

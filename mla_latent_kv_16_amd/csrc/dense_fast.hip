@@ -22,8 +22,6 @@ namespace {
 
 constexpr int kWRowBytes = kDc * 2;  // 1024 bytes per weight row
 
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
-
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr)
                : "memory");
@@ -31,48 +29,67 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t 
 
 #define MLA_VMCNT0 ((7 << 4) | (15 << 8))
 
+// XCD-aware workgroup numbering: workgroup i runs on XCD i % 8.  Give the
+// `per` consecutive blocks of one head the same XCD so they share its L2.
+__device__ __forceinline__ void xcd_split(int i, int per, int& head, int& sub) {
+  const int xcd = i & 7, k = i >> 3;
+  sub = k % per;
+  head = (k / per) * 8 + xcd;
+}
+
 // ---------------------------------------------------------------------------
-// absorb: q~^T[512 x b] = (W^UK_h)^T[512 x 128] . q^C^T[128 x b].
-// W^UK_h (128 KiB) is staged in LDS, rows swizzled like the decode cache, and
-// read transposed (ds_read_b64_tr_b16) as the A operand.
+// absorb: q~^T[512 x b] = (W^UK_h)^T[512 x 128] . q^C^T[128 x b], one
+// workgroup per (head, quarter of the 512 latent columns, 64 sequences).
+// The [128 x 128] weight tile (32 KiB) is staged in LDS, rows of 256 bytes with
+// chunk position ch ^ tsw(row), and read transposed (ds_read_b64_tr_b16) as
+// the A operand: each half-wave then touches rows {r..r+3, r+8..r+11} x two
+// adjacent chunks, 16 distinct 16-byte bank groups.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 1) void absorb_kernel(
+__device__ __forceinline__ int tsw(int row) { return ((row & 3) << 1) | (((row >> 3) & 1) << 3); }
+
+__global__ __launch_bounds__(256) void absorb_kernel(
     int batch, int H, double rope_base, const uint16_t* __restrict__ q_nope,
     const uint16_t* __restrict__ q_pe, const int32_t* __restrict__ positions,
     const char* __restrict__ w_uk, uint16_t* __restrict__ q_abs) {
-  __shared__ __attribute__((aligned(1024))) char lds[kDh * kWRowBytes];
+  constexpr int kCols = 128, kTileRow = kCols * 2;  // 256 bytes
+  __shared__ __attribute__((aligned(1024))) char lds[kDh * kTileRow];
   const uint32_t lds_base = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
-  const int h = blockIdx.x;
+  int h, quarter;
+  xcd_split(blockIdx.x, 4, h, quarter);
+  const int c0 = quarter * kCols;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, q = lane & 15;
 
-  // stage W^UK_h: wave w copies rows 32w .. 32w+31, one row per instruction
-  const char* wh = w_uk + static_cast<int64_t>(h) * kDh * kWRowBytes;
-#pragma unroll 8
-  for (int i = 0; i < 32; ++i) {
-    const int row = 32 * w + i;
-    const uint32_t off = row * kWRowBytes + 16 * (lane ^ swz(row));
-    dma16(wh, off, lds_base + row * kWRowBytes);
+  // stage W^UK_h[:, c0:c0+128]: LDS chunk p = row * 16 + pc holds chunk pc ^ tsw(row)
+  const char* wh = w_uk + static_cast<int64_t>(h) * kDh * (kDc * 2) + c0 * 2;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = (8 * w + i) * 64 + lane;
+    const int row = p >> 4, pc = p & 15;
+    dma16(wh, row * (kDc * 2) + 16 * (pc ^ tsw(row)), lds_base + (8 * w + i) * 1024);
   }
 
-  // RoPE part, float64 angle, float32 rotation: (b, k) pairs of this batch group
   const int b0 = blockIdx.y * 64;
   const int nb = min(64, batch - b0);
-  for (int e = threadIdx.x; e < nb * (kDr / 2); e += 256) {
-    const int b = b0 + e / (kDr / 2), k = e % (kDr / 2);
+  // RoPE part, float64 angle, float32 rotation.  The four quarter-workgroups
+  // of a head share the (sequence, pair) list; thread t keeps pair k = t % 32.
+  {
+    const int k = threadIdx.x & (kDr / 2 - 1);
     const double theta = pow(rope_base, -2.0 * k / kDr);
-    double sd, cd;
-    sincos(static_cast<double>(positions[b]) * theta, &sd, &cd);
-    const float c = static_cast<float>(cd), s = static_cast<float>(sd);
-    const int64_t r = static_cast<int64_t>(b) * H + h;
-    const uint32_t xy = *reinterpret_cast<const uint32_t*>(q_pe + r * kDr + 2 * k);
-    const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(xy & 0xffffu));
-    const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(xy >> 16));
-    const uint32_t o = static_cast<uint32_t>(f32_to_bf16_bits(x0 * c - x1 * s)) |
-                       (static_cast<uint32_t>(f32_to_bf16_bits(x0 * s + x1 * c)) << 16);
-    *reinterpret_cast<uint32_t*>(q_abs + r * kDq + kDc + 2 * k) = o;
+    for (int bi = quarter * 8 + (threadIdx.x >> 5); bi < nb; bi += 32) {
+      const int bb = b0 + bi;
+      double sd, cd;
+      sincos(static_cast<double>(positions[bb]) * theta, &sd, &cd);
+      const float c = static_cast<float>(cd), sn = static_cast<float>(sd);
+      const int64_t r = static_cast<int64_t>(bb) * H + h;
+      const uint32_t xy = *reinterpret_cast<const uint32_t*>(q_pe + r * kDr + 2 * k);
+      const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(xy & 0xffffu));
+      const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(xy >> 16));
+      *reinterpret_cast<uint32_t*>(q_abs + r * kDq + kDc + 2 * k) =
+          pack_bf16x2(x0 * c - x1 * sn, x0 * sn + x1 * c);
+    }
   }
 
   // B operand: q^C of sequence b = b0 + 16w + q, values 32ks + 8g .. +8
@@ -91,20 +108,20 @@ __global__ __launch_bounds__(256, 1) void absorb_kernel(
   __syncthreads();
   if (16 * w >= nb) return;  // no sequence for this wave (no barrier follows)
 
-  // A operand rows d = 32ks + 8g + s (+4), columns 16cb + 4(q%4): source-lane
-  // role q -> row 8g + q/4 of the k block, column chunk 2cb + (q%4)/2.
+  // A operand rows d = 32ks + 8g + s (+4), columns 16cb + 4(q%4) of the tile:
+  // source-lane role q -> row 8g + q/4 of the k block, chunk 2cb + (q%4)/2.
   const int arow = 8 * g + (q >> 2);
-  const int sw0 = swz(arow), sw1 = swz(arow + 4);
-  uint16_t* qrow = q_abs + (static_cast<int64_t>(b) * H + h) * kDq + 4 * g;
-#pragma unroll 4
-  for (int cb = 0; cb < 32; ++cb) {
+  const int sw0 = tsw(arow), sw1 = tsw(arow + 4);
+  uint16_t* qrow = q_abs + (static_cast<int64_t>(b) * H + h) * kDq + c0 + 4 * g;
+#pragma unroll
+  for (int cb = 0; cb < kCols / 16; ++cb) {
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
     const int ch = 2 * cb + ((q & 3) >> 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int r0 = 32 * ks + arow;
-      const uint32_t o0 = r0 * kWRowBytes + 16 * (ch ^ sw0) + 8 * (q & 1);
-      const uint32_t o1 = (r0 + 4) * kWRowBytes + 16 * (ch ^ sw1) + 8 * (q & 1);
+      const uint32_t o0 = r0 * kTileRow + 16 * (ch ^ sw0) + 8 * (q & 1);
+      const uint32_t o1 = (r0 + 4) * kTileRow + 16 * (ch ^ sw1) + 8 * (q & 1);
       const short4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (__attribute__((address_space(3))) short4_t*)((__attribute__((address_space(3))) char*)lds + o0));
       const short4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -112,28 +129,27 @@ __global__ __launch_bounds__(256, 1) void absorb_kernel(
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qn[ks], acc, 0, 0, 0);
     }
-    // lane holds q~[16cb + 4g + i] of sequence b
+    // lane holds q~[c0 + 16cb + 4g + i] of sequence b
     if (bvalid) {
-      const uint32_t lo = static_cast<uint32_t>(f32_to_bf16_bits(acc[0])) |
-                          (static_cast<uint32_t>(f32_to_bf16_bits(acc[1])) << 16);
-      const uint32_t hi = static_cast<uint32_t>(f32_to_bf16_bits(acc[2])) |
-                          (static_cast<uint32_t>(f32_to_bf16_bits(acc[3])) << 16);
       uint32_t* dst = reinterpret_cast<uint32_t*>(qrow + 16 * cb);
-      dst[0] = lo;
-      dst[1] = hi;
+      dst[0] = pack_bf16x2(acc[0], acc[1]);
+      dst[1] = pack_bf16x2(acc[2], acc[3]);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// out_proj: o^T[128 x b] = W^UV_h[128 x 512] . o~^T[512 x b].  The float32 o~
-// is split into bf16 hi + lo (lo = bf16(x - hi)); two MFMAs per step.
+// out_proj: o^T[16 x b] = W^UV_h[16 rows x 512] . o~^T[512 x b] for one block of
+// 16 output rows per workgroup (8 per head), 16 sequences per wave.  Every
+// operand of the workgroup is loaded up front.  The float32 o~ is split into
+// bf16 hi + lo (lo = bf16(x - hi)); two MFMAs per step.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void out_proj_kernel(int batch, int H,
                                                        const float* __restrict__ o_lat,
                                                        const uint16_t* __restrict__ w_uv,
                                                        float* __restrict__ out) {
-  const int h = blockIdx.x;
+  int h, db;
+  xcd_split(blockIdx.x, kDh / 16, h, db);
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int g = lane >> 4, q = lane & 15;
@@ -141,42 +157,37 @@ __global__ __launch_bounds__(256) void out_proj_kernel(int batch, int H,
   if (bblk * 16 >= batch) return;
   const int b = bblk * 16 + q;
   const bool bvalid = b < batch;
+  const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * kDh + 16 * db + q) * kDc + 8 * g;
   const float* orow = o_lat + (static_cast<int64_t>(b) * H + h) * kDc + 8 * g;
-  const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * kDh + q) * kDc + 8 * g;
-  float4_t acc[8];
+  bf16x8 a[16];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) acc[db] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
+  for (int ks = 0; ks < 16; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(wrow + 32 * ks);
+  float4_t x[16][2];
+#pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
-    float x[8];
     if (bvalid) {
-      const float4_t x0 = *reinterpret_cast<const float4_t*>(orow + 32 * ks);
-      const float4_t x1 = *reinterpret_cast<const float4_t*>(orow + 32 * ks + 4);
-      x[0] = x0[0]; x[1] = x0[1]; x[2] = x0[2]; x[3] = x0[3];
-      x[4] = x1[0]; x[5] = x1[1]; x[6] = x1[2]; x[7] = x1[3];
+      x[ks][0] = *reinterpret_cast<const float4_t*>(orow + 32 * ks);
+      x[ks][1] = *reinterpret_cast<const float4_t*>(orow + 32 * ks + 4);
     } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = 0.f;
-    }
-    uint16_t hb[8], lb[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      hb[j] = f32_to_bf16_bits(x[j]);
-      lb[j] = f32_to_bf16_bits(x[j] - bf16_bits_to_f32(hb[j]));
-    }
-    const bf16x8 bhi = __builtin_bit_cast(bf16x8, hb);
-    const bf16x8 blo = __builtin_bit_cast(bf16x8, lb);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wrow + (16 * db) * kDc + 32 * ks);
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bhi, acc[db], 0, 0, 0);
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, blo, acc[db], 0, 0, 0);
+      x[ks][0] = x[ks][1] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
   }
-  if (!bvalid) return;
-  float* dst = out + (static_cast<int64_t>(b) * H + h) * kDh + 4 * g;
+  float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int db = 0; db < 8; ++db) *reinterpret_cast<float4_t*>(dst + 16 * db) = acc[db];
+  for (int ks = 0; ks < 16; ++ks) {
+    uint32_t hb[4], lb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v0 = x[ks][j >> 1][2 * (j & 1)], v1 = x[ks][j >> 1][2 * (j & 1) + 1];
+      hb[j] = pack_bf16x2(v0, v1);
+      lb[j] = pack_bf16x2(v0 - __uint_as_float(hb[j] << 16), v1 - __uint_as_float(hb[j] & 0xffff0000u));
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], __builtin_bit_cast(bf16x8, hb), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], __builtin_bit_cast(bf16x8, lb), acc, 0, 0, 0);
+  }
+  // lane holds o[b][h][16db + 4g + i]
+  if (bvalid)
+    *reinterpret_cast<float4_t*>(out + (static_cast<int64_t>(b) * H + h) * kDh + 16 * db + 4 * g) = acc;
 }
 
 }  // namespace
@@ -185,8 +196,8 @@ hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const v
                        const int32_t* positions, const void* w_uk, void* q_abs,
                        hipStream_t stream) {
   const int groups = (batch + 63) / 64;
-  if (groups > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(absorb_kernel, dim3(d.n_heads, groups), dim3(256), 0, stream, batch,
+  if (groups > 65535 || d.n_heads % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(absorb_kernel, dim3(d.n_heads * 4, groups), dim3(256), 0, stream, batch,
                      d.n_heads, d.rope_base, static_cast<const uint16_t*>(q_nope),
                      static_cast<const uint16_t*>(q_pe), positions,
                      static_cast<const char*>(w_uk), static_cast<uint16_t*>(q_abs));
@@ -196,8 +207,8 @@ hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const v
 hipError_t out_proj_fast(const mla_dims& d, int batch, const float* o_latent, const void* w_uv,
                          float* out, hipStream_t stream) {
   const int groups = (batch + 63) / 64;
-  if (groups > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(out_proj_kernel, dim3(d.n_heads, groups), dim3(256), 0, stream, batch,
+  if (groups > 65535 || d.n_heads % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(out_proj_kernel, dim3(d.n_heads * (kDh / 16), groups), dim3(256), 0, stream, batch,
                      d.n_heads, o_latent, static_cast<const uint16_t*>(w_uv), out);
   return hipGetLastError();
 }

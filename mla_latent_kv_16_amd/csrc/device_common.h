@@ -36,4 +36,14 @@ __device__ __forceinline__ void store_elem(void* p, int64_t i, float v, bool is_
     static_cast<float*>(p)[i] = v;
 }
 
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// Two float32 -> bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 r;
+  r[0] = static_cast<__bf16>(a);
+  r[1] = static_cast<__bf16>(b);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 }  // namespace mla
