@@ -7,10 +7,12 @@ resident in HBM (the split plan is made once per batch shape, before timing).
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-flush]
                     [--no-cpu-baseline] [--copy-probe]
 
-Prints ONE JSON line on stdout; progress goes to stderr.  Between timed steps a
-512 MiB buffer is written (untimed) so the 256 MB last-level cache holds none
-of the cache rows.  Step and kernel times come from HIP events recorded on the
-stream the kernels run on.
+Prints ONE JSON line on stdout; progress goes to stderr.  Before every step a
+512 MiB buffer is read (a reduction, untimed), so the 256 MB last-level cache
+holds other data, as after the other layers of a model, and the step reads its
+cache rows from HBM.  The flush reads rather than writes so that the step does
+not also pay for writing back dirty flush lines.  Step and kernel times come
+from HIP events recorded on the stream the kernels run on.
 """
 from __future__ import annotations
 
@@ -153,8 +155,15 @@ def main():
         "lse": torch.empty((B, H), dtype=torch.float32, device="cuda"),
         "out": torch.empty((B, H, cfg.d_head), dtype=torch.float32, device="cuda"),
     }
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = None
+    if not args.no_flush:
+        flush = torch.full((128 << 20,), 1.0, dtype=torch.float32, device="cuda")  # 512 MiB
+        sink = torch.empty(1, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+
+    def evict():
+        if flush is not None:
+            torch.sum(flush, dim=0, keepdim=True, out=sink)
 
     def step(ev=None):
         if ev is not None:
@@ -175,8 +184,7 @@ def main():
             ev[4].record(stream)
 
     for _ in range(args.warmup):
-        if flush is not None:
-            flush.fill_(1)
+        evict()
         step()
     torch.cuda.synchronize()
 
@@ -184,8 +192,7 @@ def main():
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for k in range(args.steps):
-        if flush is not None:
-            flush.fill_(k & 0xff)
+        evict()
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0

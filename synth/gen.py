@@ -15,7 +15,7 @@ What one decode step receives, per sequence b of length L_b:
     i*d_h .. i*d_h + d_h - 1;
   * a block table and the sequence lengths.
 
-Value distributions (drawn directly; see the recipe notes in the design doc):
+Value distributions (drawn directly, in place of projecting hidden states):
   * c^KV_j: for RMS-normalised workloads, uniform on the sphere of radius
     sqrt(d_c) -- the law of an RMS-normalised isotropic Gaussian; otherwise
     N(0, 1) per component.
