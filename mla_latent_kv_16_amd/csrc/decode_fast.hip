@@ -13,10 +13,12 @@
 // Data movement
 //  * Rows stream HBM -> LDS with global_load_lds_dwordx4 (16 bytes per lane,
 //    no VGPR round trip) into a ring of 32-token slots (36,864 bytes each),
-//    three slices ahead of the one being consumed.  The 16-byte chunk `ch` of
-//    token row `t` sits at chunk position ch ^ swz(t) of that row in LDS (see
-//    swz).  Each lane picks which global chunk it fetches, so the swizzle
-//    costs nothing at load time.
+//    three slices ahead of the one being consumed.  A slot is stored as 4 x 9
+//    tiles of 8 rows x 128 bytes (1 KiB, one DMA instruction each); inside a
+//    tile the 16-byte chunk `ch` of row `t` sits at chunk position
+//    ch ^ swz(t) (see swz).  Each lane picks which global chunk it fetches,
+//    so the swizzle costs nothing at load time, and one per-lane offset plus
+//    a scalar base address every tile of a wave.
 //  * QK^T operands: a lane reads 16 contiguous bytes (8 latent values of one
 //    token) with ds_read_b128.
 //  * PV operands: C^T needs 8 tokens of one latent column per lane; two
@@ -56,7 +58,6 @@ namespace mla {
 namespace {
 
 constexpr int kRowBytes = kDq * 2;             // 1152
-constexpr int kChunksPerRow = kRowBytes / 16;  // 72
 constexpr int kSliceTok = 32;
 constexpr int kSlotBytes = kSliceTok * kRowBytes;  // 36,864
 constexpr int kStages = 4;
@@ -81,17 +82,20 @@ static_assert(kStages * kSlotBytes + kPBytes + 16 <= 163840, "LDS budget");
 
 #define MLA_VMCNT(n) (((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
-// Row swizzle: chunk position of logical chunk `ch` in LDS row `t` is
-// ch ^ swz(t), which permutes only within aligned groups of 8 chunks (a row is
-// 72 chunks).  LDS has 64 banks (256 bytes); a 1152-byte row advances the bank
-// position by half a period, so row parity picks the half.  With
-// swz(t) = j'(t >> 1), j'(j) = 2 (j % 4) + (j / 4) % 2:
-//  * 16 consecutive rows, one chunk (a ds_read_b128 quarter-wave of the QK^T
-//    reads): rows of equal parity get 8 distinct positions;
-//  * 8 consecutive rows x 2 adjacent chunks (a half-wave of the transposed PV
-//    reads): the 4 rows of equal parity give distinct chunk pairs.
-// Both patterns therefore touch 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int swz(int t) { return (((t >> 1) & 3) << 1) | ((t >> 3) & 1); }
+// Row swizzle: logical 16-byte chunk `ch` of LDS row `t` sits at chunk position
+// ch ^ swz(t), a permutation inside aligned groups of 8 chunks (a row has 72).
+// LDS has 64 four-byte banks; a 1152-byte row moves the bank position by half
+// of the 256-byte period, so row parity picks the half.  How gfx950 services a
+// wave (measured with the SQ_LDS_BANK_CONFLICT counter): ds_read_b128 takes 16
+// lanes per cycle, namely the lanes of one half-wave whose lane-index bits 2..4
+// have equal parity; ds_read_b64_tr_b16 takes one half-wave per cycle.
+// With swz(t) = 2 ((t >> 1) & 3):
+//  * QK^T reads, lane 16g + q reading row q, chunk 4k + g: in one cycle
+//    (q0, g0, q1 ^ g1, q2) takes all 16 values, so the 16 lanes hit 16
+//    distinct bank groups;
+//  * PV reads, row 4g + q/4, chunk 2c + q1, half q0: over a half-wave the
+//    8-byte bank pair (q2, q1, q3 ^ c0, g0 ^ c1, q0) takes all 32 values.
+__device__ __forceinline__ int swz(int t) { return ((t >> 1) & 3) << 1; }
 
 // Maximum / sum over the four lanes q, q+16, q+32, q+48 (the 16-lane rows of
 // a wave) with the gfx950 row-swap permutes: v_permlane16_swap exchanges rows
@@ -109,7 +113,9 @@ __device__ __forceinline__ float rows_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// 16 bytes per lane from `base + voff` into LDS at m0 + 16 * lane.
+// 16 bytes per lane from `base + voff` into LDS at m0 + 16 * lane.  (The
+// instruction's immediate offset is left at 0: it would move the LDS
+// destination as well.)
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr)
                : "memory");
@@ -177,18 +183,12 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
   if (threadIdx.x == 0) restart_flag = 0;
   __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
 
-  // --- per-lane DMA source: LDS chunk p = (9w + i) * 64 + lane of a slot holds
-  // logical chunk ch = (p % 72) ^ swz(t) of token t = p / 72.  The 9 byte
-  // offsets (< 36864) are kept two to a register.
-  uint32_t dma_pk[(kLoadsPerWave + 1) / 2] = {};
-#pragma unroll
-  for (int i = 0; i < kLoadsPerWave; ++i) {
-    const int p = (kLoadsPerWave * w + i) * 64 + lane;
-    const int t = p / kChunksPerRow;
-    const uint32_t off = static_cast<uint32_t>(t * kRowBytes + ((p % kChunksPerRow) ^ swz(t)) * 16);
-    dma_pk[i / 2] |= off << (16 * (i & 1));
-  }
-  auto dma_off = [&](int i) -> uint32_t { return (dma_pk[i / 2] >> (16 * (i & 1))) & 0xffffu; };
+  // --- DMA: wave w fetches rows 8w .. 8w+7 of a slice, tiles j = 0..8 (tile
+  // (w, j) at slot offset (9w + j) KiB).  Lane l covers row 8w + l/8 at chunk
+  // position l % 8 of the tile, i.e. logical chunk 8j + ((l % 8) ^ swz(l / 8)).
+  const int drow = 8 * w + (lane >> 3);
+  const uint32_t dma_lane =
+      static_cast<uint32_t>(drow * kRowBytes + ((lane & 7) ^ swz(lane >> 3)) * 16);
 
   auto issue = [&](int n) {
     const int tok0 = t_begin + n * kSliceTok;
@@ -196,34 +196,31 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
     const char* src = cache + static_cast<int64_t>(page) * (kPage * kRowBytes) +
                       (tok0 & (kPage - 1)) * kRowBytes;
     const uint32_t dst = lds_base + (n % kStages) * kSlotBytes + kLoadsPerWave * w * 1024;
+    // tail slice: rows of tokens >= nv are filled from token 0 of the slice
+    // (finite data, weight 0), so empty cache slots are never read.
     const int nv = t_end - tok0;
-    if (nv >= kSliceTok) {
+    const uint32_t voff = drow < nv ? dma_lane : dma_lane - drow * kRowBytes;
 #pragma unroll
-      for (int i = 0; i < kLoadsPerWave; ++i) dma16(src, dma_off(i), dst + i * 1024);
-    } else {
-      // tail slice: rows of tokens >= nv are filled from token 0 of the slice
-      // (finite data, weight 0), so empty cache slots are never read.
-#pragma unroll
-      for (int i = 0; i < kLoadsPerWave; ++i) {
-        const uint32_t off = dma_off(i);
-        const uint32_t t = off / kRowBytes;
-        dma16(src, static_cast<int>(t) < nv ? off : off - t * kRowBytes, dst + i * 1024);
-      }
-    }
+    for (int j = 0; j < kLoadsPerWave; ++j) dma16(src + 128 * j, voff, dst + 1024 * j);
   };
 
-  // --- per-lane LDS read offsets (within a slot)
+  // --- per-lane LDS read offsets (within a slot).  Row t, logical chunk c
+  // lives at tile (t / 8, c / 8): (9 (t / 8) + c / 8) KiB + 128 (t % 8) +
+  // 16 ((c % 8) ^ swz(t)); rows t and t + 16 are kRowGroup2 bytes apart.
+  constexpr uint32_t kTileRowGroup = 9 * 1024;
+  constexpr uint32_t kRowGroup2 = 2 * kTileRowGroup;
   const int sw = swz(q);  // rows q and q + 16 share it
   // scores A operand: token tb*16 + q, logical chunk 4ks + g
-  const uint32_t qk_off0 = q * kRowBytes + 16 * ((g) ^ sw);       // even ks
-  const uint32_t qk_off1 = q * kRowBytes + 16 * ((4 + g) ^ sw);   // odd ks
+  const uint32_t qk_base = (q >> 3) * kTileRowGroup + (q & 7) * 128;
+  const uint32_t qk_off0 = qk_base + 16 * ((g) ^ sw);       // even ks
+  const uint32_t qk_off1 = qk_base + 16 * ((4 + g) ^ sw);   // odd ks
   // PV A operand (transposed read): token 4g + q/4 (+16), column 16cb + 4(q%4)
   const int vrow = 4 * g + (q >> 2);
   const int vsw = swz(vrow);
-  const uint32_t pv_base = vrow * kRowBytes + 8 * (q & 1);
+  const uint32_t pv_base = (vrow >> 3) * kTileRowGroup + (vrow & 7) * 128 + 8 * (q & 1);
   const int pv_hc = (q & 3) >> 1;
   auto pv_off = [&](int cb) -> uint32_t {  // cb: global 16-column block 0..31
-    return pv_base + 128 * (cb >> 2) + 16 * ((2 * (cb & 3) + pv_hc) ^ vsw);
+    return pv_base + 1024 * (cb >> 2) + 16 * ((2 * (cb & 3) + pv_hc) ^ vsw);
   };
 
   float4_t oacc[8][kHeadBlocks];  // [latent block of this wave][head block]
@@ -241,7 +238,7 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
     constexpr int kSteps = 36, kAhead = MLA_QK_AHEAD;
     auto off_of = [&](int st) -> uint32_t {
       const int ks = st >> 1, tb = st & 1;
-      return tb * 16 * kRowBytes + 128 * (ks >> 1) + ((ks & 1) ? qk_off1 : qk_off0);
+      return tb * kRowGroup2 + 1024 * (ks >> 1) + ((ks & 1) ? qk_off1 : qk_off0);
     };
     bf16x8 fa[kAhead];
 #pragma unroll
@@ -355,14 +352,14 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
 #pragma unroll
       for (int c = 0; c < kAhead; ++c) {
         f0[c] = lds_read_tr(slot, pv_off(8 * w + c));
-        f1[c] = lds_read_tr(slot, pv_off(8 * w + c) + 16 * kRowBytes);
+        f1[c] = lds_read_tr(slot, pv_off(8 * w + c) + kRowGroup2);
       }
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const bf16x8 a = __builtin_shufflevector(f0[c % kAhead], f1[c % kAhead], 0, 1, 2, 3, 4, 5, 6, 7);
         if (c + kAhead < 8) {
           f0[c % kAhead] = lds_read_tr(slot, pv_off(8 * w + c + kAhead));
-          f1[c % kAhead] = lds_read_tr(slot, pv_off(8 * w + c + kAhead) + 16 * kRowBytes);
+          f1[c % kAhead] = lds_read_tr(slot, pv_off(8 * w + c + kAhead) + kRowGroup2);
         }
 #pragma unroll
         for (int hb = 0; hb < kHeadBlocks; ++hb)
