@@ -117,7 +117,9 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, const void* q_nope,
  * Each sequence's pages 0 .. ceil(L_b / page_size)-1 are cut into contiguous,
  * non-empty page ranges; every page of every sequence lands in exactly one item.
  * The item size is chosen so that about `num_slots` workgroups (CUs times
- * workgroups resident per CU) stay busy with even loads.
+ * workgroups resident per CU) stay busy with even loads; on the gfx950 fast
+ * path with 128 heads each item is decoded by two workgroups (one per half of
+ * the heads), so about num_slots / 2 items are made.
  * items_host [max_items][4] receives (b, split, page_begin, page_end) for items
  * 0 .. *num_items-1, grouped by sequence in order; split_offsets_host [batch + 1]
  * receives the CSR offsets.  Both are plain host memory owned by the caller.

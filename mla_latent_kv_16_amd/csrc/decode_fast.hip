@@ -13,7 +13,7 @@
 // Data movement
 //  * Rows stream HBM -> LDS with global_load_lds_dwordx4 (16 bytes per lane,
 //    no VGPR round trip) into a ring of 32-token slots (36,864 bytes each),
-//    three slices ahead of the one being consumed.  A slot is stored as 4 x 9
+//    two slices ahead of the one being scored.  A slot is stored as 4 x 9
 //    tiles of 8 rows x 128 bytes (1 KiB, one DMA instruction each); inside a
 //    tile the 16-byte chunk `ch` of row `t` sits at chunk position
 //    ch ^ swz(t) (see swz).  Each lane picks which global chunk it fetches,
@@ -27,24 +27,22 @@
 //    permuted (k -> token sigma(g, k), see below) so that the QK^T
 //    accumulators of a lane already hold the P^T operand of the same lane.
 //
-// Work split inside a workgroup (4 waves, one per SIMD), H = 128:
-//  * scores: wave w owns heads 32w .. 32w+31 over every token (its Q
-//    fragments stay in 144 VGPRs); it turns them into bf16 weights and puts
-//    them in an 8 KiB LDS exchange buffer;
-//  * latent PV: wave w owns latent columns 128w .. 128w+127 for all 128 heads
-//    (256 accumulator registers), so each transposed C^T fragment feeds 8
-//    MFMAs.  LDS transposed reads cost as much issue time as 16-byte reads but
-//    move half the bytes; this split issues a quarter of them compared with
-//    giving each wave its heads' full 512 columns.
-//  Two workgroup barriers per slice: ring hand-over and weight exchange.
+// Work split, H = 128: two workgroups per work item, one per half of the
+// heads (see decode_h128_kernel), each with eight waves in two roles:
+//  * S waves: scores of 16 heads over every token (Q fragments stay in 72
+//    VGPRs), turned into bf16 weights and put in a 4 KiB LDS exchange buffer;
+//  * V waves: the DMA and the latent PV of 128 columns for the workgroup's 64
+//    heads (128 accumulators), so each transposed C^T fragment feeds 4 MFMAs.
+//  The V waves run one slice behind the S waves; one workgroup barrier per
+//  slice.
 //
 // Softmax in base 2 against a fixed reference per head: the maximum of the
 // item's first slice.  Weights 2^(x - m_ref) may exceed 1 by up to 2^20, which
 // float32 accumulators and bf16 weights carry without loss of relative
-// precision, so the 256 accumulators are never rescaled in registers.  If a
+// precision, so the accumulators are never rescaled in registers.  If a
 // later slice exceeds the reference by more than that, the workgroup agrees on
-// it through an LDS flag at the next barrier, takes the exact per-head maxima in
-// a scores-only pass and redoes the item against them; the result is the same
+// it through an LDS vote after the pass, takes the exact per-head maxima in a
+// scores-only pass and redoes the item against them; the result is the same
 // softmax either way.
 #include <math.h>
 #include <stdlib.h>
@@ -61,10 +59,8 @@ constexpr int kRowBytes = kDq * 2;             // 1152
 constexpr int kSliceTok = 32;
 constexpr int kSlotBytes = kSliceTok * kRowBytes;  // 36,864
 constexpr int kStages = 4;
-constexpr int kWaves = 4;
-constexpr int kLoadsPerWave = kSlotBytes / 1024 / kWaves;  // 9 instructions of 1 KiB
-constexpr int kHeadBlocks = 8;                              // 128 heads / 16
-constexpr int kPBytes = kHeadBlocks * 64 * 16;              // weight exchange, 8 KiB
+constexpr int kDmaWaves = 4;
+constexpr int kLoadsPerWave = kSlotBytes / 1024 / kDmaWaves;  // 9 instructions of 1 KiB
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kMaxJumpDefault = 20.0f;  // log2 units; see the softmax note above
@@ -76,9 +72,11 @@ constexpr float kMaxJumpDefault = 20.0f;  // log2 units; see the softmax note ab
 #ifndef MLA_PV_AHEAD
 #define MLA_PV_AHEAD 2
 #endif
+#ifndef MLA_S_PRIO
+#define MLA_S_PRIO 3
+#endif
 
-static_assert(kSlotBytes % (1024 * kWaves) == 0, "slot must split evenly over the waves");
-static_assert(kStages * kSlotBytes + kPBytes + 16 <= 163840, "LDS budget");
+static_assert(kSlotBytes % (1024 * kDmaWaves) == 0, "slot must split evenly over the waves");
 
 #define MLA_VMCNT(n) (((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
 
@@ -132,7 +130,19 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* lds, uint32_t off) {
 }
 
 // ---------------------------------------------------------------------------
-// H = 128.
+// H = 128, two workgroups per work item: workgroup half hh takes heads
+// 64hh .. 64hh+63.  Both stream the same rows; the second read of a row is
+// served by the L2 of the XCD they share (blocks i and i + 8 run on one XCD
+// and are dispatched together).  Eight waves, two per SIMD, in two roles:
+//  * S waves (w = 0..3): scores and softmax of head block r = w (16 heads,
+//    Q fragments in 72 VGPRs);
+//  * V waves (w = 4..7): the DMA of row group r = w - 4 and the latent PV of
+//    columns 128r .. 128r+127 for all 64 heads (128 accumulators).
+// Iteration k: S waves score slice k and publish its weights; V waves
+// accumulate slice k-1 with the weights published one iteration earlier.  One
+// workgroup barrier per iteration; the two waves sharing a SIMD overlap their
+// MFMA, LDS and VALU work.
+//
 // MFMA operand layouts (v_mfma_f32_16x16x32_bf16, lane l, g = l / 16, q = l % 16):
 //   A[m][k]: lane holds m = q, k = 8g .. 8g+7;  B[k][n]: k = 8g .. 8g+7, n = q;
 //   C[m][n]: lane holds m = 4g + i (i = 0..3), n = q.
@@ -142,24 +152,47 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* lds, uint32_t off) {
 // reduction index k = 8g + j standing for token sigma(g, j) = 4g + j (j < 4) or
 // 16 + 4g + (j - 4) (j >= 4): exactly the tokens whose weights lane l holds.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 1) void decode_h128_kernel(
+constexpr int kHeadsWG = 64;
+constexpr int kHeadBlocksWG = kHeadsWG / 16;     // 4
+constexpr int kPBytesWG = kHeadBlocksWG * 64 * 16;  // 4 KiB of weights per slice
+static_assert(kStages * kSlotBytes + 2 * kPBytesWG + 4 * 4 + kHeadsWG * 4 <= 163840, "LDS budget");
+
+__global__ __launch_bounds__(512, 1) void decode_h128_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ items, float scale, float max_jump, float* __restrict__ o_part,
-    float* __restrict__ lse_part) {
+    const int32_t* __restrict__ items, int num_items, float scale, float max_jump,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
   constexpr int H = 128;
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes + kPBytes];
-  __shared__ int restart_flag;
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes + 2 * kPBytesWG];
+  __shared__ int votes[4];              // after a pass: jump flags of the S waves
+  __shared__ float lsum[kHeadsWG];      // epilogue: row sums
   char* const pbuf = lds + kStages * kSlotBytes;
   const uint32_t lds_base =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool v_role = w >= 4;
+  const int r = w & 3;
   const int g = lane >> 4;   // lane group (k block of the MFMA operands)
   const int q = lane & 15;   // row/column within a 16-block
 
-  const int it = blockIdx.x;
+  // block -> (item, half): blocks 16m + j and 16m + j + 8 (j < 8) take the two
+  // halves of item 8m + j; a last incomplete group of items is laid out the
+  // same way over the blocks that remain.
+  int it, hh;
+  {
+    const int blk = blockIdx.x;
+    const int full = num_items & ~7;
+    if (blk < 2 * full) {
+      it = (blk >> 4) * 8 + (blk & 7);
+      hh = (blk >> 3) & 1;
+    } else {
+      const int j = blk - 2 * full, rest = num_items - full;
+      it = full + j % rest;
+      hh = j / rest;
+    }
+  }
   const int b = items[4 * it];
   const int p0 = items[4 * it + 2];
   const int p1 = items[4 * it + 3];
@@ -168,254 +201,260 @@ __global__ __launch_bounds__(256, 1) void decode_h128_kernel(
   const int t_end = min(p1 * kPage, L);
   const int n_slices = (t_end - t_begin + kSliceTok - 1) / kSliceTok;
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
+  const int head0 = kHeadsWG * hh;
 
-  // --- Q fragments (B operand of the scores): lane holds head 32w + 16hb + q,
-  // values 32ks + 8g .. +8.
-  bf16x8 qf[2][18];
-  {
-    const uint16_t* qrow0 = q_abs + (static_cast<int64_t>(b) * H + 32 * w + q) * kDq + 8 * g;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks)
-        qf[hb][ks] = *reinterpret_cast<const bf16x8*>(qrow0 + hb * 16 * kDq + 32 * ks);
-  }
-  if (threadIdx.x == 0) restart_flag = 0;
-  __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+  auto slot_of = [&](int n) -> const char* { return lds + (n % kStages) * kSlotBytes; };
+  auto pbuf_of = [&](int n) -> char* { return pbuf + (n & 1) * kPBytesWG; };
 
-  // --- DMA: wave w fetches rows 8w .. 8w+7 of a slice, tiles j = 0..8 (tile
-  // (w, j) at slot offset (9w + j) KiB).  Lane l covers row 8w + l/8 at chunk
-  // position l % 8 of the tile, i.e. logical chunk 8j + ((l % 8) ^ swz(l / 8)).
-  const int drow = 8 * w + (lane >> 3);
-  const uint32_t dma_lane =
-      static_cast<uint32_t>(drow * kRowBytes + ((lane & 7) ^ swz(lane >> 3)) * 16);
-
-  auto issue = [&](int n) {
-    const int tok0 = t_begin + n * kSliceTok;
-    const int page = bt[tok0 >> 6];
-    const char* src = cache + static_cast<int64_t>(page) * (kPage * kRowBytes) +
-                      (tok0 & (kPage - 1)) * kRowBytes;
-    const uint32_t dst = lds_base + (n % kStages) * kSlotBytes + kLoadsPerWave * w * 1024;
-    // tail slice: rows of tokens >= nv are filled from token 0 of the slice
-    // (finite data, weight 0), so empty cache slots are never read.
-    const int nv = t_end - tok0;
-    const uint32_t voff = drow < nv ? dma_lane : dma_lane - drow * kRowBytes;
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j) dma16(src + 128 * j, voff, dst + 1024 * j);
-  };
-
-  // --- per-lane LDS read offsets (within a slot).  Row t, logical chunk c
-  // lives at tile (t / 8, c / 8): (9 (t / 8) + c / 8) KiB + 128 (t % 8) +
-  // 16 ((c % 8) ^ swz(t)); rows t and t + 16 are kRowGroup2 bytes apart.
+  // Slot layout: row t, logical chunk c at tile (t / 8, c / 8): (9 (t / 8) +
+  // c / 8) KiB + 128 (t % 8) + 16 ((c % 8) ^ swz(t)); rows t and t + 16 are
+  // kRowGroup2 bytes apart.
   constexpr uint32_t kTileRowGroup = 9 * 1024;
   constexpr uint32_t kRowGroup2 = 2 * kTileRowGroup;
-  const int sw = swz(q);  // rows q and q + 16 share it
-  // scores A operand: token tb*16 + q, logical chunk 4ks + g
-  const uint32_t qk_base = (q >> 3) * kTileRowGroup + (q & 7) * 128;
-  const uint32_t qk_off0 = qk_base + 16 * ((g) ^ sw);       // even ks
-  const uint32_t qk_off1 = qk_base + 16 * ((4 + g) ^ sw);   // odd ks
-  // PV A operand (transposed read): token 4g + q/4 (+16), column 16cb + 4(q%4)
-  const int vrow = 4 * g + (q >> 2);
-  const int vsw = swz(vrow);
-  const uint32_t pv_base = (vrow >> 3) * kTileRowGroup + (vrow & 7) * 128 + 8 * (q & 1);
-  const int pv_hc = (q & 3) >> 1;
-  auto pv_off = [&](int cb) -> uint32_t {  // cb: global 16-column block 0..31
-    return pv_base + 1024 * (cb >> 2) + 16 * ((2 * (cb & 3) + pv_hc) ^ vsw);
-  };
 
-  float4_t oacc[8][kHeadBlocks];  // [latent block of this wave][head block]
-  float m_ref[2], l_run[2];
-  const float c2 = scale * kLog2e;
+  // Every wave runs the same sequence of workgroup barriers: per pass, one per
+  // iteration, plus the ones named below.
 
-  // S^T[32 tokens x 32 heads] of one slot = Rows . Q^T.  36 steps (ks, tb); LDS
-  // reads run kAhead steps ahead of their MFMAs; scheduling fences keep the
-  // compiler from hoisting more of them.
-  auto scores = [&](const char* slot, float4_t (&sacc)[2][2]) {
+  if (!v_role) {
+    // ======================= S waves: scores and softmax =======================
+    // The S waves are the critical path (their softmax cannot overlap their own
+    // MFMAs); a higher issue priority lets the V waves' MFMAs fill the gaps.
+    __builtin_amdgcn_s_setprio(MLA_S_PRIO);
+    bf16x8 qf[18];  // B operand: head head0 + 16r + q, values 32ks + 8g .. +8
+    {
+      const uint16_t* qrow = q_abs + (static_cast<int64_t>(b) * H + head0 + 16 * r + q) * kDq + 8 * g;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) sacc[tb][hb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    constexpr int kSteps = 36, kAhead = MLA_QK_AHEAD;
-    auto off_of = [&](int st) -> uint32_t {
-      const int ks = st >> 1, tb = st & 1;
-      return tb * kRowGroup2 + 1024 * (ks >> 1) + ((ks & 1) ? qk_off1 : qk_off0);
-    };
-    bf16x8 fa[kAhead];
-#pragma unroll
-    for (int st = 0; st < kAhead; ++st) fa[st] = lds_read128(slot, off_of(st));
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      const int ks = st >> 1, tb = st & 1;
-      const bf16x8 a = fa[st % kAhead];
-      if (st + kAhead < kSteps) fa[st % kAhead] = lds_read128(slot, off_of(st + kAhead));
-      sacc[tb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][ks], sacc[tb][0], 0, 0, 0);
-      sacc[tb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][ks], sacc[tb][1], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
     }
-  };
+    const int sw = swz(q);  // rows q and q + 16 share it
+    const uint32_t qk_base = (q >> 3) * kTileRowGroup + (q & 7) * 128;
+    const uint32_t qk_off0 = qk_base + 16 * ((g) ^ sw);      // even ks: logical chunk 8(ks/2) + g
+    const uint32_t qk_off1 = qk_base + 16 * ((4 + g) ^ sw);  // odd ks: logical chunk 8(ks/2) + 4 + g
+    const float c2 = scale * kLog2e;
+    float m_ref = -INFINITY, l_run = 0.f;
 
-  // Per-head maximum of the slice's scores in log2 units (scale folded in);
-  // tokens past the end of the item (tail slice only) are set to -inf.
-  auto slice_max = [&](float4_t (&sacc)[2][2], int nv, float (&mx)[2]) {
-    if (nv < kSliceTok) {
+    // S^T[32 tokens x 16 heads] of one slot, log2 units (scale folded in);
+    // tokens of the slice at or past `nv` are -inf.  Four accumulator chains
+    // (token block x k parity), LDS reads kAhead steps ahead.
+    auto scores = [&](const char* slot, int nv, float (&s)[2][4]) {
+      float4_t acc[2][2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) acc[tb][0] = acc[tb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+      constexpr int kSteps = 36, kAhead = MLA_QK_AHEAD;
+      auto off_of = [&](int st) -> uint32_t {
+        const int ks = st >> 1, tb = st & 1;
+        return tb * kRowGroup2 + 1024 * (ks >> 1) + ((ks & 1) ? qk_off1 : qk_off0);
+      };
+      bf16x8 fa[kAhead];
+#pragma unroll
+      for (int st = 0; st < kAhead; ++st) fa[st] = lds_read128(slot, off_of(st));
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        const int ks = st >> 1, tb = st & 1;
+        const bf16x8 a = fa[st % kAhead];
+        if (st + kAhead < kSteps) fa[st % kAhead] = lds_read128(slot, off_of(st + kAhead));
+        acc[tb][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc[tb][ks & 1], 0, 0, 0);
+      }
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
+        for (int i = 0; i < 4; ++i) {
+          const float v = (acc[tb][0][i] + acc[tb][1][i]) * c2;
+          s[tb][i] = (tb * 16 + 4 * g + i < nv) ? v : -INFINITY;
+        }
+    };
+    auto lane_max = [&](const float (&s)[2][4]) {
+      return fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    };
+    auto nvalid = [&](int n) { return min(kSliceTok, t_end - (t_begin + n * kSliceTok)); };
+    // weights 2^(s - m_ref) of slice k (masked tokens: 2^-inf = 0) into its buffer
+    auto publish = [&](int k, const float (&s)[2][4]) {
+      uint32_t pk[4];
+      float sum[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (tb * 16 + 4 * g + i >= nv) sacc[tb][hb][i] = -INFINITY;
-    }
+      for (int tb = 0; tb < 2; ++tb) {
+        float p[4];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float m = fmaxf(fmaxf(fmaxf(sacc[0][hb][0], sacc[0][hb][1]), fmaxf(sacc[0][hb][2], sacc[0][hb][3])),
-                      fmaxf(fmaxf(sacc[1][hb][0], sacc[1][hb][1]), fmaxf(sacc[1][hb][2], sacc[1][hb][3])));
-      mx[hb] = rows_max(m) * c2;
-    }
-  };
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[tb][i] - m_ref);
+        sum[tb] = (p[0] + p[1]) + (p[2] + p[3]);
+        pk[2 * tb] = pack_bf16x2(p[0], p[1]);
+        pk[2 * tb + 1] = pack_bf16x2(p[2], p[3]);
+      }
+      l_run += sum[0] + sum[1];
+      *reinterpret_cast<bf16x8*>(pbuf_of(k) + (r * 64 + lane) * 16) = __builtin_bit_cast(bf16x8, pk);
+    };
 
-  // One pass over the item's slices through the LDS ring.
-  //  kFull = true:  scores, weights p = 2^(s c2 - m_ref), O += C^T P^T.  With
-  //                 `first` the reference m_ref is the first slice's maximum and
-  //                 a jump beyond max_jump aborts the pass (returns false).
-  //  kFull = false: scores only, m_ref = exact per-head maximum.
-  // Every wave executes the same barriers in every case.
-  auto run_pass = [&](auto full_tag, bool first) -> bool {
-    constexpr bool kFull = decltype(full_tag)::value;
-    for (int n = 0; n < kStages - 1 && n < n_slices; ++n) issue(n);
-    bool aborted = false;
-    for (int n = 0; n < n_slices; ++n) {
-      const int ahead = min(kStages - 2, n_slices - 1 - n);
-      if (ahead >= 2)
-        __builtin_amdgcn_s_waitcnt(MLA_VMCNT(2 * kLoadsPerWave));
-      else if (ahead == 1)
+    // Full pass.  With `first`, m_ref is the first slice's per-head maximum and
+    // the lane keeps a running maximum of its later scores; the pass is
+    // discarded (returns false) if some head's maximum exceeds m_ref by more
+    // than max_jump.  Slices 1 .. n-2 are whole, so only the first and the
+    // last one are masked.
+    auto full_pass = [&](bool first) -> bool {
+      float m_lane = -INFINITY;
+      float s[2][4];
+      __syncthreads();
+      scores(slot_of(0), nvalid(0), s);
+      if (first) m_ref = rows_max(lane_max(s));
+      publish(0, s);
+      for (int k = 1; k < n_slices - 1; ++k) {
+        __syncthreads();
+        scores(slot_of(k), kSliceTok, s);
+        if (first) m_lane = fmaxf(m_lane, lane_max(s));
+        publish(k, s);
+      }
+      if (n_slices > 1) {
+        __syncthreads();
+        scores(slot_of(n_slices - 1), nvalid(n_slices - 1), s);
+        if (first) m_lane = fmaxf(m_lane, lane_max(s));
+        publish(n_slices - 1, s);
+      }
+      __syncthreads();
+      // vote: did a head of any S wave jump?
+      const bool mine = __any(first && rows_max(m_lane) > m_ref + max_jump);
+      if (lane == 0) votes[r] = mine ? 1 : 0;
+      __syncthreads();
+      const bool any = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+      __syncthreads();
+      return !any;
+    };
+
+    if (!full_pass(true)) {
+      // A head's maximum jumped by more than max_jump: exact maxima first,
+      // then the item again against them (every weight <= 1).
+      m_ref = -INFINITY;
+      for (int k = 0; k < n_slices; ++k) {
+        __syncthreads();
+        float s[2][4];
+        scores(slot_of(k), nvalid(k), s);
+        m_ref = fmaxf(m_ref, rows_max(lane_max(s)));
+      }
+      __syncthreads();
+      l_run = 0.f;
+      full_pass(false);
+    }
+    // epilogue: row sums to LDS and the partial log-sum-exp
+    const float l = rows_sum(l_run);
+    if (g == 0) {
+      lsum[16 * r + q] = l;
+      lse_part[static_cast<int64_t>(it) * H + head0 + 16 * r + q] = m_ref * kLn2 + logf(l);
+    }
+    __syncthreads();
+  } else {
+    // ======================= V waves: DMA and latent PV =======================
+    // DMA: this wave fetches rows 8r .. 8r+7 of a slice, tiles j = 0..8 (tile
+    // (r, j) at slot offset (9r + j) KiB).  Lane l covers row 8r + l/8 at chunk
+    // position l % 8 of the tile, i.e. logical chunk 8j + ((l % 8) ^ swz(l / 8)).
+    const int drow = 8 * r + (lane >> 3);
+    const uint32_t dma_lane =
+        static_cast<uint32_t>(drow * kRowBytes + ((lane & 7) ^ swz(lane >> 3)) * 16);
+    auto issue = [&](int n) {
+      const int tok0 = t_begin + n * kSliceTok;
+      const int page = bt[tok0 >> 6];
+      const char* src = cache + static_cast<int64_t>(page) * (kPage * kRowBytes) +
+                        (tok0 & (kPage - 1)) * kRowBytes;
+      const uint32_t dst = lds_base + (n % kStages) * kSlotBytes + kLoadsPerWave * r * 1024;
+      // tail slice: rows of tokens >= nv are filled from token 0 of the slice
+      // (finite data, weight 0), so empty cache slots are never read.
+      const int nv = t_end - tok0;
+      const uint32_t voff = drow < nv ? dma_lane : dma_lane - drow * kRowBytes;
+#pragma unroll
+      for (int j = 0; j < kLoadsPerWave; ++j) dma16(src + 128 * j, voff, dst + 1024 * j);
+    };
+    // wait for this wave's part of slice k (slice k+1 may stay in flight)
+    auto wait_slice = [&](int k) {
+      if (k + 1 < n_slices)
         __builtin_amdgcn_s_waitcnt(MLA_VMCNT(kLoadsPerWave));
       else
         __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
-      __syncthreads();  // (A) slice n landed; slot of n-1 and the weight buffer are free
-      if (kFull && first && restart_flag) {  // same value in every wave after the barrier
-        aborted = true;
-        break;
-      }
-      if (n + kStages - 1 < n_slices) issue(n + kStages - 1);
+    };
 
-      const char* slot = lds + (n % kStages) * kSlotBytes;
-      const int nv = min(kSliceTok, t_end - (t_begin + n * kSliceTok));
-      float4_t sacc[2][2];
-      scores(slot, sacc);
-      float mx[2];
-      slice_max(sacc, nv, mx);
-      if (!kFull) {
-        m_ref[0] = fmaxf(m_ref[0], mx[0]);
-        m_ref[1] = fmaxf(m_ref[1], mx[1]);
-        continue;
-      }
-      if (first) {
-        if (n == 0) {
-          m_ref[0] = mx[0];
-          m_ref[1] = mx[1];
-        }
-        if (__any(mx[0] > m_ref[0] + max_jump || mx[1] > m_ref[1] + max_jump) && lane == 0)
-          restart_flag = 1;  // this pass will be discarded at the next barrier (A)
-      }
-      // weights p = 2^(s c2 - m_ref) (masked tokens: 2^-inf = 0), packed to bf16
-      // in the token order sigma(g, .) and handed over through LDS
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        uint32_t pk[4];
-        float sum = 0.f;
-        const float neg_m = -m_ref[hb];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          float p[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[i] = __builtin_amdgcn_exp2f(fmaf(sacc[tb][hb][i], c2, neg_m));
-            sum += p[i];
-          }
-          pk[2 * tb] = pack_bf16x2(p[0], p[1]);
-          pk[2 * tb + 1] = pack_bf16x2(p[2], p[3]);
-        }
-        l_run[hb] += sum;
-        *reinterpret_cast<bf16x8*>(pbuf + ((2 * w + hb) * 64 + lane) * 16) =
-            __builtin_bit_cast(bf16x8, pk);
-      }
-      __syncthreads();  // (B) every head block's weights are in the buffer
+    // PV A operand (transposed read): token 4g + q/4 (+16), column 16cb + 4(q%4)
+    const int vrow = 4 * g + (q >> 2);
+    const int vsw = swz(vrow);
+    const uint32_t pv_base = (vrow >> 3) * kTileRowGroup + (vrow & 7) * 128 + 8 * (q & 1);
+    const int pv_hc = (q & 3) >> 1;
+    auto pv_off = [&](int cb) -> uint32_t {  // cb: global 16-column block 0..31
+      return pv_base + 1024 * (cb >> 2) + 16 * ((2 * (cb & 3) + pv_hc) ^ vsw);
+    };
 
-      // O^T[128 columns of this wave x 128 heads] += C^T . P^T
-      bf16x8 pf[kHeadBlocks];
+    float4_t oacc[8][kHeadBlocksWG];  // [latent block of this wave][head block]
+    auto zero_acc = [&]() {
 #pragma unroll
-      for (int hb = 0; hb < kHeadBlocks; ++hb)
-        pf[hb] = *reinterpret_cast<const bf16x8*>(pbuf + (hb * 64 + lane) * 16);
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int hb = 0; hb < kHeadBlocksWG; ++hb) oacc[c][hb] = float4_t{0.f, 0.f, 0.f, 0.f};
+    };
+    // O^T[128 columns x 64 heads] += C^T . P^T for one slice
+    auto accumulate = [&](const char* slot, const char* pb) {
+      bf16x8 pf[kHeadBlocksWG];
+#pragma unroll
+      for (int hb = 0; hb < kHeadBlocksWG; ++hb)
+        pf[hb] = *reinterpret_cast<const bf16x8*>(pb + (hb * 64 + lane) * 16);
       constexpr int kAhead = MLA_PV_AHEAD;
       bf16x4 f0[kAhead], f1[kAhead];
 #pragma unroll
       for (int c = 0; c < kAhead; ++c) {
-        f0[c] = lds_read_tr(slot, pv_off(8 * w + c));
-        f1[c] = lds_read_tr(slot, pv_off(8 * w + c) + kRowGroup2);
+        f0[c] = lds_read_tr(slot, pv_off(8 * r + c));
+        f1[c] = lds_read_tr(slot, pv_off(8 * r + c) + kRowGroup2);
       }
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const bf16x8 a = __builtin_shufflevector(f0[c % kAhead], f1[c % kAhead], 0, 1, 2, 3, 4, 5, 6, 7);
         if (c + kAhead < 8) {
-          f0[c % kAhead] = lds_read_tr(slot, pv_off(8 * w + c + kAhead));
-          f1[c % kAhead] = lds_read_tr(slot, pv_off(8 * w + c + kAhead) + kRowGroup2);
+          f0[c % kAhead] = lds_read_tr(slot, pv_off(8 * r + c + kAhead));
+          f1[c % kAhead] = lds_read_tr(slot, pv_off(8 * r + c + kAhead) + kRowGroup2);
         }
 #pragma unroll
-        for (int hb = 0; hb < kHeadBlocks; ++hb)
+        for (int hb = 0; hb < kHeadBlocksWG; ++hb)
           oacc[c][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[hb], oacc[c][hb], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    auto full_pass = [&]() -> bool {
+      issue(0);
+      if (n_slices > 1) issue(1);
+      for (int k = 0; k <= n_slices; ++k) {
+        if (k < n_slices) wait_slice(k);
+        __syncthreads();
+        if (k + 2 < n_slices) issue(k + 2);
+        if (k >= 1) accumulate(slot_of(k - 1), pbuf_of(k - 1));
+      }
+      // vote (written by the S waves)
+      __syncthreads();
+      const bool any = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+      __syncthreads();
+      return !any;
+    };
+
+    zero_acc();
+    if (!full_pass()) {
+      // exact-maximum pass of the S waves: stream the slices again
+      issue(0);
+      if (n_slices > 1) issue(1);
+      for (int k = 0; k < n_slices; ++k) {
+        wait_slice(k);
+        __syncthreads();
+        if (k + 2 < n_slices) issue(k + 2);
+      }
+      __syncthreads();
+      zero_acc();
+      full_pass();
     }
-    if (aborted) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));  // loads of abandoned slices
-    __syncthreads();  // ring free again; restart_flag final
-    return !(kFull && first && restart_flag);
-  };
-
-  auto zero_state = [&]() {
+    // epilogue: normalise by the row sums of the S waves and write the partial
+    __syncthreads();
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int hb = 0; hb < kHeadBlocksWG; ++hb) {
+      const float inv = 1.f / lsum[16 * hb + q];
+      float* orow = o_part + (static_cast<int64_t>(it) * H + head0 + 16 * hb + q) * kDc + 128 * r + 4 * g;
 #pragma unroll
-      for (int hb = 0; hb < kHeadBlocks; ++hb) oacc[c][hb] = float4_t{0.f, 0.f, 0.f, 0.f};
-    l_run[0] = l_run[1] = 0.f;
-  };
-
-  zero_state();
-  if (!run_pass(std::integral_constant<bool, true>{}, true)) {
-    // A head's maximum jumped by more than max_jump: take the exact maxima
-    // first, then redo the item with them (every weight <= 1).
-    m_ref[0] = m_ref[1] = -INFINITY;
-    run_pass(std::integral_constant<bool, false>{}, false);
-    zero_state();
-    run_pass(std::integral_constant<bool, true>{}, false);
-  }
-
-  // ---- epilogue: row sums of the wave's own heads to LDS, then every wave
-  // normalises its 128 columns for all heads and writes the partial.
-  float* lsum = reinterpret_cast<float*>(pbuf);  // [128], reuses the weight buffer
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const float l = rows_sum(l_run[hb]);
-    const int head = 32 * w + 16 * hb + q;
-    if (g == 0) {
-      lsum[head] = l;
-      lse_part[static_cast<int64_t>(it) * H + head] = m_ref[hb] * kLn2 + logf(l);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int hb = 0; hb < kHeadBlocks; ++hb) {
-    const int head = 16 * hb + q;
-    const float inv = 1.f / lsum[head];
-    float* orow = o_part + (static_cast<int64_t>(it) * H + head) * kDc + 128 * w + 4 * g;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float4_t v = oacc[c][hb];
-      v[0] *= inv;
-      v[1] *= inv;
-      v[2] *= inv;
-      v[3] *= inv;
-      *reinterpret_cast<float4_t*>(orow + 16 * c) = v;
+      for (int c = 0; c < 8; ++c) {
+        float4_t v = oacc[c][hb];
+        v[0] *= inv;
+        v[1] *= inv;
+        v[2] *= inv;
+        v[3] *= inv;
+        *reinterpret_cast<float4_t*>(orow + 16 * c) = v;
+      }
     }
   }
 }
@@ -437,10 +476,10 @@ hipError_t decode_fast(const mla_dims& d, const void* q_abs, const void* kv_cach
                        const int32_t* items, int num_items, float* o_part, float* lse_part,
                        hipStream_t stream) {
   if (d.n_heads == 128) {
-    hipLaunchKernelGGL(decode_h128_kernel, dim3(num_items), dim3(256), 0, stream,
+    hipLaunchKernelGGL(decode_h128_kernel, dim3(2 * num_items), dim3(512), 0, stream,
                        static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
-                       block_table, max_pages, seq_lens, items, d.softmax_scale, max_jump(),
-                       o_part, lse_part);
+                       block_table, max_pages, seq_lens, items, num_items, d.softmax_scale,
+                       max_jump(), o_part, lse_part);
     return hipGetLastError();
   }
   return decode_generic(d, q_abs, kv_cache, block_table, max_pages, seq_lens, items, num_items,

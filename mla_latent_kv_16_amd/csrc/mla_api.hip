@@ -93,7 +93,11 @@ mla_status mla_plan_splits(const mla_dims* dims, int32_t batch, const int32_t* s
                            int32_t* split_offsets_host, int32_t* num_items) {
   mla_status s = check_dims(dims);
   if (s != MLA_OK) return s;
-  return plan_splits(dims->page_size, batch, seq_lens_host, num_slots, max_items, items_host,
+  // With 128 heads the fast decode gives every item two workgroups (one per half
+  // of the heads), so about num_slots / 2 items fill the machine.
+  const int per_item = (is_fast_shape(*dims) && dims->n_heads == 128) ? 2 : 1;
+  const int slots = num_slots >= per_item ? num_slots / per_item : num_slots;
+  return plan_splits(dims->page_size, batch, seq_lens_host, slots, max_items, items_host,
                      split_offsets_host, num_items, dims->n_heads);
 }
 

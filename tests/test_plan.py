@@ -36,11 +36,14 @@ def test_plan_edges(lens):
 
 
 def test_plan_headline_shapes():
-    # uniform lengths that divide evenly fill the machine with equal items
+    # uniform lengths that divide evenly fill the machine with equal items; at
+    # 128 heads each item takes two workgroups, so 256 slots make 128 items
     items, offs = mla.plan_splits(V2, [8192] * 64, 256)
-    assert len(items) == 256 and np.all(items[:, 3] - items[:, 2] == 32)
+    assert len(items) == 128 and np.all(items[:, 3] - items[:, 2] == 64)
     items, offs = mla.plan_splits(V2, [131072] * 8, 256)
-    assert len(items) == 256 and np.all(items[:, 3] - items[:, 2] == 64)
+    assert len(items) == 128 and np.all(items[:, 3] - items[:, 2] == 128)
+    items, offs = mla.plan_splits(LITE, [4096] * 32, 256)
+    assert len(items) == 256 and np.all(items[:, 3] - items[:, 2] == 8)
     L = seq_lens(CONFIGS["v2_varlen_b128"])
     items, offs = mla.plan_splits(V2, L, 256)
     check_plan(L, items, offs)
@@ -64,7 +67,7 @@ def test_plan_capacity_error_reports_need():
     n = ctypes.c_int32(0)
     st = lib.mla_plan_splits(ctypes.byref(V2.c()), 64, lens.ctypes.data_as(pi32), 256, 10,
                              items.ctypes.data_as(pi32), offs.ctypes.data_as(pi32), ctypes.byref(n))
-    assert st == -3 and n.value == 256
+    assert st == -3 and n.value == 128   # two workgroups per item at 128 heads
     assert not items.any() and not offs.any()
 
 
