@@ -67,7 +67,7 @@ constexpr float kMaxJumpDefault = 20.0f;  // log2 units; see the softmax note ab
 
 // Pipelining depths (steps of LDS reads issued ahead of their MFMAs).
 #ifndef MLA_QK_AHEAD
-#define MLA_QK_AHEAD 8
+#define MLA_QK_AHEAD 4
 #endif
 #ifndef MLA_PV_AHEAD
 #define MLA_PV_AHEAD 2
@@ -133,47 +133,51 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* lds, uint32_t off) {
 // H = 128, two workgroups per work item: workgroup half hh takes heads
 // 64hh .. 64hh+63.  Both stream the same rows; the second read of a row is
 // served by the L2 of the XCD they share (blocks i and i + 8 run on one XCD
-// and are dispatched together).  Eight waves, two per SIMD, in two roles:
-//  * S waves (w = 0..3): scores and softmax of head block r = w (16 heads,
-//    Q fragments in 72 VGPRs);
-//  * V waves (w = 4..7): the DMA of row group r = w - 4 and the latent PV of
-//    columns 128r .. 128r+127 for all 64 heads (128 accumulators).
+// and are dispatched together).  Sixteen waves, four per SIMD, in two roles:
+//  * S waves (w = 0..7): scores and softmax of head block hb = w % 4 (16
+//    heads, Q fragments in 72 VGPRs) for token half th = w / 4 of every slice;
+//  * V waves (w = 8..15): the latent PV of columns 64u .. 64u+63, u = w - 8,
+//    for all 64 heads (64 accumulators); V waves u < 4 also run the DMA of
+//    row group u.
 // Iteration k: S waves score slice k and publish its weights; V waves
 // accumulate slice k-1 with the weights published one iteration earlier.  One
-// workgroup barrier per iteration; the two waves sharing a SIMD overlap their
-// MFMA, LDS and VALU work.
+// workgroup barrier per iteration (two in the first); the waves sharing a SIMD
+// overlap their MFMA, LDS and VALU work.
 //
 // MFMA operand layouts (v_mfma_f32_16x16x32_bf16, lane l, g = l / 16, q = l % 16):
 //   A[m][k]: lane holds m = q, k = 8g .. 8g+7;  B[k][n]: k = 8g .. 8g+7, n = q;
 //   C[m][n]: lane holds m = 4g + i (i = 0..3), n = q.
-// Scores: S^T[token][head], A = rows (token q of a 16-block, 8 latent values),
-// B = Q^T.  C leaves lane l with tokens 4g+i of token block tb, head q.
+// Scores: S^T[token][head], A = rows (token 16th + q, 8 latent values), B = Q^T.
+// C leaves lane l with tokens 16th + 4g + i, head q.
 // PV: O^T[latent][head] += C^T[latent][token] . P^T[token][head] with the
 // reduction index k = 8g + j standing for token sigma(g, j) = 4g + j (j < 4) or
-// 16 + 4g + (j - 4) (j >= 4): exactly the tokens whose weights lane l holds.
+// 16 + 4g + (j - 4) (j >= 4): exactly the tokens whose weights lane l of the
+// two S waves of a head block hold (token half 0 fills bytes 0..7 of the
+// lane's 16-byte fragment, half 1 bytes 8..15).
 // ---------------------------------------------------------------------------
 constexpr int kHeadsWG = 64;
-constexpr int kHeadBlocksWG = kHeadsWG / 16;     // 4
+constexpr int kHeadBlocksWG = kHeadsWG / 16;        // 4
 constexpr int kPBytesWG = kHeadBlocksWG * 64 * 16;  // 4 KiB of weights per slice
-static_assert(kStages * kSlotBytes + 2 * kPBytesWG + 4 * 4 + kHeadsWG * 4 <= 163840, "LDS budget");
+constexpr int kSWaves = 8;
+static_assert(kStages * kSlotBytes + 2 * kPBytesWG + kSWaves * 4 + 4 * kHeadsWG * 4 <= 163840,
+              "LDS budget");
 
-__global__ __launch_bounds__(512, 1) void decode_h128_kernel(
+__global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ items, int num_items, float scale, float max_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part) {
   constexpr int H = 128;
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes + 2 * kPBytesWG];
-  __shared__ int votes[4];              // after a pass: jump flags of the S waves
-  __shared__ float lsum[kHeadsWG];      // epilogue: row sums
+  __shared__ int votes[kSWaves];          // after a pass: jump flags of the S waves
+  __shared__ float mref_x[2][kHeadsWG];   // per token half: a head's maximum
+  __shared__ float lsum2[2][kHeadsWG];    // per token half: a head's row sum
   char* const pbuf = lds + kStages * kSlotBytes;
   const uint32_t lds_base =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool v_role = w >= 4;
-  const int r = w & 3;
   const int g = lane >> 4;   // lane group (k block of the MFMA operands)
   const int q = lane & 15;   // row/column within a 16-block
 
@@ -212,90 +216,81 @@ __global__ __launch_bounds__(512, 1) void decode_h128_kernel(
   constexpr uint32_t kTileRowGroup = 9 * 1024;
   constexpr uint32_t kRowGroup2 = 2 * kTileRowGroup;
 
-  // Every wave runs the same sequence of workgroup barriers: per pass, one per
-  // iteration, plus the ones named below.
-
-  if (!v_role) {
+  // Every wave runs the same sequence of workgroup barriers: a full pass has
+  // n_slices + 4 of them, the exact-maximum pass n_slices + 2, the epilogue 1.
+  if (w < kSWaves) {
     // ======================= S waves: scores and softmax =======================
     // The S waves are the critical path (their softmax cannot overlap their own
     // MFMAs); a higher issue priority lets the V waves' MFMAs fill the gaps.
     __builtin_amdgcn_s_setprio(MLA_S_PRIO);
-    bf16x8 qf[18];  // B operand: head head0 + 16r + q, values 32ks + 8g .. +8
+    const int hb = w & 3, th = w >> 2;
+    bf16x8 qf[18];  // B operand: head head0 + 16hb + q, values 32ks + 8g .. +8
     {
-      const uint16_t* qrow = q_abs + (static_cast<int64_t>(b) * H + head0 + 16 * r + q) * kDq + 8 * g;
+      const uint16_t* qrow = q_abs + (static_cast<int64_t>(b) * H + head0 + 16 * hb + q) * kDq + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
     }
-    const int sw = swz(q);  // rows q and q + 16 share it
-    const uint32_t qk_base = (q >> 3) * kTileRowGroup + (q & 7) * 128;
+    const int sw = swz(q);
+    const uint32_t qk_base = th * kRowGroup2 + (q >> 3) * kTileRowGroup + (q & 7) * 128;
     const uint32_t qk_off0 = qk_base + 16 * ((g) ^ sw);      // even ks: logical chunk 8(ks/2) + g
     const uint32_t qk_off1 = qk_base + 16 * ((4 + g) ^ sw);  // odd ks: logical chunk 8(ks/2) + 4 + g
     const float c2 = scale * kLog2e;
+    const int hidx = 16 * hb + q;  // head within the workgroup
     float m_ref = -INFINITY, l_run = 0.f;
 
-    // S^T[32 tokens x 16 heads] of one slot, log2 units (scale folded in);
-    // tokens of the slice at or past `nv` are -inf.  Four accumulator chains
-    // (token block x k parity), LDS reads kAhead steps ahead.
-    auto scores = [&](const char* slot, int nv, float (&s)[2][4]) {
-      float4_t acc[2][2];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) acc[tb][0] = acc[tb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-      constexpr int kSteps = 36, kAhead = MLA_QK_AHEAD;
-      auto off_of = [&](int st) -> uint32_t {
-        const int ks = st >> 1, tb = st & 1;
-        return tb * kRowGroup2 + 1024 * (ks >> 1) + ((ks & 1) ? qk_off1 : qk_off0);
+    // S^T[16 tokens x 16 heads] of this token half, log2 units (scale folded
+    // in); tokens of the slice at or past `nv` are -inf.  Two accumulator
+    // chains (k parity), LDS reads kAhead steps ahead.
+    auto scores = [&](const char* slot, int nv, float (&s)[4]) {
+      float4_t acc[2] = {float4_t{0.f, 0.f, 0.f, 0.f}, float4_t{0.f, 0.f, 0.f, 0.f}};
+      constexpr int kSteps = 18, kAhead = MLA_QK_AHEAD;
+      auto off_of = [&](int ks) -> uint32_t {
+        return 1024 * (ks >> 1) + ((ks & 1) ? qk_off1 : qk_off0);
       };
       bf16x8 fa[kAhead];
 #pragma unroll
-      for (int st = 0; st < kAhead; ++st) fa[st] = lds_read128(slot, off_of(st));
+      for (int ks = 0; ks < kAhead; ++ks) fa[ks] = lds_read128(slot, off_of(ks));
 #pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
-        const int ks = st >> 1, tb = st & 1;
-        const bf16x8 a = fa[st % kAhead];
-        if (st + kAhead < kSteps) fa[st % kAhead] = lds_read128(slot, off_of(st + kAhead));
-        acc[tb][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc[tb][ks & 1], 0, 0, 0);
+      for (int ks = 0; ks < kSteps; ++ks) {
+        const bf16x8 a = fa[ks % kAhead];
+        if (ks + kAhead < kSteps) fa[ks % kAhead] = lds_read128(slot, off_of(ks + kAhead));
+        acc[ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc[ks & 1], 0, 0, 0);
       }
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = (acc[tb][0][i] + acc[tb][1][i]) * c2;
-          s[tb][i] = (tb * 16 + 4 * g + i < nv) ? v : -INFINITY;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float v = (acc[0][i] + acc[1][i]) * c2;
+        s[i] = (16 * th + 4 * g + i < nv) ? v : -INFINITY;
+      }
     };
-    auto lane_max = [&](const float (&s)[2][4]) {
-      return fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    };
+    auto lane_max = [&](const float (&s)[4]) { return fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])); };
     auto nvalid = [&](int n) { return min(kSliceTok, t_end - (t_begin + n * kSliceTok)); };
     // weights 2^(s - m_ref) of slice k (masked tokens: 2^-inf = 0) into its buffer
-    auto publish = [&](int k, const float (&s)[2][4]) {
-      uint32_t pk[4];
-      float sum[2];
+    auto publish = [&](int k, const float (&s)[4]) {
+      float p[4];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[tb][i] - m_ref);
-        sum[tb] = (p[0] + p[1]) + (p[2] + p[3]);
-        pk[2 * tb] = pack_bf16x2(p[0], p[1]);
-        pk[2 * tb + 1] = pack_bf16x2(p[2], p[3]);
-      }
-      l_run += sum[0] + sum[1];
-      *reinterpret_cast<bf16x8*>(pbuf_of(k) + (r * 64 + lane) * 16) = __builtin_bit_cast(bf16x8, pk);
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - m_ref);
+      l_run += (p[0] + p[1]) + (p[2] + p[3]);
+      const uint32_t pk[2] = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      *reinterpret_cast<bf16x4*>(pbuf_of(k) + (hb * 64 + lane) * 16 + 8 * th) =
+          __builtin_bit_cast(bf16x4, pk);
     };
 
-    // Full pass.  With `first`, m_ref is the first slice's per-head maximum and
-    // the lane keeps a running maximum of its later scores; the pass is
-    // discarded (returns false) if some head's maximum exceeds m_ref by more
-    // than max_jump.  Slices 1 .. n-2 are whole, so only the first and the
-    // last one are masked.
+    // Full pass.  With `first`, m_ref is the per-head maximum of the first
+    // slice (both token halves, exchanged through LDS) and the lane keeps a
+    // running maximum of its later scores; the pass is discarded (returns
+    // false) if some head's maximum exceeds m_ref by more than max_jump.
+    // Slices 1 .. n-2 are whole, so only the first and the last are masked.
     auto full_pass = [&](bool first) -> bool {
       float m_lane = -INFINITY;
-      float s[2][4];
+      float s[4];
       __syncthreads();
       scores(slot_of(0), nvalid(0), s);
-      if (first) m_ref = rows_max(lane_max(s));
+      if (first) {
+        const float m = rows_max(lane_max(s));
+        if (g == 0) mref_x[th][hidx] = m;
+      }
+      __syncthreads();
+      if (first) m_ref = fmaxf(mref_x[0][hidx], mref_x[1][hidx]);
       publish(0, s);
       for (int k = 1; k < n_slices - 1; ++k) {
         __syncthreads();
@@ -312,40 +307,48 @@ __global__ __launch_bounds__(512, 1) void decode_h128_kernel(
       __syncthreads();
       // vote: did a head of any S wave jump?
       const bool mine = __any(first && rows_max(m_lane) > m_ref + max_jump);
-      if (lane == 0) votes[r] = mine ? 1 : 0;
+      if (lane == 0) votes[w] = mine ? 1 : 0;
       __syncthreads();
-      const bool any = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+      int any = 0;
+#pragma unroll
+      for (int i = 0; i < kSWaves; ++i) any |= votes[i];
       __syncthreads();
-      return !any;
+      return any == 0;
     };
 
     if (!full_pass(true)) {
       // A head's maximum jumped by more than max_jump: exact maxima first,
       // then the item again against them (every weight <= 1).
-      m_ref = -INFINITY;
+      float m_lane = -INFINITY;
       for (int k = 0; k < n_slices; ++k) {
         __syncthreads();
-        float s[2][4];
+        float s[4];
         scores(slot_of(k), nvalid(k), s);
-        m_ref = fmaxf(m_ref, rows_max(lane_max(s)));
+        m_lane = fmaxf(m_lane, lane_max(s));
       }
       __syncthreads();
+      const float m = rows_max(m_lane);
+      if (g == 0) mref_x[th][hidx] = m;
+      __syncthreads();
+      m_ref = fmaxf(mref_x[0][hidx], mref_x[1][hidx]);
       l_run = 0.f;
       full_pass(false);
     }
-    // epilogue: row sums to LDS and the partial log-sum-exp
+    // epilogue: partial row sums to LDS, then the partial log-sum-exp
     const float l = rows_sum(l_run);
-    if (g == 0) {
-      lsum[16 * r + q] = l;
-      lse_part[static_cast<int64_t>(it) * H + head0 + 16 * r + q] = m_ref * kLn2 + logf(l);
-    }
+    if (g == 0) lsum2[th][hidx] = l;
     __syncthreads();
+    if (th == 0 && g == 0)
+      lse_part[static_cast<int64_t>(it) * H + head0 + hidx] =
+          m_ref * kLn2 + logf(lsum2[0][hidx] + lsum2[1][hidx]);
   } else {
     // ======================= V waves: DMA and latent PV =======================
-    // DMA: this wave fetches rows 8r .. 8r+7 of a slice, tiles j = 0..8 (tile
-    // (r, j) at slot offset (9r + j) KiB).  Lane l covers row 8r + l/8 at chunk
-    // position l % 8 of the tile, i.e. logical chunk 8j + ((l % 8) ^ swz(l / 8)).
-    const int drow = 8 * r + (lane >> 3);
+    const int u = w - kSWaves;
+    const bool dma = u < kDmaWaves;
+    // DMA (u < 4): rows 8u .. 8u+7 of a slice, tiles j = 0..8 (tile (u, j) at
+    // slot offset (9u + j) KiB).  Lane l covers row 8u + l/8 at chunk position
+    // l % 8 of the tile, i.e. logical chunk 8j + ((l % 8) ^ swz(l / 8)).
+    const int drow = 8 * u + (lane >> 3);
     const uint32_t dma_lane =
         static_cast<uint32_t>(drow * kRowBytes + ((lane & 7) ^ swz(lane >> 3)) * 16);
     auto issue = [&](int n) {
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(512, 1) void decode_h128_kernel(
       const int page = bt[tok0 >> 6];
       const char* src = cache + static_cast<int64_t>(page) * (kPage * kRowBytes) +
                         (tok0 & (kPage - 1)) * kRowBytes;
-      const uint32_t dst = lds_base + (n % kStages) * kSlotBytes + kLoadsPerWave * r * 1024;
+      const uint32_t dst = lds_base + (n % kStages) * kSlotBytes + kLoadsPerWave * u * 1024;
       // tail slice: rows of tokens >= nv are filled from token 0 of the slice
       // (finite data, weight 0), so empty cache slots are never read.
       const int nv = t_end - tok0;
@@ -378,65 +381,71 @@ __global__ __launch_bounds__(512, 1) void decode_h128_kernel(
       return pv_base + 1024 * (cb >> 2) + 16 * ((2 * (cb & 3) + pv_hc) ^ vsw);
     };
 
-    float4_t oacc[8][kHeadBlocksWG];  // [latent block of this wave][head block]
+    float4_t oacc[4][kHeadBlocksWG];  // [column block 4u + c][head block]
     auto zero_acc = [&]() {
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int hb = 0; hb < kHeadBlocksWG; ++hb) oacc[c][hb] = float4_t{0.f, 0.f, 0.f, 0.f};
     };
-    // O^T[128 columns x 64 heads] += C^T . P^T for one slice
+    // O^T[64 columns x 64 heads] += C^T . P^T for one slice
     auto accumulate = [&](const char* slot, const char* pb) {
       bf16x8 pf[kHeadBlocksWG];
 #pragma unroll
       for (int hb = 0; hb < kHeadBlocksWG; ++hb)
         pf[hb] = *reinterpret_cast<const bf16x8*>(pb + (hb * 64 + lane) * 16);
-      constexpr int kAhead = MLA_PV_AHEAD;
-      bf16x4 f0[kAhead], f1[kAhead];
+      bf16x4 f0[4], f1[4];
 #pragma unroll
-      for (int c = 0; c < kAhead; ++c) {
-        f0[c] = lds_read_tr(slot, pv_off(8 * r + c));
-        f1[c] = lds_read_tr(slot, pv_off(8 * r + c) + kRowGroup2);
+      for (int c = 0; c < 4; ++c) {
+        f0[c] = lds_read_tr(slot, pv_off(4 * u + c));
+        f1[c] = lds_read_tr(slot, pv_off(4 * u + c) + kRowGroup2);
       }
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const bf16x8 a = __builtin_shufflevector(f0[c % kAhead], f1[c % kAhead], 0, 1, 2, 3, 4, 5, 6, 7);
-        if (c + kAhead < 8) {
-          f0[c % kAhead] = lds_read_tr(slot, pv_off(8 * r + c + kAhead));
-          f1[c % kAhead] = lds_read_tr(slot, pv_off(8 * r + c + kAhead) + kRowGroup2);
-        }
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 a = __builtin_shufflevector(f0[c], f1[c], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int hb = 0; hb < kHeadBlocksWG; ++hb)
           oacc[c][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[hb], oacc[c][hb], 0, 0, 0);
       }
     };
     auto full_pass = [&]() -> bool {
-      issue(0);
-      if (n_slices > 1) issue(1);
-      for (int k = 0; k <= n_slices; ++k) {
-        if (k < n_slices) wait_slice(k);
+      if (dma) {
+        issue(0);
+        if (n_slices > 1) issue(1);
+        wait_slice(0);
+      }
+      __syncthreads();
+      if (dma && 2 < n_slices) issue(2);
+      __syncthreads();  // the S waves' first-slice maximum exchange
+      for (int k = 1; k <= n_slices; ++k) {
+        if (dma && k < n_slices) wait_slice(k);
         __syncthreads();
-        if (k + 2 < n_slices) issue(k + 2);
-        if (k >= 1) accumulate(slot_of(k - 1), pbuf_of(k - 1));
+        if (dma && k + 2 < n_slices) issue(k + 2);
+        accumulate(slot_of(k - 1), pbuf_of(k - 1));
       }
       // vote (written by the S waves)
       __syncthreads();
-      const bool any = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+      int any = 0;
+#pragma unroll
+      for (int i = 0; i < kSWaves; ++i) any |= votes[i];
       __syncthreads();
-      return !any;
+      return any == 0;
     };
 
     zero_acc();
     if (!full_pass()) {
       // exact-maximum pass of the S waves: stream the slices again
-      issue(0);
-      if (n_slices > 1) issue(1);
+      if (dma) {
+        issue(0);
+        if (n_slices > 1) issue(1);
+      }
       for (int k = 0; k < n_slices; ++k) {
-        wait_slice(k);
+        if (dma) wait_slice(k);
         __syncthreads();
-        if (k + 2 < n_slices) issue(k + 2);
+        if (dma && k + 2 < n_slices) issue(k + 2);
       }
       __syncthreads();
+      __syncthreads();  // the S waves' maximum exchange
       zero_acc();
       full_pass();
     }
@@ -444,10 +453,10 @@ __global__ __launch_bounds__(512, 1) void decode_h128_kernel(
     __syncthreads();
 #pragma unroll
     for (int hb = 0; hb < kHeadBlocksWG; ++hb) {
-      const float inv = 1.f / lsum[16 * hb + q];
-      float* orow = o_part + (static_cast<int64_t>(it) * H + head0 + 16 * hb + q) * kDc + 128 * r + 4 * g;
+      const float inv = 1.f / (lsum2[0][16 * hb + q] + lsum2[1][16 * hb + q]);
+      float* orow = o_part + (static_cast<int64_t>(it) * H + head0 + 16 * hb + q) * kDc + 64 * u + 4 * g;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+      for (int c = 0; c < 4; ++c) {
         float4_t v = oacc[c][hb];
         v[0] *= inv;
         v[1] *= inv;
@@ -476,7 +485,7 @@ hipError_t decode_fast(const mla_dims& d, const void* q_abs, const void* kv_cach
                        const int32_t* items, int num_items, float* o_part, float* lse_part,
                        hipStream_t stream) {
   if (d.n_heads == 128) {
-    hipLaunchKernelGGL(decode_h128_kernel, dim3(2 * num_items), dim3(512), 0, stream,
+    hipLaunchKernelGGL(decode_h128_kernel, dim3(2 * num_items), dim3(1024), 0, stream,
                        static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
                        block_table, max_pages, seq_lens, items, num_items, d.softmax_scale,
                        max_jump(), o_part, lse_part);
