@@ -20,7 +20,6 @@
 namespace mla {
 namespace {
 
-constexpr int kWRowBytes = kDc * 2;  // 1024 bytes per weight row
 
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr)
@@ -139,55 +138,92 @@ __global__ __launch_bounds__(256) void absorb_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// out_proj: o^T[16 x b] = W^UV_h[16 rows x 512] . o~^T[512 x b] for one block of
-// 16 output rows per workgroup (8 per head), 16 sequences per wave.  Every
-// operand of the workgroup is loaded up front.  The float32 o~ is split into
-// bf16 hi + lo (lo = bf16(x - hi)); two MFMAs per step.
+// out_proj: o^T[64 x b] = W^UV_h[64 rows x 512] . o~^T[512 x b], one workgroup
+// per (head, half of the 128 output rows, 64 sequences); the two halves of a
+// head run on one XCD and share its o~ through the L2.  The float32 o~ of the
+// 64 sequences is staged once in LDS as bf16 hi + lo (lo = bf16(x - hi)),
+// rows of 1 KiB with 16-byte chunk c at position c ^ 2 (b % 8): the B-operand
+// reads (16 sequences x one chunk per quarter-wave) then hit distinct bank
+// groups.  Wave w owns output rows 16w .. 16w+15 of the half for all 64
+// sequences (four accumulators), W^UV rows straight from global memory.
 // ---------------------------------------------------------------------------
+constexpr int kOutSeq = 64;
+constexpr int kOutHalfBytes = kOutSeq * kDc * 2;  // one bf16 copy of the staged o~
+
 __global__ __launch_bounds__(256) void out_proj_kernel(int batch, int H,
                                                        const float* __restrict__ o_lat,
                                                        const uint16_t* __restrict__ w_uv,
                                                        float* __restrict__ out) {
-  int h, db;
-  xcd_split(blockIdx.x, kDh / 16, h, db);
+  __shared__ __attribute__((aligned(16))) char lds[2 * kOutHalfBytes];  // [hi | lo][b][512]
+  int h, half;
+  xcd_split(blockIdx.x, 2, h, half);
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, q = lane & 15;
-  const int bblk = blockIdx.y * 4 + w;
-  if (bblk * 16 >= batch) return;
-  const int b = bblk * 16 + q;
-  const bool bvalid = b < batch;
-  const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * kDh + 16 * db + q) * kDc + 8 * g;
-  const float* orow = o_lat + (static_cast<int64_t>(b) * H + h) * kDc + 8 * g;
+  const int b0 = blockIdx.y * kOutSeq;
+  const int nb = min(kOutSeq, batch - b0);
+
+  // A operand: W^UV row 64 half + 16w + q, values 32ks + 8g .. +8
+  const int drow = 64 * half + 16 * w + q;
+  const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * kDh + drow) * kDc + 8 * g;
   bf16x8 a[16];
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(wrow + 32 * ks);
-  float4_t x[16][2];
+
+  // stage o~: float4 f = t + 256 i covers sequence f / 128, values 4 (f % 128) .. +4
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    if (bvalid) {
-      x[ks][0] = *reinterpret_cast<const float4_t*>(orow + 32 * ks);
-      x[ks][1] = *reinterpret_cast<const float4_t*>(orow + 32 * ks + 4);
-    } else {
-      x[ks][0] = x[ks][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < 32; i0 += 8) {
+    float4_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int f = threadIdx.x + 256 * (i0 + i);
+      const int bl = f >> 7;
+      v[i] = bl < nb ? *reinterpret_cast<const float4_t*>(
+                           o_lat + (static_cast<int64_t>(b0 + bl) * H + h) * kDc + 4 * (f & 127))
+                     : float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int f = threadIdx.x + 256 * (i0 + i);
+      const int bl = f >> 7, c = 4 * (f & 127);
+      const uint32_t off = bl * (kDc * 2) + 16 * ((c >> 3) ^ (2 * (bl & 7))) + 2 * (c & 7);
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        hi[j] = pack_bf16x2(v[i][2 * j], v[i][2 * j + 1]);
+        lo[j] = pack_bf16x2(v[i][2 * j] - __uint_as_float(hi[j] << 16),
+                            v[i][2 * j + 1] - __uint_as_float(hi[j] & 0xffff0000u));
+      }
+      *reinterpret_cast<uint64_t*>(lds + off) = (static_cast<uint64_t>(hi[1]) << 32) | hi[0];
+      *reinterpret_cast<uint64_t*>(lds + kOutHalfBytes + off) = (static_cast<uint64_t>(lo[1]) << 32) | lo[0];
     }
   }
-  float4_t acc = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+
+  // B operand: sequence 16bb + q, values 32ks + 8g .. +8 (chunk 4ks + g)
+  float4_t acc[4] = {};
+  const uint32_t brow = q * (kDc * 2);
+  const int bsw = 2 * (q & 7);
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
-    uint32_t hb[4], lb[4];
+    const uint32_t col = 16 * ((4 * ks + g) ^ bsw);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float v0 = x[ks][j >> 1][2 * (j & 1)], v1 = x[ks][j >> 1][2 * (j & 1) + 1];
-      hb[j] = pack_bf16x2(v0, v1);
-      lb[j] = pack_bf16x2(v0 - __uint_as_float(hb[j] << 16), v1 - __uint_as_float(hb[j] & 0xffff0000u));
+    for (int bb = 0; bb < 4; ++bb) {
+      const uint32_t off = bb * 16 * (kDc * 2) + brow + col;
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(lds + off);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(lds + kOutHalfBytes + off);
+      acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bh, acc[bb], 0, 0, 0);
+      acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bl, acc[bb], 0, 0, 0);
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], __builtin_bit_cast(bf16x8, hb), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], __builtin_bit_cast(bf16x8, lb), acc, 0, 0, 0);
   }
-  // lane holds o[b][h][16db + 4g + i]
-  if (bvalid)
-    *reinterpret_cast<float4_t*>(out + (static_cast<int64_t>(b) * H + h) * kDh + 16 * db + 4 * g) = acc;
+  // lane holds o[b0 + 16bb + q][h][64 half + 16w + 4g + i]
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    const int bl = 16 * bb + q;
+    if (bl < nb)
+      *reinterpret_cast<float4_t*>(out + (static_cast<int64_t>(b0 + bl) * H + h) * kDh + 64 * half +
+                                   16 * w + 4 * g) = acc[bb];
+  }
 }
 
 }  // namespace
@@ -208,7 +244,7 @@ hipError_t out_proj_fast(const mla_dims& d, int batch, const float* o_latent, co
                          float* out, hipStream_t stream) {
   const int groups = (batch + 63) / 64;
   if (groups > 65535 || d.n_heads % 8 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(out_proj_kernel, dim3(d.n_heads * (kDh / 16), groups), dim3(256), 0, stream, batch,
+  hipLaunchKernelGGL(out_proj_kernel, dim3(d.n_heads * 2, groups), dim3(256), 0, stream, batch,
                      d.n_heads, o_latent, static_cast<const uint16_t*>(w_uv), out);
   return hipGetLastError();
 }
