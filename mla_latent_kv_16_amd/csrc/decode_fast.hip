@@ -468,6 +468,215 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// H = 16: one workgroup of four waves per work item.  At 16 heads the step is
+// far from the MFMA roof (about 30 flop per cached byte), so every wave
+// computes the scores of all 16 heads over the whole slice itself: its score
+// accumulators are then already the P^T operand of its own PV MFMAs (token
+// order sigma(g, .), as above) and no weights cross between waves.  Wave w
+// owns latent columns 128w .. 128w+127 of the PV (32 accumulators) and the DMA
+// of row group w.  A ring of four slots keeps three slices in flight.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void decode_h16_kernel(
+    const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
+    const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ items, float scale, float max_jump, float* __restrict__ o_part,
+    float* __restrict__ lse_part) {
+  constexpr int H = 16;
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes];
+  __shared__ int votes[4];
+  const uint32_t lds_base =
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int q = lane & 15;
+
+  const int it = blockIdx.x;
+  const int b = items[4 * it];
+  const int p0 = items[4 * it + 2];
+  const int p1 = items[4 * it + 3];
+  const int L = seq_lens[b];
+  const int t_begin = p0 * kPage;
+  const int t_end = min(p1 * kPage, L);
+  const int n_slices = (t_end - t_begin + kSliceTok - 1) / kSliceTok;
+  const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
+  constexpr uint32_t kTileRowGroup = 9 * 1024;
+  constexpr uint32_t kRowGroup2 = 2 * kTileRowGroup;
+  auto slot_of = [&](int n) -> const char* { return lds + (n % kStages) * kSlotBytes; };
+
+  // Q fragments (B operand of the scores): head q, values 32ks + 8g .. +8
+  bf16x8 qf[18];
+  {
+    const uint16_t* qrow = q_abs + (static_cast<int64_t>(b) * H + q) * kDq + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+  }
+  __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+
+  // DMA: rows 8w .. 8w+7 of a slice (see the 128-head kernel)
+  const int drow = 8 * w + (lane >> 3);
+  const uint32_t dma_lane =
+      static_cast<uint32_t>(drow * kRowBytes + ((lane & 7) ^ swz(lane >> 3)) * 16);
+  auto issue = [&](int n) {
+    const int tok0 = t_begin + n * kSliceTok;
+    const int page = bt[tok0 >> 6];
+    const char* src = cache + static_cast<int64_t>(page) * (kPage * kRowBytes) +
+                      (tok0 & (kPage - 1)) * kRowBytes;
+    const uint32_t dst = lds_base + (n % kStages) * kSlotBytes + kLoadsPerWave * w * 1024;
+    const int nv = t_end - tok0;
+    const uint32_t voff = drow < nv ? dma_lane : dma_lane - drow * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j) dma16(src + 128 * j, voff, dst + 1024 * j);
+  };
+
+  const int sw = swz(q);
+  const uint32_t qk_base = (q >> 3) * kTileRowGroup + (q & 7) * 128;
+  const uint32_t qk_off0 = qk_base + 16 * ((g) ^ sw);
+  const uint32_t qk_off1 = qk_base + 16 * ((4 + g) ^ sw);
+  const int vrow = 4 * g + (q >> 2);
+  const int vsw = swz(vrow);
+  const uint32_t pv_base = (vrow >> 3) * kTileRowGroup + (vrow & 7) * 128 + 8 * (q & 1);
+  const int pv_hc = (q & 3) >> 1;
+  auto pv_off = [&](int cb) -> uint32_t {
+    return pv_base + 1024 * (cb >> 2) + 16 * ((2 * (cb & 3) + pv_hc) ^ vsw);
+  };
+  const float c2 = scale * kLog2e;
+
+  // S^T[32 tokens x 16 heads], log2 units; tokens at or past `nv` are -inf
+  auto scores = [&](const char* slot, int nv, float (&s)[2][4]) {
+    float4_t acc[2][2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) acc[tb][0] = acc[tb][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+    constexpr int kSteps = 36, kAhead = 8;
+    auto off_of = [&](int st) -> uint32_t {
+      const int ks = st >> 1, tb = st & 1;
+      return tb * kRowGroup2 + 1024 * (ks >> 1) + ((ks & 1) ? qk_off1 : qk_off0);
+    };
+    bf16x8 fa[kAhead];
+#pragma unroll
+    for (int st = 0; st < kAhead; ++st) fa[st] = lds_read128(slot, off_of(st));
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const int ks = st >> 1, tb = st & 1;
+      const bf16x8 a = fa[st % kAhead];
+      if (st + kAhead < kSteps) fa[st % kAhead] = lds_read128(slot, off_of(st + kAhead));
+      acc[tb][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc[tb][ks & 1], 0, 0, 0);
+    }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = (acc[tb][0][i] + acc[tb][1][i]) * c2;
+        s[tb][i] = (tb * 16 + 4 * g + i < nv) ? v : -INFINITY;
+      }
+  };
+  auto lane_max = [&](const float (&s)[2][4]) {
+    return fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                 fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  };
+  auto nvalid = [&](int n) { return min(kSliceTok, t_end - (t_begin + n * kSliceTok)); };
+
+  float4_t oacc[8];
+  float m_ref = -INFINITY, l_run = 0.f;
+  // wait for slice n (later ones may stay in flight), then the ring barrier;
+  // the slot of slice n-1 is free afterwards, so slice n+3 goes there
+  auto enter = [&](int n) {
+    const int ahead = min(kStages - 2, n_slices - 1 - n);
+    if (ahead >= 2)
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(2 * kLoadsPerWave));
+    else if (ahead == 1)
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(kLoadsPerWave));
+    else
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+    __syncthreads();
+    if (n + kStages - 1 < n_slices) issue(n + kStages - 1);
+  };
+  auto start = [&]() {
+    for (int n = 0; n < kStages - 1 && n < n_slices; ++n) issue(n);
+  };
+  // weights and O += C^T P^T for one slice
+  auto accumulate = [&](const char* slot, const float (&s)[2][4]) {
+    float p[2][4];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[tb][i] = __builtin_amdgcn_exp2f(s[tb][i] - m_ref);
+    l_run += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+    const uint32_t pk[4] = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                            pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+    bf16x4 f0[8], f1[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      f0[c] = lds_read_tr(slot, pv_off(8 * w + c));
+      f1[c] = lds_read_tr(slot, pv_off(8 * w + c) + kRowGroup2);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      oacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_shufflevector(f0[c], f1[c], 0, 1, 2, 3, 4, 5, 6, 7), pf, oacc[c], 0, 0, 0);
+  };
+
+  // Full pass (see the softmax note at the top); every wave computes the same
+  // scores, the vote only keeps the waves' control flow provably identical.
+  auto full_pass = [&](bool first) -> bool {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+    float m_lane = -INFINITY;
+    start();
+    for (int n = 0; n < n_slices; ++n) {
+      enter(n);
+      float s[2][4];
+      scores(slot_of(n), nvalid(n), s);
+      if (first) {
+        if (n == 0)
+          m_ref = rows_max(lane_max(s));
+        else
+          m_lane = fmaxf(m_lane, lane_max(s));
+      }
+      accumulate(slot_of(n), s);
+    }
+    const bool mine = __any(first && rows_max(m_lane) > m_ref + max_jump);
+    __syncthreads();
+    if (lane == 0) votes[w] = mine ? 1 : 0;
+    __syncthreads();
+    const bool any = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
+    __syncthreads();
+    return !any;
+  };
+
+  if (!full_pass(true)) {
+    float m_lane = -INFINITY;
+    start();
+    for (int n = 0; n < n_slices; ++n) {
+      enter(n);
+      float s[2][4];
+      scores(slot_of(n), nvalid(n), s);
+      m_lane = fmaxf(m_lane, lane_max(s));
+    }
+    __syncthreads();
+    m_ref = rows_max(m_lane);
+    full_pass(false);
+  }
+
+  const float l = rows_sum(l_run);
+  if (w == 0 && g == 0) lse_part[static_cast<int64_t>(it) * H + q] = m_ref * kLn2 + logf(l);
+  const float inv = 1.f / l;
+  float* orow = o_part + (static_cast<int64_t>(it) * H + q) * kDc + 128 * w + 4 * g;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float4_t v = oacc[c];
+    v[0] *= inv;
+    v[1] *= inv;
+    v[2] *= inv;
+    v[3] *= inv;
+    *reinterpret_cast<float4_t*>(orow + 16 * c) = v;
+  }
+}
+
 // Threshold (log2 units) beyond which a head's score maximum triggers the
 // exact-maximum pass.  MLA_DECODE_MAX_JUMP overrides it (a value in (0, 30]),
 // which lets tests drive that pass with ordinary inputs.
@@ -491,8 +700,11 @@ hipError_t decode_fast(const mla_dims& d, const void* q_abs, const void* kv_cach
                        max_jump(), o_part, lse_part);
     return hipGetLastError();
   }
-  return decode_generic(d, q_abs, kv_cache, block_table, max_pages, seq_lens, items, num_items,
-                        o_part, lse_part, stream);
+  hipLaunchKernelGGL(decode_h16_kernel, dim3(num_items), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
+                     block_table, max_pages, seq_lens, items, d.softmax_scale, max_jump(), o_part,
+                     lse_part);
+  return hipGetLastError();
 }
 
 }  // namespace mla
