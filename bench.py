@@ -7,12 +7,16 @@ resident in HBM (the split plan is made once per batch shape, before timing).
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-flush]
                     [--no-cpu-baseline] [--copy-probe]
 
-Prints ONE JSON line on stdout; progress goes to stderr.  Before every step a
+Prints ONE JSON line on stdout; progress goes to stderr.  The step time comes
+from HIP events at the step boundaries; a second pass over the same steps with
+an event between every two kernels gives the per-kernel times (those events
+add a few microseconds each, so the breakdown sums to more than the step).
+Before every step a
 512 MiB buffer is read (a reduction, untimed), so the 256 MB last-level cache
 holds other data, as after the other layers of a model, and the step reads its
 cache rows from HBM.  The flush reads rather than writes so that the step does
-not also pay for writing back dirty flush lines.  Step and kernel times come
-from HIP events recorded on the stream the kernels run on.
+not also pay for writing back dirty flush lines.  All events are recorded on
+the stream the kernels run on.
 """
 from __future__ import annotations
 
@@ -188,17 +192,29 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # Timed region: K steps, HIP events on the kernels' stream at the step
+    # boundaries only (an event between two kernels adds several microseconds
+    # of its own to the step).
+    step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     for k in range(args.steps):
         evict()
-        step(evs[k])
+        step_ev[k][0].record(stream)
+        step()
+        step_ev[k][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    t = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])  # ms
-    step_ms = t.sum(axis=1)
+    step_ms = np.array([e[0].elapsed_time(e[1]) for e in step_ev])
     ms = float(step_ms.mean())
+    # Per-kernel breakdown (and the decode launch time for the roofline): the
+    # same K steps again with an event between every two kernels.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        evict()
+        step(evs[k])
+    torch.cuda.synchronize()
+    t = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])  # ms
     k_ms = t.mean(axis=0)
     names = ["absorb_q", "decode_splitkv", "combine", "out_proj"]
     log("[bench] per-kernel mean ms: " + ", ".join(f"{n} {v:.4f}" for n, v in zip(names, k_ms)))
