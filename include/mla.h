@@ -11,6 +11,7 @@
  *   mla_decode_splitkv  per work item: scores against [c^KV | k^R], online
  *                       softmax, latent-space weighted sum, partial LSE
  *   mla_combine         log-sum-exp merge of the work items of a sequence
+ *   mla_decode_merged   the two above in one launch
  *   mla_out_proj        o_i = W^UV_i o~_i                                    (per head i)
  *
  * Pages describing the method (titles as published):
@@ -160,6 +161,29 @@ mla_status mla_decode_splitkv(const mla_dims* dims, int32_t batch, const void* q
 mla_status mla_combine(const mla_dims* dims, int32_t batch, const int32_t* split_offsets,
                        const float* o_part, const float* lse_part, float* o_latent, float* lse,
                        void* stream);
+
+/* Split-KV decode with the log-sum-exp merge fused in: the o_latent and lse of
+ * mla_combine from one launch (same items and split_offsets as the two calls).
+ * Pages as for mla_decode_splitkv; the merge is the combine's exact algebra.
+ * On the gfx950 fast path every workgroup writes its partial to o_part /
+ * lse_part, releases it, and takes a ticket; the last workgroup of a sequence
+ * (of a half of its heads, at 128 heads) merges the partials in item order
+ * and resets the ticket.  A sequence with a single item writes o_latent and
+ * lse directly.  On other shapes this is mla_decode_splitkv followed by
+ * mla_combine on the same stream.
+ *   tickets   int32 [2 * batch] device memory, all zero on entry; every call
+ *             leaves it zero (a call that fails before launching writes nothing)
+ *   o_part, lse_part  scratch of the sizes mla_decode_splitkv needs; their
+ *             contents afterwards are unspecified
+ *   o_latent, lse     as for mla_combine (`lse` may be NULL)
+ * Concurrent calls must not share `tickets`.
+ * Errors: MLA_ERR_INVALID_ARG for null pointers, sizes < 1 or misalignment. */
+mla_status mla_decode_merged(const mla_dims* dims, int32_t batch, const void* q_abs,
+                             const void* kv_cache, int32_t num_pages, const int32_t* block_table,
+                             int32_t max_pages_per_seq, const int32_t* seq_lens,
+                             const int32_t* items, int32_t num_items,
+                             const int32_t* split_offsets, float* o_part, float* lse_part,
+                             int32_t* tickets, float* o_latent, float* lse, void* stream);
 
 /* Map the latent-space result out through W^UV: out[b][i] = W^UV_i o_latent[b][i].
  * Page "DeepSeek V2 技术解析" 2.2.1.1 (W^UV absorbed on the output side) and page

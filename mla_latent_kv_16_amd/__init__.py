@@ -6,7 +6,7 @@ C ABI as raw device pointers.  The binding fails loudly when libmla.so has not
 been built -- there is no fallback.
 
 Entry points mirror include/mla.h:
-    absorb_q, plan_splits, decode_splitkv, combine, out_proj
+    absorb_q, plan_splits, decode_splitkv, combine, decode_merged, out_proj
 plus `decode_step`, which runs the four device steps in order.
 """
 from __future__ import annotations
@@ -19,6 +19,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = ["MlaError", "Dims", "load", "lib_path", "absorb_q", "plan_splits", "decode_splitkv",
+           "decode_merged",
            "combine", "out_proj", "decode_step", "fast_path", "version", "BF16", "F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +93,8 @@ def load():
         "mla_plan_max_items": (ctypes.c_int64, [pd, i32, pi32]),
         "mla_decode_splitkv": (i32, [pd, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp]),
         "mla_combine": (i32, [pd, i32, vp, vp, vp, vp, vp, vp]),
+        "mla_decode_merged": (i32, [pd, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp,
+                                     vp, vp]),
         "mla_out_proj": (i32, [pd, i32, vp, vp, vp, vp]),
         "mla_status_string": (ctypes.c_char_p, [i32]),
         "mla_version": (i32, []),
@@ -231,6 +234,41 @@ def combine(dims: Dims, split_offsets, o_part, lse_part, batch: int, o_latent=No
         _ptr(lse_part, torch.float32, (W, H), "lse_part"),
         _ptr(o_latent, torch.float32, (batch, H, dims.d_latent), "o_latent"),
         _ptr(lse, torch.float32, (batch, H), "lse"), _stream(stream)), "mla_combine")
+    return o_latent, lse
+
+
+def decode_merged(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items, split_offsets,
+                  tickets, o_part=None, lse_part=None, o_latent=None, lse=None, stream=None,
+                  want_lse: bool = True):
+    """decode_splitkv + combine in one launch: (o_latent [B, H, d_c], lse [B, H] or None).
+
+    `tickets` is an int32 device tensor of 2 * B zeros; every call leaves it zero.
+    """
+    torch = _torch()
+    dt = _store_dtype(dims)
+    B, H = q_abs.shape[0], dims.n_heads
+    W = items.shape[0]
+    dev = q_abs.device
+    if o_part is None:
+        o_part = torch.empty((W, H, dims.d_latent), dtype=torch.float32, device=dev)
+    if lse_part is None:
+        lse_part = torch.empty((W, H), dtype=torch.float32, device=dev)
+    if o_latent is None:
+        o_latent = torch.empty((B, H, dims.d_latent), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    num_pages = kv_cache.shape[0]
+    _check(load().mla_decode_merged(
+        ctypes.byref(dims.c()), B, _ptr(q_abs, dt, (B, H, dims.row), "q_abs"),
+        _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
+        _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
+        _ptr(seq_lens, torch.int32, (B,), "seq_lens"), _ptr(items, torch.int32, (W, 4), "items"), W,
+        _ptr(split_offsets, torch.int32, (B + 1,), "split_offsets"),
+        _ptr(o_part, torch.float32, (W, H, dims.d_latent), "o_part"),
+        _ptr(lse_part, torch.float32, (W, H), "lse_part"),
+        _ptr(tickets, torch.int32, (2 * B,), "tickets"),
+        _ptr(o_latent, torch.float32, (B, H, dims.d_latent), "o_latent"),
+        _ptr(lse, torch.float32, (B, H), "lse"), _stream(stream)), "mla_decode_merged")
     return o_latent, lse
 
 

@@ -166,9 +166,11 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ items, int num_items, float scale, float max_jump,
-    float* __restrict__ o_part, float* __restrict__ lse_part) {
+    float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
+    int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
   constexpr int H = 128;
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes + 2 * kPBytesWG];
+  __shared__ int ticket_lds;
   __shared__ int votes[kSWaves];          // after a pass: jump flags of the S waves
   __shared__ float mref_x[2][kHeadsWG];   // per token half: a head's maximum
   __shared__ float lsum2[2][kHeadsWG];    // per token half: a head's row sum
@@ -206,6 +208,14 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
   const int n_slices = (t_end - t_begin + kSliceTok - 1) / kSliceTok;
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
   const int head0 = kHeadsWG * hh;
+  // Merged mode (tickets != null): o~ and lse of the sequence instead of a
+  // partial when the sequence has one item, else the partial and, in the last
+  // workgroup of the sequence half to finish, the merge of all its partials.
+  const bool merged = tickets != nullptr;
+  const int s0 = merged ? split_offsets[b] : 0;
+  const int nsplit = merged ? split_offsets[b + 1] - s0 : 0;
+  const bool direct = merged && nsplit == 1;
+  const bool merge_tail = merged && nsplit > 1;
 
   auto slot_of = [&](int n) -> const char* { return lds + (n % kStages) * kSlotBytes; };
   auto pbuf_of = [&](int n) -> char* { return pbuf + (n & 1) * kPBytesWG; };
@@ -338,9 +348,20 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     const float l = rows_sum(l_run);
     if (g == 0) lsum2[th][hidx] = l;
     __syncthreads();
-    if (th == 0 && g == 0)
-      lse_part[static_cast<int64_t>(it) * H + head0 + hidx] =
-          m_ref * kLn2 + logf(lsum2[0][hidx] + lsum2[1][hidx]);
+    if (th == 0 && g == 0) {
+      const float lse_v = m_ref * kLn2 + logf(lsum2[0][hidx] + lsum2[1][hidx]);
+      if (direct) {
+        if (lse_out) lse_out[static_cast<int64_t>(b) * H + head0 + hidx] = lse_v;
+      } else {
+        lse_part[static_cast<int64_t>(it) * H + head0 + hidx] = lse_v;
+      }
+    }
+    if (merge_tail) {  // same barriers as the V waves' merge tail
+      __threadfence();
+      __syncthreads();
+      if (threadIdx.x == 0) ticket_lds = atomicAdd(&tickets[2 * b + hh], 1);
+      __syncthreads();
+    }
   } else {
     // ======================= V waves: DMA and latent PV =======================
     const int u = w - kSWaves;
@@ -450,19 +471,66 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       full_pass();
     }
     // epilogue: normalise by the row sums of the S waves and write the partial
+    // (or, for a sequence with one item in merged mode, o~ itself)
     __syncthreads();
 #pragma unroll
     for (int hb = 0; hb < kHeadBlocksWG; ++hb) {
       const float inv = 1.f / (lsum2[0][16 * hb + q] + lsum2[1][16 * hb + q]);
-      float* orow = o_part + (static_cast<int64_t>(it) * H + head0 + 16 * hb + q) * kDc + 64 * u + 4 * g;
+      const int64_t row = direct ? static_cast<int64_t>(b) * H + head0 + 16 * hb + q
+                                 : static_cast<int64_t>(it) * H + head0 + 16 * hb + q;
+      float* orow = (direct ? o_latent : o_part) + row * kDc + 64 * u + 4 * g;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        float4_t v = oacc[c][hb];
-        v[0] *= inv;
-        v[1] *= inv;
-        v[2] *= inv;
-        v[3] *= inv;
-        *reinterpret_cast<float4_t*>(orow + 16 * c) = v;
+        oacc[c][hb][0] *= inv;
+        oacc[c][hb][1] *= inv;
+        oacc[c][hb][2] *= inv;
+        oacc[c][hb][3] *= inv;
+        *reinterpret_cast<float4_t*>(orow + 16 * c) = oacc[c][hb];
+      }
+    }
+    if (merge_tail) {
+      // release this workgroup's partial, take a ticket; the last workgroup of
+      // the sequence half merges every partial in item order (the combine's
+      // arithmetic, its own partial from registers) and resets the ticket
+      __threadfence();
+      __syncthreads();
+      __syncthreads();
+      if (ticket_lds == nsplit - 1) {
+        __threadfence();
+#pragma unroll
+        for (int hb = 0; hb < kHeadBlocksWG; ++hb) {
+          const int head = head0 + 16 * hb + q;
+          float M = -INFINITY;
+          for (int s = s0; s < s0 + nsplit; ++s) M = fmaxf(M, lse_part[static_cast<int64_t>(s) * H + head]);
+          float Z = 0.f;
+          float4_t acc[4] = {};
+          for (int s = s0; s < s0 + nsplit; ++s) {
+            const int64_t r = static_cast<int64_t>(s) * H + head;
+            const float wgt = expf(lse_part[r] - M);
+            Z += wgt;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float4_t v = s == it ? oacc[c][hb]
+                                         : *reinterpret_cast<const float4_t*>(o_part + r * kDc + 64 * u + 16 * c + 4 * g);
+              acc[c][0] = fmaf(wgt, v[0], acc[c][0]);
+              acc[c][1] = fmaf(wgt, v[1], acc[c][1]);
+              acc[c][2] = fmaf(wgt, v[2], acc[c][2]);
+              acc[c][3] = fmaf(wgt, v[3], acc[c][3]);
+            }
+          }
+          const float inv = 1.f / Z;
+          float* orow = o_latent + (static_cast<int64_t>(b) * H + head) * kDc + 64 * u + 4 * g;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc[c][0] *= inv;
+            acc[c][1] *= inv;
+            acc[c][2] *= inv;
+            acc[c][3] *= inv;
+            *reinterpret_cast<float4_t*>(orow + 16 * c) = acc[c];
+          }
+          if (lse_out && u == 0 && g == 0) lse_out[static_cast<int64_t>(b) * H + head] = M + logf(Z);
+        }
+        if (u == 0 && lane == 0) tickets[2 * b + hh] = 0;
       }
     }
   }
@@ -481,10 +549,12 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ items, float scale, float max_jump, float* __restrict__ o_part,
-    float* __restrict__ lse_part) {
+    float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
+    int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
   constexpr int H = 16;
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes];
   __shared__ int votes[4];
+  __shared__ int ticket_lds;
   const uint32_t lds_base =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
 
@@ -505,6 +575,11 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
   constexpr uint32_t kTileRowGroup = 9 * 1024;
   constexpr uint32_t kRowGroup2 = 2 * kTileRowGroup;
   auto slot_of = [&](int n) -> const char* { return lds + (n % kStages) * kSlotBytes; };
+  // merged mode, as in the 128-head kernel (one ticket per sequence)
+  const bool merged = tickets != nullptr;
+  const int s0 = merged ? split_offsets[b] : 0;
+  const int nsplit = merged ? split_offsets[b + 1] - s0 : 0;
+  const bool direct = merged && nsplit == 1;
 
   // Q fragments (B operand of the scores): head q, values 32ks + 8g .. +8
   bf16x8 qf[18];
@@ -663,17 +738,63 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
   }
 
   const float l = rows_sum(l_run);
-  if (w == 0 && g == 0) lse_part[static_cast<int64_t>(it) * H + q] = m_ref * kLn2 + logf(l);
+  if (w == 0 && g == 0) {
+    const float lse_v = m_ref * kLn2 + logf(l);
+    if (direct) {
+      if (lse_out) lse_out[static_cast<int64_t>(b) * H + q] = lse_v;
+    } else {
+      lse_part[static_cast<int64_t>(it) * H + q] = lse_v;
+    }
+  }
   const float inv = 1.f / l;
-  float* orow = o_part + (static_cast<int64_t>(it) * H + q) * kDc + 128 * w + 4 * g;
+  float* orow = (direct ? o_latent + static_cast<int64_t>(b) * H * kDc
+                        : o_part + static_cast<int64_t>(it) * H * kDc) + q * kDc + 128 * w + 4 * g;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    float4_t v = oacc[c];
-    v[0] *= inv;
-    v[1] *= inv;
-    v[2] *= inv;
-    v[3] *= inv;
-    *reinterpret_cast<float4_t*>(orow + 16 * c) = v;
+    oacc[c][0] *= inv;
+    oacc[c][1] *= inv;
+    oacc[c][2] *= inv;
+    oacc[c][3] *= inv;
+    *reinterpret_cast<float4_t*>(orow + 16 * c) = oacc[c];
+  }
+  if (merged && nsplit > 1) {
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) ticket_lds = atomicAdd(&tickets[2 * b], 1);
+    __syncthreads();
+    if (ticket_lds == nsplit - 1) {
+      __threadfence();
+      float M = -INFINITY;
+      for (int s = s0; s < s0 + nsplit; ++s) M = fmaxf(M, lse_part[static_cast<int64_t>(s) * H + q]);
+      float Z = 0.f;
+      float4_t acc[8] = {};
+      for (int s = s0; s < s0 + nsplit; ++s) {
+        const int64_t r = static_cast<int64_t>(s) * H + q;
+        const float wgt = expf(lse_part[r] - M);
+        Z += wgt;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float4_t v = s == it ? oacc[c]
+                                     : *reinterpret_cast<const float4_t*>(o_part + r * kDc + 128 * w + 16 * c + 4 * g);
+          acc[c][0] = fmaf(wgt, v[0], acc[c][0]);
+          acc[c][1] = fmaf(wgt, v[1], acc[c][1]);
+          acc[c][2] = fmaf(wgt, v[2], acc[c][2]);
+          acc[c][3] = fmaf(wgt, v[3], acc[c][3]);
+        }
+      }
+      const float zinv = 1.f / Z;
+      float* lrow = o_latent + (static_cast<int64_t>(b) * H + q) * kDc + 128 * w + 4 * g;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        acc[c][0] *= zinv;
+        acc[c][1] *= zinv;
+        acc[c][2] *= zinv;
+        acc[c][3] *= zinv;
+        *reinterpret_cast<float4_t*>(lrow + 16 * c) = acc[c];
+      }
+      if (lse_out && w == 0 && g == 0) lse_out[static_cast<int64_t>(b) * H + q] = M + logf(Z);
+      if (threadIdx.x == 0) tickets[2 * b] = 0;
+    }
   }
 }
 
@@ -692,18 +813,19 @@ float max_jump() {
 hipError_t decode_fast(const mla_dims& d, const void* q_abs, const void* kv_cache,
                        const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                        const int32_t* items, int num_items, float* o_part, float* lse_part,
-                       hipStream_t stream) {
+                       const int32_t* split_offsets, int32_t* tickets, float* o_latent,
+                       float* lse_out, hipStream_t stream) {
   if (d.n_heads == 128) {
     hipLaunchKernelGGL(decode_h128_kernel, dim3(2 * num_items), dim3(1024), 0, stream,
                        static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
                        block_table, max_pages, seq_lens, items, num_items, d.softmax_scale,
-                       max_jump(), o_part, lse_part);
+                       max_jump(), o_part, lse_part, split_offsets, tickets, o_latent, lse_out);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(decode_h16_kernel, dim3(num_items), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
                      block_table, max_pages, seq_lens, items, d.softmax_scale, max_jump(), o_part,
-                     lse_part);
+                     lse_part, split_offsets, tickets, o_latent, lse_out);
   return hipGetLastError();
 }
 

@@ -118,9 +118,39 @@ mla_status mla_decode_splitkv(const mla_dims* dims, int32_t batch, const void* q
   (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
   if (is_fast_shape(*dims))
     return launched(decode_fast(*dims, q_abs, kv_cache, block_table, max_pages_per_seq, seq_lens,
-                                items, num_items, o_part, lse_part, st));
+                                items, num_items, o_part, lse_part, nullptr, nullptr, nullptr,
+                                nullptr, st));
   return launched(decode_generic(*dims, q_abs, kv_cache, block_table, max_pages_per_seq, seq_lens,
                                  items, num_items, o_part, lse_part, st));
+}
+
+mla_status mla_decode_merged(const mla_dims* dims, int32_t batch, const void* q_abs,
+                             const void* kv_cache, int32_t num_pages, const int32_t* block_table,
+                             int32_t max_pages_per_seq, const int32_t* seq_lens,
+                             const int32_t* items, int32_t num_items,
+                             const int32_t* split_offsets, float* o_part, float* lse_part,
+                             int32_t* tickets, float* o_latent, float* lse, void* stream) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  if (batch < 1 || num_pages < 1 || max_pages_per_seq < 1 || num_items < 1) return MLA_ERR_INVALID_ARG;
+  if (!q_abs || !kv_cache || !block_table || !seq_lens || !items || !split_offsets || !o_part ||
+      !lse_part || !tickets || !o_latent)
+    return MLA_ERR_INVALID_ARG;
+  if (!al16(q_abs) || !al16(kv_cache) || !al16(o_part) || !al16(o_latent) || !al4(lse_part) ||
+      !al4(block_table) || !al4(seq_lens) || !al4(items) || !al4(split_offsets) || !al4(tickets) ||
+      (lse && !al4(lse)))
+    return MLA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+  if (is_fast_shape(*dims))
+    return launched(decode_fast(*dims, q_abs, kv_cache, block_table, max_pages_per_seq, seq_lens,
+                                items, num_items, o_part, lse_part, split_offsets, tickets,
+                                o_latent, lse, st));
+  if (batch > 65535) return MLA_ERR_UNSUPPORTED;
+  mla_status r = launched(decode_generic(*dims, q_abs, kv_cache, block_table, max_pages_per_seq,
+                                         seq_lens, items, num_items, o_part, lse_part, st));
+  if (r != MLA_OK) return r;
+  return launched(combine_generic(*dims, batch, split_offsets, o_part, lse_part, o_latent, lse, st));
 }
 
 mla_status mla_combine(const mla_dims* dims, int32_t batch, const int32_t* split_offsets,

@@ -27,3 +27,10 @@ def mla():
     import mla_latent_kv_16_amd as m
     m.load()  # raises if libmla.so is missing
     return m
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The same check as `mla`, for tests that import the package under that name."""
+    import mla_latent_kv_16_amd as pkg
+    return pkg.load()

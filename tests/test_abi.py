@@ -30,7 +30,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"mla_absorb_q", "mla_plan_splits", "mla_decode_splitkv", "mla_combine",
-            "mla_out_proj"} <= set(names)
+            "mla_decode_merged", "mla_out_proj"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -95,6 +95,25 @@ def test_decode_rejects_bad_arguments(lib):
     args = list(good)
     args[8] = A + 4                                # o_part misaligned
     assert f(_d(), 2, *args) == INVALID
+
+
+def test_decode_merged_rejects_bad_arguments(lib):
+    f = lib.mla_decode_merged
+    # q_abs kv_cache num_pages bt max_pages seq_lens items num_items offs o_part lse_part tickets o_lat lse stream
+    good = [A, A, 10, A, 4, A, A, 3, A, A, A, A, A, None, None]
+    assert f(_d(), 0, *good) == INVALID
+    for i in (0, 1, 3, 5, 6, 8, 9, 10, 11, 12):    # each required pointer set to NULL
+        args = list(good)
+        args[i] = None
+        assert f(_d(), 2, *args) == INVALID, i
+    for i, bad in ((2, 0), (4, 0), (7, 0)):        # num_pages, max_pages, num_items < 1
+        args = list(good)
+        args[i] = bad
+        assert f(_d(), 2, *args) == INVALID, i
+    for i, bad in ((1, MIS), (9, A + 4), (11, A + 2), (12, A + 8), (13, A + 2)):
+        args = list(good)                          # misaligned cache, o_part, tickets, o_latent, lse
+        args[i] = bad
+        assert f(_d(), 2, *args) == INVALID, i
 
 
 def test_combine_and_out_proj_reject_bad_arguments(lib):
