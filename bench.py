@@ -3,9 +3,10 @@
 A step is one pass of the whole path over a batch: mla_absorb_q ->
 mla_decode_splitkv -> mla_combine -> mla_out_proj, on synthetic inputs already
 resident in HBM (the split plan is made once per batch shape, before timing).
+With --merged the decode and the merge run as one launch, mla_decode_merged.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-flush]
-                    [--no-cpu-baseline] [--copy-probe]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--merged]
+                    [--no-flush] [--no-cpu-baseline] [--copy-probe]
 
 Prints ONE JSON line on stdout; progress goes to stderr.  The step time comes
 from HIP events at the step boundaries; a second pass over the same steps with
@@ -109,6 +110,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v2_b64_l8192")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--merged", action="store_true",
+                    help="decode and merge in one launch (mla_decode_merged)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -158,6 +161,7 @@ def main():
         "o_latent": torch.empty((B, H, cfg.d_latent), dtype=torch.float32, device="cuda"),
         "lse": torch.empty((B, H), dtype=torch.float32, device="cuda"),
         "out": torch.empty((B, H, cfg.d_head), dtype=torch.float32, device="cuda"),
+        "tickets": torch.zeros(2 * B, dtype=torch.int32, device="cuda"),
     }
     flush = None
     if not args.no_flush:
@@ -169,23 +173,34 @@ def main():
         if flush is not None:
             torch.sum(flush, dim=0, keepdim=True, out=sink)
 
+    if not args.merged:
+        names = ["absorb_q", "decode_splitkv", "combine", "out_proj"]
+        launches = [
+            lambda: mla.absorb_q(dims, q_nope, q_pe, positions, w_uk, bufs["q_abs"], stream),
+            lambda: mla.decode_splitkv(dims, bufs["q_abs"], cache, block_table, seq_lens, items,
+                                       bufs["o_part"], bufs["lse_part"], stream),
+            lambda: mla.combine(dims, offs, bufs["o_part"], bufs["lse_part"], B, bufs["o_latent"],
+                                bufs["lse"], stream),
+            lambda: mla.out_proj(dims, bufs["o_latent"], w_uv, bufs["out"], stream),
+        ]
+    else:
+        names = ["absorb_q", "decode_merged", "out_proj"]
+        launches = [
+            lambda: mla.absorb_q(dims, q_nope, q_pe, positions, w_uk, bufs["q_abs"], stream),
+            lambda: mla.decode_merged(dims, bufs["q_abs"], cache, block_table, seq_lens, items, offs,
+                                      bufs["tickets"], bufs["o_part"], bufs["lse_part"],
+                                      bufs["o_latent"], bufs["lse"], stream),
+            lambda: mla.out_proj(dims, bufs["o_latent"], w_uv, bufs["out"], stream),
+        ]
+    n_k = len(launches)
+
     def step(ev=None):
+        for i, launch in enumerate(launches):
+            if ev is not None:
+                ev[i].record(stream)
+            launch()
         if ev is not None:
-            ev[0].record(stream)
-        mla.absorb_q(dims, q_nope, q_pe, positions, w_uk, bufs["q_abs"], stream)
-        if ev is not None:
-            ev[1].record(stream)
-        mla.decode_splitkv(dims, bufs["q_abs"], cache, block_table, seq_lens, items,
-                           bufs["o_part"], bufs["lse_part"], stream)
-        if ev is not None:
-            ev[2].record(stream)
-        mla.combine(dims, offs, bufs["o_part"], bufs["lse_part"], B, bufs["o_latent"],
-                    bufs["lse"], stream)
-        if ev is not None:
-            ev[3].record(stream)
-        mla.out_proj(dims, bufs["o_latent"], w_uv, bufs["out"], stream)
-        if ev is not None:
-            ev[4].record(stream)
+            ev[n_k].record(stream)
 
     for _ in range(args.warmup):
         evict()
@@ -209,14 +224,13 @@ def main():
     ms = float(step_ms.mean())
     # Per-kernel breakdown (and the decode launch time for the roofline): the
     # same K steps again with an event between every two kernels.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_k + 1)] for _ in range(args.steps)]
     for k in range(args.steps):
         evict()
         step(evs[k])
     torch.cuda.synchronize()
-    t = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])  # ms
+    t = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(n_k)] for e in evs])  # ms
     k_ms = t.mean(axis=0)
-    names = ["absorb_q", "decode_splitkv", "combine", "out_proj"]
     log("[bench] per-kernel mean ms: " + ", ".join(f"{n} {v:.4f}" for n, v in zip(names, k_ms)))
     log(f"[bench] step ms: mean {ms:.4f}  p10 {np.percentile(step_ms, 10):.4f}  "
         f"p90 {np.percentile(step_ms, 90):.4f}; wall incl. flushes {wall * 1e3 / args.steps:.3f} ms/step")
@@ -242,13 +256,14 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "seq_len": int(wl.seq_lens.max()),
                    "total_tokens": int(wl.seq_lens.sum()), "n_heads": H, "d_head": cfg.d_head,
                    "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "page_size": cfg.page_size,
-                   "work_items": int(len(items_h)), "mall_flushed": flush is not None},
+                   "work_items": int(len(items_h)), "mall_flushed": flush is not None,
+                   "decode_entry": names[1]},
         "latent_cache_GBps": round(work["cache_bytes"] / (ms * 1e-3) / 1e9, 1),
         "tokens_per_s": round(B / (ms * 1e-3), 1),
         "kernel_ms": {n: round(float(v), 5) for n, v in zip(names, k_ms)},
         "decode_TFLOPs": round(work["decode_flop"] / dec_s / 1e12, 2),
         "decode_mfma_frac": round(work["decode_flop"] / dec_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "roofline": {"kernel": "mla_decode_splitkv", "bound": "hbm",
+        "roofline": {"kernel": names[1], "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": work["decode_bytes"]},

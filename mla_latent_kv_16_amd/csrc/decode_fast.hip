@@ -357,10 +357,19 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       }
     }
     if (merge_tail) {  // same barriers as the V waves' merge tail
-      __threadfence();
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));  // this wave's stores have reached the L2
       __syncthreads();
-      if (threadIdx.x == 0) ticket_lds = atomicAdd(&tickets[2 * b + hh], 1);
+      if (threadIdx.x == 0) {
+        // release every wave's partial to the other XCDs (one L2 write-back),
+        // then take the ticket
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        ticket_lds = atomicAdd(&tickets[2 * b + hh], 1);
+      }
       __syncthreads();
+      if (ticket_lds == nsplit - 1) {
+        if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __syncthreads();
+      }
     }
   } else {
     // ======================= V waves: DMA and latent PV =======================
@@ -489,14 +498,15 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       }
     }
     if (merge_tail) {
-      // release this workgroup's partial, take a ticket; the last workgroup of
-      // the sequence half merges every partial in item order (the combine's
-      // arithmetic, its own partial from registers) and resets the ticket
-      __threadfence();
+      // release this workgroup's partial, take a ticket (S wave 0 does both);
+      // the last workgroup of the sequence half merges every partial in item
+      // order (the combine's arithmetic, its own partial from registers) and
+      // resets the ticket
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
       __syncthreads();
       __syncthreads();
       if (ticket_lds == nsplit - 1) {
-        __threadfence();
+        __syncthreads();  // after the acquire of S wave 0
 #pragma unroll
         for (int hb = 0; hb < kHeadBlocksWG; ++hb) {
           const int head = head0 + 16 * hb + q;
@@ -758,12 +768,16 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     *reinterpret_cast<float4_t*>(orow + 16 * c) = oacc[c];
   }
   if (merged && nsplit > 1) {
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));  // this wave's stores have reached the L2
     __syncthreads();
-    if (threadIdx.x == 0) ticket_lds = atomicAdd(&tickets[2 * b], 1);
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // one L2 write-back
+      ticket_lds = atomicAdd(&tickets[2 * b], 1);
+    }
     __syncthreads();
     if (ticket_lds == nsplit - 1) {
-      __threadfence();
+      if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __syncthreads();
       float M = -INFINITY;
       for (int s = s0; s < s0 + nsplit; ++s) M = fmaxf(M, lse_part[static_cast<int64_t>(s) * H + q]);
       float Z = 0.f;
