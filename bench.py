@@ -268,6 +268,33 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": work["decode_bytes"]},
     }
+    # The cache write of the next token of every sequence (mla_append_kv), timed
+    # on its own: it precedes the step in a model and is not part of `value`.
+    from synth import append_recipe, f32_to_bf16_bits
+    ar = append_recipe(cfg, B)
+    conv = (lambda a: f32_to_bf16_bits(a.astype(np.float32))) if bf else (lambda a: a.astype(np.float32))
+    h_d, wdkv_d, wkr_d = dev(conv(ar["h"]), bf), dev(conv(ar["w_dkv"]), bf), dev(conv(ar["w_kr"]), bf)
+    app_pos = torch.from_numpy(np.minimum(wl.seq_lens, wl.block_table.shape[1] * cfg.page_size - 1)
+                               .astype(np.int32)).cuda()
+    cache_bak = cache  # the rows written (one slot per sequence) are rewritten identically each launch
+    a_ms = []
+    for k in range(args.warmup + args.steps):
+        evict()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        mla.append_kv(dims, h_d, wdkv_d, wkr_d, app_pos, cache_bak, block_table, rms_norm=cfg.rms_norm_latent,
+                      stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if k >= args.warmup:
+            a_ms.append(e0.elapsed_time(e1))
+    a_ms = float(np.mean(a_ms))
+    esz = 2 if bf else 4
+    D = cfg.d_latent + cfg.d_rope
+    a_bytes = (D * cfg.d_model + B * cfg.d_model + B * D) * esz
+    result["append_kv"] = {"ms": round(a_ms, 5), "algorithmic_bytes": a_bytes,
+                           "GBps": round(a_bytes / (a_ms * 1e-3) / 1e9, 1), "d_model": cfg.d_model}
+    log(f"[bench] append_kv {a_ms * 1e3:.1f} us for {B} tokens ({a_bytes / 1e6:.2f} MB algorithmic)")
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -12,6 +12,7 @@
  *                       softmax, latent-space weighted sum, partial LSE
  *   mla_combine         log-sum-exp merge of the work items of a sequence
  *   mla_decode_merged   the two above in one launch
+ *   mla_append_kv       write the decoded token's [c^KV | RoPE(k^R)] row into the cache
  *   mla_out_proj        o_i = W^UV_i o~_i                                    (per head i)
  *
  * Pages describing the method (titles as published):
@@ -193,6 +194,34 @@ mla_status mla_decode_merged(const mla_dims* dims, int32_t batch, const void* q_
  * Errors: MLA_ERR_INVALID_ARG for null pointers, batch < 1 or misalignment. */
 mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const float* o_latent,
                         const void* w_uv, float* out, void* stream);
+
+/* Write the token being decoded into the paged latent cache, one per sequence.
+ * Page "DeepSeek V2 技术解析" 2.2.1.1 (only c^KV = W^DKV h_t is kept for the keys
+ * and values) and 2.2.2 (k^R_t = W^KR h_t, shared by the heads, cached after the
+ * rotation R_t); page "DeepSeek-V2/V3：大模型的两张账" "第一张账" (normalised latent).
+ * For every b, with p = positions[b]:
+ *   c  = W^DKV h[b]; if rms_norm: c = c / sqrt(mean(c^2) + eps)   (no gain)
+ *   kr = RoPE_p(W^KR h[b])  (pairs (2k, 2k+1), angle p * rope_base^(-2k/d_rope) in float64)
+ *   kv_cache row (page block_table[b][p / page_size], slot p % page_size) = [c | kr],
+ *   rounded to dtype (nearest, ties to even).  No other byte of the cache changes.
+ * Layouts: h [batch][d_model] dtype; w_dkv [d_latent][d_model] dtype; w_kr
+ * [d_rope][d_model] dtype (both map column vectors); positions [batch] int32;
+ * kv_cache, block_table as for mla_decode_splitkv.  Products accumulate in float32.
+ * workspace: device memory of at least mla_append_kv_workspace_bytes() bytes,
+ * 16-byte aligned, owned by the caller; its contents afterwards are unspecified.
+ * Device data is not checked: p must lie in [0, max_pages_per_seq * page_size)
+ * and the block-table entry in [0, num_pages); two sequences must not write the
+ * same slot.
+ * Errors: MLA_ERR_INVALID_ARG for null pointers, sizes < 1, misalignment or a
+ * non-positive eps with rms_norm set; MLA_ERR_WORKSPACE for a short workspace. */
+mla_status mla_append_kv(const mla_dims* dims, int32_t d_model, int32_t batch, const void* h,
+                         const void* w_dkv, const void* w_kr, const int32_t* positions,
+                         int32_t rms_norm, float eps, void* kv_cache, int32_t num_pages,
+                         const int32_t* block_table, int32_t max_pages_per_seq, void* workspace,
+                         int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mla_append_kv needs; -1 on bad arguments.  Host only. */
+int64_t mla_append_kv_workspace_bytes(const mla_dims* dims, int32_t d_model, int32_t batch);
 
 /* Text of the last HIP error that made a libmla call on this thread return
  * MLA_ERR_HIP ("" if none).  Valid until the next libmla call on the thread. */

@@ -6,7 +6,7 @@ C ABI as raw device pointers.  The binding fails loudly when libmla.so has not
 been built -- there is no fallback.
 
 Entry points mirror include/mla.h:
-    absorb_q, plan_splits, decode_splitkv, combine, decode_merged, out_proj
+    absorb_q, plan_splits, decode_splitkv, combine, decode_merged, out_proj, append_kv
 plus `decode_step`, which runs the four device steps in order.
 """
 from __future__ import annotations
@@ -19,7 +19,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = ["MlaError", "Dims", "load", "lib_path", "absorb_q", "plan_splits", "decode_splitkv",
-           "decode_merged",
+           "decode_merged", "append_kv",
            "combine", "out_proj", "decode_step", "fast_path", "version", "BF16", "F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -96,6 +96,9 @@ def load():
         "mla_decode_merged": (i32, [pd, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp,
                                      vp, vp]),
         "mla_out_proj": (i32, [pd, i32, vp, vp, vp, vp]),
+        "mla_append_kv": (i32, [pd, i32, i32, vp, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, i32,
+                                 vp, ctypes.c_int64, vp]),
+        "mla_append_kv_workspace_bytes": (ctypes.c_int64, [pd, i32, i32]),
         "mla_status_string": (ctypes.c_char_p, [i32]),
         "mla_version": (i32, []),
         "mla_fast_path": (i32, [pd]),
@@ -270,6 +273,30 @@ def decode_merged(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items, spl
         _ptr(o_latent, torch.float32, (B, H, dims.d_latent), "o_latent"),
         _ptr(lse, torch.float32, (B, H), "lse"), _stream(stream)), "mla_decode_merged")
     return o_latent, lse
+
+
+def append_kv(dims: Dims, h, w_dkv, w_kr, positions, kv_cache, block_table, rms_norm: bool = True,
+              eps: float = 1e-6, workspace=None, stream=None):
+    """Write each sequence's new token row [c^KV | RoPE(k^R)] into the paged cache (in place)."""
+    torch = _torch()
+    dt = _store_dtype(dims)
+    B, d_model = h.shape
+    L = load()
+    need = L.mla_append_kv_workspace_bytes(ctypes.byref(dims.c()), d_model, B)
+    if need < 0:
+        raise MlaError(-1, "mla_append_kv_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=h.device)
+    num_pages = kv_cache.shape[0]
+    _check(L.mla_append_kv(
+        ctypes.byref(dims.c()), d_model, B, _ptr(h, dt, (B, d_model), "h"),
+        _ptr(w_dkv, dt, (dims.d_latent, d_model), "w_dkv"), _ptr(w_kr, dt, (dims.d_rope, d_model), "w_kr"),
+        _ptr(positions, torch.int32, (B,), "positions"), int(bool(rms_norm)), float(eps),
+        _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
+        _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
+        _ptr(workspace, None, None, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "mla_append_kv")
+    return kv_cache
 
 
 def out_proj(dims: Dims, o_latent, w_uv, out=None, stream=None):

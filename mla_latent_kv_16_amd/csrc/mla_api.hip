@@ -170,6 +170,35 @@ mla_status mla_combine(const mla_dims* dims, int32_t batch, const int32_t* split
   return launched(combine_generic(*dims, batch, split_offsets, o_part, lse_part, o_latent, lse, st));
 }
 
+int64_t mla_append_kv_workspace_bytes(const mla_dims* dims, int32_t d_model, int32_t batch) {
+  if (check_dims(dims) != MLA_OK || d_model < 1 || batch < 1) return -1;
+  return static_cast<int64_t>(append_slices(d_model)) * batch * (dims->d_latent + dims->d_rope) *
+         static_cast<int64_t>(sizeof(float));
+}
+
+mla_status mla_append_kv(const mla_dims* dims, int32_t d_model, int32_t batch, const void* h,
+                         const void* w_dkv, const void* w_kr, const int32_t* positions,
+                         int32_t rms_norm, float eps, void* kv_cache, int32_t num_pages,
+                         const int32_t* block_table, int32_t max_pages_per_seq, void* workspace,
+                         int64_t workspace_bytes, void* stream) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  if (d_model < 1 || batch < 1 || num_pages < 1 || max_pages_per_seq < 1) return MLA_ERR_INVALID_ARG;
+  if (!h || !w_dkv || !w_kr || !positions || !kv_cache || !block_table || !workspace)
+    return MLA_ERR_INVALID_ARG;
+  if (rms_norm && !(eps > 0.f && isfinite(eps))) return MLA_ERR_INVALID_ARG;
+  if (!al16(h) || !al16(w_dkv) || !al16(w_kr) || !al16(kv_cache) || !al16(workspace) ||
+      !al4(positions) || !al4(block_table))
+    return MLA_ERR_INVALID_ARG;
+  if (d_model > (1 << 20) || batch > 65535) return MLA_ERR_UNSUPPORTED;
+  if (workspace_bytes < mla_append_kv_workspace_bytes(dims, d_model, batch)) return MLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+  return launched(append_kv(*dims, d_model, batch, h, w_dkv, w_kr, positions, rms_norm != 0, eps,
+                            kv_cache, block_table, max_pages_per_seq,
+                            static_cast<float*>(workspace), st));
+}
+
 mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const float* o_latent,
                         const void* w_uv, float* out, void* stream) {
   mla_status s = check_dims(dims);

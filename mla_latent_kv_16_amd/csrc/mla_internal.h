@@ -47,6 +47,14 @@ hipError_t combine_fast(const mla_dims& d, int batch, const int32_t* split_offse
 hipError_t out_proj_fast(const mla_dims& d, int batch, const float* o_latent, const void* w_uv,
                          float* out, hipStream_t stream);
 
+// Cache write of one token per sequence (append.hip); `ws` holds
+// append_slices(d_model) x batch x (d_latent + d_rope) floats.
+int append_slices(int d_model);
+hipError_t append_kv(const mla_dims& d, int d_model, int batch, const void* h, const void* w_dkv,
+                     const void* w_kr, const int32_t* positions, bool rms_norm, float eps,
+                     void* kv_cache, const int32_t* block_table, int max_pages, float* ws,
+                     hipStream_t stream);
+
 // Host planner (plan.cpp).
 mla_status plan_splits(int page_size, int batch, const int32_t* seq_lens, int num_slots,
                        int max_items, int32_t* items, int32_t* split_offsets, int32_t* num_items,

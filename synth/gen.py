@@ -256,3 +256,16 @@ def hidden_recipe(cfg: MLAConfig, length: int) -> dict:
     }
     out["h"] = r.standard_normal((length, dm))
     return out
+
+
+def append_recipe(cfg: MLAConfig, batch: int) -> dict:
+    """Inputs of the cache write of one new token per sequence, float64:
+    h [batch, d_model] ~ N(0, 1), W^DKV [d_c, d_model] and W^KR [d_h^R, d_model]
+    ~ N(0, 1/d_model) (matrices map column vectors)."""
+    r = _rng(cfg, 4)
+    dm = cfg.d_model
+    return {
+        "w_dkv": r.standard_normal((cfg.d_latent, dm)) / np.sqrt(dm),
+        "w_kr": r.standard_normal((cfg.d_rope, dm)) / np.sqrt(dm),
+        "h": r.standard_normal((batch, dm)),
+    }

@@ -30,7 +30,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"mla_absorb_q", "mla_plan_splits", "mla_decode_splitkv", "mla_combine",
-            "mla_decode_merged", "mla_out_proj"} <= set(names)
+            "mla_decode_merged", "mla_append_kv", "mla_out_proj"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -114,6 +114,33 @@ def test_decode_merged_rejects_bad_arguments(lib):
         args = list(good)                          # misaligned cache, o_part, tickets, o_latent, lse
         args[i] = bad
         assert f(_d(), 2, *args) == INVALID, i
+
+
+def test_append_kv_rejects_bad_arguments(lib):
+    f = lib.mla_append_kv
+    need = lib.mla_append_kv_workspace_bytes(_d(), 5120, 64)
+    assert need == 8 * 64 * 576 * 4                   # ceil(5120 / 640) K-slices
+    assert lib.mla_append_kv_workspace_bytes(_d(), 0, 64) == -1
+    # d_model batch h w_dkv w_kr positions rms eps cache num_pages bt max_pages ws ws_bytes stream
+    good = [5120, 64, A, A, A, A, 1, 1e-6, A, 10, A, 4, A, need, None]
+    for i in (2, 3, 4, 5, 8, 10, 12):              # each pointer argument set to NULL
+        args = list(good)
+        args[i] = None
+        assert f(_d(), *args) == INVALID, i
+    for i, bad in ((0, 0), (1, 0), (9, 0), (11, 0)):   # sizes < 1
+        args = list(good)
+        args[i] = bad
+        assert f(_d(), *args) == INVALID, i
+    for i, bad in ((2, MIS), (8, MIS), (12, MIS), (5, A + 2)):  # misaligned
+        args = list(good)
+        args[i] = bad
+        assert f(_d(), *args) == INVALID, i
+    args = list(good)
+    args[7] = 0.0                                  # rms_norm with eps <= 0
+    assert f(_d(), *args) == INVALID
+    args = list(good)
+    args[13] = need - 4                            # short workspace
+    assert f(_d(), *args) == WORKSPACE
 
 
 def test_combine_and_out_proj_reject_bad_arguments(lib):
