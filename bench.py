@@ -4,9 +4,12 @@ A step is one pass of the whole path over a batch: mla_absorb_q ->
 mla_decode_splitkv -> mla_combine -> mla_out_proj, on synthetic inputs already
 resident in HBM (the split plan is made once per batch shape, before timing).
 With --merged the decode and the merge run as one launch, mla_decode_merged.
+With --q-len T every sequence decodes its T newest tokens at once (causal among
+them): absorb and out_proj on B*T rows, mla_decode_splitkv_multi and
+mla_combine_multi in between.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--merged]
-                    [--no-flush] [--no-cpu-baseline] [--copy-probe]
+                    [--q-len T] [--no-flush] [--no-cpu-baseline] [--copy-probe]
 
 Prints ONE JSON line on stdout; progress goes to stderr.  The step time comes
 from HIP events at the step boundaries; a second pass over the same steps with
@@ -43,16 +46,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic(cfg, lens):
-    """Algorithmic work of one step and of one decode launch."""
+def algorithmic(cfg, lens, q_len: int = 1):
+    """Algorithmic work of one step and of one decode launch (q_len query
+    tokens per sequence; token t of T sees L - T + t + 1 rows)."""
     L = lens.astype(np.int64)
-    B, H = cfg.batch, cfg.n_heads
+    B, H, T = cfg.batch, cfg.n_heads, q_len
     D = cfg.d_latent + cfg.d_rope
     pages = int(((L + cfg.page_size - 1) // cfg.page_size).sum())
-    decode_flop = int(L.sum()) * H * 2 * (D + cfg.d_latent)
-    dense_flop = 2 * B * H * cfg.d_head * cfg.d_latent * 2   # absorb + out_proj
+    seen = int(L.sum()) * T - B * T * (T - 1) // 2       # rows scored, over all tokens
+    decode_flop = seen * H * 2 * (D + cfg.d_latent)
+    dense_flop = 2 * B * T * H * cfg.d_head * cfg.d_latent * 2   # absorb + out_proj
     cache_bytes = int(L.sum()) * D * 2
-    decode_bytes = cache_bytes + B * H * D * 2 + B * H * (cfg.d_latent + 1) * 4 + 4 * pages
+    decode_bytes = (cache_bytes + B * T * H * D * 2 + B * T * H * (cfg.d_latent + 1) * 4
+                    + 4 * pages)
     return dict(decode_flop=decode_flop, step_flop=decode_flop + dense_flop,
                 cache_bytes=cache_bytes, decode_bytes=decode_bytes, pages=pages)
 
@@ -112,6 +118,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--merged", action="store_true",
                     help="decode and merge in one launch (mla_decode_merged)")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per sequence (multi-token decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -120,11 +128,15 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the path does not shard across GPUs in this build)", file=sys.stderr)
         sys.exit(2)
+    T = args.q_len
+    if T < 1 or (T > 1 and args.merged):
+        print("--q-len must be >= 1, and 1 with --merged", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
     import mla_latent_kv_16_amd as mla
-    from synth import CONFIGS, generate
+    from synth import CONFIGS, generate, query_multi
 
     cfg = CONFIGS[args.workload]
     t0 = time.perf_counter()
@@ -139,8 +151,16 @@ def main():
         return t.cuda()
 
     bf = cfg.dtype == "bf16"
-    q_nope, q_pe = dev(wl.q_nope, bf), dev(wl.q_pe, bf)
-    positions = dev(wl.positions, False)
+    B, H = cfg.batch, cfg.n_heads
+    if T == 1:
+        q_nope, q_pe = dev(wl.q_nope, bf), dev(wl.q_pe, bf)
+        positions = dev(wl.positions, False)
+    else:
+        qs = [query_multi(cfg, b, T) for b in range(B)]
+        q_nope = dev(np.stack([a for a, _ in qs]).reshape(B * T, H, cfg.d_head), bf)
+        q_pe = dev(np.stack([p for _, p in qs]).reshape(B * T, H, cfg.d_rope), bf)
+        pos = wl.seq_lens[:, None].astype(np.int64) - T + np.arange(T)[None, :]
+        positions = dev(pos.reshape(-1).astype(np.int32), False)
     w_uk, w_uv = dev(wl.w_uk, bf), dev(wl.w_uv, bf)
     cache = dev(wl.cache, bf)
     block_table, seq_lens = dev(wl.block_table, False), dev(wl.seq_lens, False)
@@ -148,21 +168,25 @@ def main():
                     rope_base=cfg.rope_base, dtype=mla.BF16 if bf else mla.F32)
     props = torch.cuda.get_device_properties(0)
     slots = int(props.multi_processor_count)
-    items_h, offs_h = mla.plan_splits(dims, wl.seq_lens, slots)
+    # each item is decoded once per query token: plan for the CUs over T
+    items_h, offs_h = mla.plan_splits(dims, wl.seq_lens, max(1, slots // T))
     items, offs = torch.from_numpy(items_h).cuda(), torch.from_numpy(offs_h).cuda()
     log(f"[bench] {props.name} {getattr(props, 'gcnArchName', '')}, {slots} CUs; "
-        f"{len(items_h)} work items")
+        f"{len(items_h)} work items, q_len {T}")
 
-    B, H = cfg.batch, cfg.n_heads
+    W = len(items_h)
     bufs = {
-        "q_abs": torch.empty((B, H, dims.row), dtype=q_nope.dtype, device="cuda"),
-        "o_part": torch.empty((len(items_h), H, cfg.d_latent), dtype=torch.float32, device="cuda"),
-        "lse_part": torch.empty((len(items_h), H), dtype=torch.float32, device="cuda"),
-        "o_latent": torch.empty((B, H, cfg.d_latent), dtype=torch.float32, device="cuda"),
-        "lse": torch.empty((B, H), dtype=torch.float32, device="cuda"),
-        "out": torch.empty((B, H, cfg.d_head), dtype=torch.float32, device="cuda"),
+        "q_abs": torch.empty((B * T, H, dims.row), dtype=q_nope.dtype, device="cuda"),
+        "o_part": torch.empty((W, T, H, cfg.d_latent), dtype=torch.float32, device="cuda"),
+        "lse_part": torch.empty((W, T, H), dtype=torch.float32, device="cuda"),
+        "o_latent": torch.empty((B * T, H, cfg.d_latent), dtype=torch.float32, device="cuda"),
+        "lse": torch.empty((B * T, H), dtype=torch.float32, device="cuda"),
+        "out": torch.empty((B * T, H, cfg.d_head), dtype=torch.float32, device="cuda"),
         "tickets": torch.zeros(2 * B, dtype=torch.int32, device="cuda"),
     }
+    if T == 1:
+        for k in ("o_part", "lse_part"):
+            bufs[k] = bufs[k].view(W, *bufs[k].shape[2:])
     flush = None
     if not args.no_flush:
         flush = torch.full((128 << 20,), 1.0, dtype=torch.float32, device="cuda")  # 512 MiB
@@ -173,7 +197,20 @@ def main():
         if flush is not None:
             torch.sum(flush, dim=0, keepdim=True, out=sink)
 
-    if not args.merged:
+    if T > 1:
+        names = ["absorb_q", "decode_splitkv_multi", "combine_multi", "out_proj"]
+        q4 = bufs["q_abs"].view(B, T, H, dims.row)
+        ol4 = bufs["o_latent"].view(B, T, H, cfg.d_latent)
+        lse3 = bufs["lse"].view(B, T, H)
+        launches = [
+            lambda: mla.absorb_q(dims, q_nope, q_pe, positions, w_uk, bufs["q_abs"], stream),
+            lambda: mla.decode_splitkv_multi(dims, q4, cache, block_table, seq_lens, items,
+                                             bufs["o_part"], bufs["lse_part"], stream),
+            lambda: mla.combine_multi(dims, offs, bufs["o_part"], bufs["lse_part"], B, ol4, lse3,
+                                      stream),
+            lambda: mla.out_proj(dims, bufs["o_latent"], w_uv, bufs["out"], stream),
+        ]
+    elif not args.merged:
         names = ["absorb_q", "decode_splitkv", "combine", "out_proj"]
         launches = [
             lambda: mla.absorb_q(dims, q_nope, q_pe, positions, w_uk, bufs["q_abs"], stream),
@@ -236,10 +273,10 @@ def main():
         f"p90 {np.percentile(step_ms, 90):.4f}; wall incl. flushes {wall * 1e3 / args.steps:.3f} ms/step")
     assert torch.isfinite(bufs["out"]).all().item(), "non-finite output"
 
-    work = algorithmic(cfg, wl.seq_lens)
+    work = algorithmic(cfg, wl.seq_lens, T)
     dec_s = float(k_ms[1]) * 1e-3
     achieved = work["decode_bytes"] / dec_s / 1e9
-    traffic = measured_traffic(cfg.name)
+    traffic = measured_traffic(cfg.name) if T == 1 and not args.merged else None
     result = {
         "metric": METRIC,
         "value": round(work["step_flop"] / (ms * 1e-3) / 1e12, 3),
@@ -257,9 +294,9 @@ def main():
                    "total_tokens": int(wl.seq_lens.sum()), "n_heads": H, "d_head": cfg.d_head,
                    "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "page_size": cfg.page_size,
                    "work_items": int(len(items_h)), "mall_flushed": flush is not None,
-                   "decode_entry": names[1]},
+                   "decode_entry": names[1], "q_len": T},
         "latent_cache_GBps": round(work["cache_bytes"] / (ms * 1e-3) / 1e9, 1),
-        "tokens_per_s": round(B / (ms * 1e-3), 1),
+        "tokens_per_s": round(B * T / (ms * 1e-3), 1),
         "kernel_ms": {n: round(float(v), 5) for n, v in zip(names, k_ms)},
         "decode_TFLOPs": round(work["decode_flop"] / dec_s / 1e12, 2),
         "decode_mfma_frac": round(work["decode_flop"] / dec_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -12,6 +12,8 @@
  *                       softmax, latent-space weighted sum, partial LSE
  *   mla_combine         log-sum-exp merge of the work items of a sequence
  *   mla_decode_merged   the two above in one launch
+ *   mla_decode_splitkv_multi, mla_combine_multi
+ *                       the same for q_len query tokens per sequence (causal)
  *   mla_append_kv       write the decoded token's [c^KV | RoPE(k^R)] row into the cache
  *   mla_out_proj        o_i = W^UV_i o~_i                                    (per head i)
  *
@@ -154,6 +156,31 @@ mla_status mla_decode_splitkv(const mla_dims* dims, int32_t batch, const void* q
                               const int32_t* items, int32_t num_items, float* o_part,
                               float* lse_part, void* stream);
 
+/* Split-KV decode with q_len query tokens per sequence (speculative or chunked
+ * decode: the newest q_len tokens of each sequence, already in the cache, are
+ * decoded at once).  Page "DeepSeek V2 技术解析" 2.2.1.2 (the query of a step
+ * sees only the tokens up to the one being predicted); the rest as for
+ * mla_decode_splitkv.  Query token t of sequence b sits at position
+ * L_b - q_len + t and sees cache rows j <= L_b - q_len + t.  For item w and token t:
+ *   s_ij = softmax_scale * (q_abs[b][t][i] . kv_row_j),  j in [p0*page_size,
+ *          min(p1*page_size, L_b - q_len + t + 1))
+ *   lse_part[w][t][i], o_part[w][t][i] as for mla_decode_splitkv over those j;
+ *   an item none of whose rows the token sees gives lse_part = -inf and o_part = 0
+ *   (weight 0 in the merge).
+ * Layouts: q_abs [batch][q_len][n_heads][d_latent + d_rope] (the rows of
+ * mla_absorb_q called on batch * q_len rows); o_part [num_items][q_len][n_heads]
+ * [d_latent] float32; lse_part [num_items][q_len][n_heads] float32.  Items and
+ * the cache as for mla_decode_splitkv; q_len = 1 is mla_decode_splitkv.
+ * Device data is not checked: every L_b must be >= q_len (a token that sees no
+ * row has no defined output).
+ * Errors: as for mla_decode_splitkv, plus MLA_ERR_INVALID_ARG for q_len < 1. */
+mla_status mla_decode_splitkv_multi(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                    const void* q_abs, const void* kv_cache, int32_t num_pages,
+                                    const int32_t* block_table, int32_t max_pages_per_seq,
+                                    const int32_t* seq_lens, const int32_t* items,
+                                    int32_t num_items, float* o_part, float* lse_part,
+                                    void* stream);
+
 /* Merge the work items of every sequence (exact softmax algebra over disjoint
  * token sets): M = max_s lse_s, w_s = exp(lse_s - M),
  * o_latent = sum_s w_s o_s / sum_s w_s, lse = M + log sum_s w_s.
@@ -162,6 +189,14 @@ mla_status mla_decode_splitkv(const mla_dims* dims, int32_t batch, const void* q
 mla_status mla_combine(const mla_dims* dims, int32_t batch, const int32_t* split_offsets,
                        const float* o_part, const float* lse_part, float* o_latent, float* lse,
                        void* stream);
+
+/* mla_combine for the partials of mla_decode_splitkv_multi: row (b, t) merges
+ * o_part[w][t] over the items w of sequence b.  o_latent [batch][q_len][n_heads]
+ * [d_latent] float32, lse [batch][q_len][n_heads] float32 or NULL.
+ * Errors: as for mla_combine, plus MLA_ERR_INVALID_ARG for q_len < 1. */
+mla_status mla_combine_multi(const mla_dims* dims, int32_t batch, int32_t q_len,
+                             const int32_t* split_offsets, const float* o_part,
+                             const float* lse_part, float* o_latent, float* lse, void* stream);
 
 /* Split-KV decode with the log-sum-exp merge fused in: the o_latent and lse of
  * mla_combine from one launch (same items and split_offsets as the two calls).

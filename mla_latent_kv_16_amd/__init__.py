@@ -6,7 +6,8 @@ C ABI as raw device pointers.  The binding fails loudly when libmla.so has not
 been built -- there is no fallback.
 
 Entry points mirror include/mla.h:
-    absorb_q, plan_splits, decode_splitkv, combine, decode_merged, out_proj, append_kv
+    absorb_q, plan_splits, decode_splitkv, combine, decode_merged, out_proj, append_kv,
+    decode_splitkv_multi, combine_multi
 plus `decode_step`, which runs the four device steps in order.
 """
 from __future__ import annotations
@@ -19,7 +20,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = ["MlaError", "Dims", "load", "lib_path", "absorb_q", "plan_splits", "decode_splitkv",
-           "decode_merged", "append_kv",
+           "decode_merged", "append_kv", "decode_splitkv_multi", "combine_multi",
            "combine", "out_proj", "decode_step", "fast_path", "version", "BF16", "F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +94,9 @@ def load():
         "mla_plan_max_items": (ctypes.c_int64, [pd, i32, pi32]),
         "mla_decode_splitkv": (i32, [pd, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp]),
         "mla_combine": (i32, [pd, i32, vp, vp, vp, vp, vp, vp]),
+        "mla_decode_splitkv_multi": (i32, [pd, i32, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp,
+                                            vp]),
+        "mla_combine_multi": (i32, [pd, i32, i32, vp, vp, vp, vp, vp, vp]),
         "mla_decode_merged": (i32, [pd, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp,
                                      vp, vp]),
         "mla_out_proj": (i32, [pd, i32, vp, vp, vp, vp]),
@@ -237,6 +241,53 @@ def combine(dims: Dims, split_offsets, o_part, lse_part, batch: int, o_latent=No
         _ptr(lse_part, torch.float32, (W, H), "lse_part"),
         _ptr(o_latent, torch.float32, (batch, H, dims.d_latent), "o_latent"),
         _ptr(lse, torch.float32, (batch, H), "lse"), _stream(stream)), "mla_combine")
+    return o_latent, lse
+
+
+def decode_splitkv_multi(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items,
+                         o_part=None, lse_part=None, stream=None):
+    """q_len query tokens per sequence, q_abs [B, T, H, d_c + d_r]:
+    (o_part [W, T, H, d_c] float32, lse_part [W, T, H] float32).  Token t of
+    sequence b sees cache rows 0 .. seq_lens[b] - T + t."""
+    torch = _torch()
+    dt = _store_dtype(dims)
+    B, T, H = q_abs.shape[0], q_abs.shape[1], dims.n_heads
+    W = items.shape[0]
+    dev = q_abs.device
+    if o_part is None:
+        o_part = torch.empty((W, T, H, dims.d_latent), dtype=torch.float32, device=dev)
+    if lse_part is None:
+        lse_part = torch.empty((W, T, H), dtype=torch.float32, device=dev)
+    num_pages = kv_cache.shape[0]
+    _check(load().mla_decode_splitkv_multi(
+        ctypes.byref(dims.c()), B, T, _ptr(q_abs, dt, (B, T, H, dims.row), "q_abs"),
+        _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
+        _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
+        _ptr(seq_lens, torch.int32, (B,), "seq_lens"), _ptr(items, torch.int32, (W, 4), "items"), W,
+        _ptr(o_part, torch.float32, (W, T, H, dims.d_latent), "o_part"),
+        _ptr(lse_part, torch.float32, (W, T, H), "lse_part"), _stream(stream)),
+        "mla_decode_splitkv_multi")
+    return o_part, lse_part
+
+
+def combine_multi(dims: Dims, split_offsets, o_part, lse_part, batch: int, o_latent=None, lse=None,
+                  stream=None, want_lse: bool = True):
+    """LSE merge per (sequence, query token): (o_latent [B, T, H, d_c], lse [B, T, H] or None)."""
+    torch = _torch()
+    H = dims.n_heads
+    W, T = o_part.shape[0], o_part.shape[1]
+    dev = o_part.device
+    if o_latent is None:
+        o_latent = torch.empty((batch, T, H, dims.d_latent), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((batch, T, H), dtype=torch.float32, device=dev)
+    _check(load().mla_combine_multi(
+        ctypes.byref(dims.c()), batch, T,
+        _ptr(split_offsets, torch.int32, (batch + 1,), "split_offsets"),
+        _ptr(o_part, torch.float32, (W, T, H, dims.d_latent), "o_part"),
+        _ptr(lse_part, torch.float32, (W, T, H), "lse_part"),
+        _ptr(o_latent, torch.float32, (batch, T, H, dims.d_latent), "o_latent"),
+        _ptr(lse, torch.float32, (batch, T, H), "lse"), _stream(stream)), "mla_combine_multi")
     return o_latent, lse
 
 

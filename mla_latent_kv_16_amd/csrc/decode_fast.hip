@@ -165,7 +165,7 @@ static_assert(kStages * kSlotBytes + 2 * kPBytesWG + kSWaves * 4 + 4 * kHeadsWG 
 __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ items, int num_items, float scale, float max_jump,
+    const int32_t* __restrict__ items, int num_items, int q_len, float scale, float max_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
   constexpr int H = 128;
@@ -183,31 +183,46 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
   const int g = lane >> 4;   // lane group (k block of the MFMA operands)
   const int q = lane & 15;   // row/column within a 16-block
 
-  // block -> (item, half): blocks 16m + j and 16m + j + 8 (j < 8) take the two
-  // halves of item 8m + j; a last incomplete group of items is laid out the
-  // same way over the blocks that remain.
-  int it, hh;
+  // block -> (item, query token, half): an item has per = 2 q_len workgroups;
+  // blocks 8 per m + 8 r + j (j < 8, r < per) take part r of item 8m + j, so
+  // all parts of an item run on one XCD (blocks go to XCDs round-robin) and
+  // are dispatched together; a last incomplete group of items is laid out the
+  // same way over the blocks that remain.  Part r = query token r / 2, half r % 2.
+  int it, part;
   {
+    const int per = 2 * q_len;
     const int blk = blockIdx.x;
     const int full = num_items & ~7;
-    if (blk < 2 * full) {
-      it = (blk >> 4) * 8 + (blk & 7);
-      hh = (blk >> 3) & 1;
+    if (blk < per * full) {
+      it = (blk / (8 * per)) * 8 + (blk & 7);
+      part = (blk >> 3) % per;
     } else {
-      const int j = blk - 2 * full, rest = num_items - full;
+      const int j = blk - per * full, rest = num_items - full;
       it = full + j % rest;
-      hh = j / rest;
+      part = j / rest;
     }
   }
+  const int hh = part & 1, tq = part >> 1;
   const int b = items[4 * it];
   const int p0 = items[4 * it + 2];
   const int p1 = items[4 * it + 3];
   const int L = seq_lens[b];
   const int t_begin = p0 * kPage;
-  const int t_end = min(p1 * kPage, L);
+  // query token tq sits at position L - q_len + tq and sees tokens up to it
+  const int t_end = min(p1 * kPage, L - q_len + tq + 1);
   const int n_slices = (t_end - t_begin + kSliceTok - 1) / kSliceTok;
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
   const int head0 = kHeadsWG * hh;
+  const int64_t qrow0 = (static_cast<int64_t>(b) * q_len + tq) * H;    // q_abs row of head 0
+  const int64_t prow0 = (static_cast<int64_t>(it) * q_len + tq) * H;   // partial row of head 0
+  if (n_slices <= 0) {
+    // none of the item's tokens is visible to this query token: an empty
+    // partial (weight 0 in the merge); uniform over the workgroup, no barrier
+    for (int i = threadIdx.x; i < kHeadsWG * kDc; i += blockDim.x)
+      o_part[(prow0 + head0 + i / kDc) * kDc + i % kDc] = 0.f;
+    if (threadIdx.x < kHeadsWG) lse_part[prow0 + head0 + threadIdx.x] = -INFINITY;
+    return;
+  }
   // Merged mode (tickets != null): o~ and lse of the sequence instead of a
   // partial when the sequence has one item, else the partial and, in the last
   // workgroup of the sequence half to finish, the merge of all its partials.
@@ -236,7 +251,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     const int hb = w & 3, th = w >> 2;
     bf16x8 qf[18];  // B operand: head head0 + 16hb + q, values 32ks + 8g .. +8
     {
-      const uint16_t* qrow = q_abs + (static_cast<int64_t>(b) * H + head0 + 16 * hb + q) * kDq + 8 * g;
+      const uint16_t* qrow = q_abs + (qrow0 + head0 + 16 * hb + q) * kDq + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
     }
@@ -353,7 +368,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       if (direct) {
         if (lse_out) lse_out[static_cast<int64_t>(b) * H + head0 + hidx] = lse_v;
       } else {
-        lse_part[static_cast<int64_t>(it) * H + head0 + hidx] = lse_v;
+        lse_part[prow0 + head0 + hidx] = lse_v;
       }
     }
     if (merge_tail) {  // same barriers as the V waves' merge tail
@@ -486,7 +501,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     for (int hb = 0; hb < kHeadBlocksWG; ++hb) {
       const float inv = 1.f / (lsum2[0][16 * hb + q] + lsum2[1][16 * hb + q]);
       const int64_t row = direct ? static_cast<int64_t>(b) * H + head0 + 16 * hb + q
-                                 : static_cast<int64_t>(it) * H + head0 + 16 * hb + q;
+                                 : prow0 + head0 + 16 * hb + q;
       float* orow = (direct ? o_latent : o_part) + row * kDc + 64 * u + 4 * g;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -558,8 +573,8 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
 __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ items, float scale, float max_jump, float* __restrict__ o_part,
-    float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
+    const int32_t* __restrict__ items, int num_items, int q_len, float scale, float max_jump,
+    float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
   constexpr int H = 16;
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes];
@@ -573,15 +588,35 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
   const int g = lane >> 4;
   const int q = lane & 15;
 
-  const int it = blockIdx.x;
+  // block -> (item, query token), laid out as in the 128-head kernel
+  int it, tq;
+  {
+    const int blk = blockIdx.x;
+    const int full = num_items & ~7;
+    if (blk < q_len * full) {
+      it = (blk / (8 * q_len)) * 8 + (blk & 7);
+      tq = (blk >> 3) % q_len;
+    } else {
+      const int j = blk - q_len * full, rest = num_items - full;
+      it = full + j % rest;
+      tq = j / rest;
+    }
+  }
   const int b = items[4 * it];
   const int p0 = items[4 * it + 2];
   const int p1 = items[4 * it + 3];
   const int L = seq_lens[b];
   const int t_begin = p0 * kPage;
-  const int t_end = min(p1 * kPage, L);
+  const int t_end = min(p1 * kPage, L - q_len + tq + 1);
   const int n_slices = (t_end - t_begin + kSliceTok - 1) / kSliceTok;
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
+  const int64_t qrow0 = (static_cast<int64_t>(b) * q_len + tq) * H;
+  const int64_t prow0 = (static_cast<int64_t>(it) * q_len + tq) * H;
+  if (n_slices <= 0) {  // empty partial, as in the 128-head kernel
+    for (int i = threadIdx.x; i < H * kDc; i += blockDim.x) o_part[prow0 * kDc + i] = 0.f;
+    if (threadIdx.x < H) lse_part[prow0 + threadIdx.x] = -INFINITY;
+    return;
+  }
   constexpr uint32_t kTileRowGroup = 9 * 1024;
   constexpr uint32_t kRowGroup2 = 2 * kTileRowGroup;
   auto slot_of = [&](int n) -> const char* { return lds + (n % kStages) * kSlotBytes; };
@@ -594,7 +629,7 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
   // Q fragments (B operand of the scores): head q, values 32ks + 8g .. +8
   bf16x8 qf[18];
   {
-    const uint16_t* qrow = q_abs + (static_cast<int64_t>(b) * H + q) * kDq + 8 * g;
+    const uint16_t* qrow = q_abs + (qrow0 + q) * kDq + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
   }
@@ -753,12 +788,12 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     if (direct) {
       if (lse_out) lse_out[static_cast<int64_t>(b) * H + q] = lse_v;
     } else {
-      lse_part[static_cast<int64_t>(it) * H + q] = lse_v;
+      lse_part[prow0 + q] = lse_v;
     }
   }
   const float inv = 1.f / l;
   float* orow = (direct ? o_latent + static_cast<int64_t>(b) * H * kDc
-                        : o_part + static_cast<int64_t>(it) * H * kDc) + q * kDc + 128 * w + 4 * g;
+                        : o_part + prow0 * kDc) + q * kDc + 128 * w + 4 * g;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     oacc[c][0] *= inv;
@@ -824,22 +859,24 @@ float max_jump() {
 
 }  // namespace
 
-hipError_t decode_fast(const mla_dims& d, const void* q_abs, const void* kv_cache,
+hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const void* kv_cache,
                        const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                        const int32_t* items, int num_items, float* o_part, float* lse_part,
                        const int32_t* split_offsets, int32_t* tickets, float* o_latent,
                        float* lse_out, hipStream_t stream) {
+  const int64_t blocks = static_cast<int64_t>(num_items) * q_len * (d.n_heads == 128 ? 2 : 1);
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
   if (d.n_heads == 128) {
-    hipLaunchKernelGGL(decode_h128_kernel, dim3(2 * num_items), dim3(1024), 0, stream,
+    hipLaunchKernelGGL(decode_h128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(1024), 0, stream,
                        static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
-                       block_table, max_pages, seq_lens, items, num_items, d.softmax_scale,
+                       block_table, max_pages, seq_lens, items, num_items, q_len, d.softmax_scale,
                        max_jump(), o_part, lse_part, split_offsets, tickets, o_latent, lse_out);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(decode_h16_kernel, dim3(num_items), dim3(256), 0, stream,
+  hipLaunchKernelGGL(decode_h16_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
-                     block_table, max_pages, seq_lens, items, d.softmax_scale, max_jump(), o_part,
-                     lse_part, split_offsets, tickets, o_latent, lse_out);
+                     block_table, max_pages, seq_lens, items, num_items, q_len, d.softmax_scale,
+                     max_jump(), o_part, lse_part, split_offsets, tickets, o_latent, lse_out);
   return hipGetLastError();
 }
 

@@ -65,9 +65,10 @@ __global__ __launch_bounds__(kThreads) void absorb_generic_kernel(
   }
 }
 
-// One workgroup per (work item, head): 256 tokens at a time, online softmax.
+// One workgroup per (work item, query token, head): 256 tokens at a time,
+// online softmax.  Query token t of q_len sees cache rows [0, L - q_len + t].
 __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
-    int H, int dc, int dr, int P, float scale, bool bf, const void* __restrict__ q_abs,
+    int H, int dc, int dr, int P, int q_len, float scale, bool bf, const void* __restrict__ q_abs,
     const void* __restrict__ cache, const int32_t* __restrict__ block_table, int max_pages,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ items,
     float* __restrict__ o_part, float* __restrict__ lse_part) {
@@ -77,12 +78,18 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
   float* q = reinterpret_cast<float*>(rowoff + kThreads);        // [D]
   float* p = q + D;                                              // [256]
   float* red = p + kThreads;                                     // [8]
-  const int it = blockIdx.x, h = blockIdx.y;
+  const int it = blockIdx.x / q_len, tq = blockIdx.x % q_len, h = blockIdx.y;
   const int b = items[4 * it], p0 = items[4 * it + 2], p1 = items[4 * it + 3];
   const int L = seq_lens[b];
   const int t0 = p0 * P;
-  const int t1 = min(p1 * P, L);
-  const int64_t qrow = static_cast<int64_t>(b) * H + h;
+  const int t1 = min(p1 * P, L - q_len + tq + 1);
+  const int64_t qrow = (static_cast<int64_t>(b) * q_len + tq) * H + h;
+  const int64_t orow = (static_cast<int64_t>(it) * q_len + tq) * H + h;
+  if (t1 <= t0) {  // the whole range lies after this token: an empty partial
+    for (int c = threadIdx.x; c < dc; c += kThreads) o_part[orow * dc + c] = 0.f;
+    if (threadIdx.x == 0) lse_part[orow] = -INFINITY;
+    return;
+  }
   for (int k = threadIdx.x; k < D; k += kThreads) q[k] = load_elem(q_abs, qrow * D + k, bf);
   constexpr int kMaxPer = 1024 / kThreads;  // d_c <= 1024
   float o[kMaxPer];
@@ -119,7 +126,6 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
     }
     __syncthreads();
   }
-  const int64_t orow = static_cast<int64_t>(it) * H + h;
   const float inv = 1.f / l;
   for (int i = 0; i < kMaxPer; ++i) {
     const int c = threadIdx.x + i * kThreads;
@@ -130,23 +136,25 @@ __global__ __launch_bounds__(kThreads) void decode_generic_kernel(
 }
 
 __global__ __launch_bounds__(kThreads) void combine_generic_kernel(
-    int H, int dc, const int32_t* __restrict__ offs, const float* __restrict__ o_part,
+    int H, int dc, int q_len, const int32_t* __restrict__ offs, const float* __restrict__ o_part,
     const float* __restrict__ lse_part, float* __restrict__ o_latent, float* __restrict__ lse) {
-  const int b = blockIdx.x, h = blockIdx.y;
+  // row r = b * q_len + t (query token t of sequence b); its partial in item s
+  // is row s * q_len + t
+  const int r = blockIdx.x, h = blockIdx.y;
+  const int b = r / q_len, t = r % q_len;
   const int s0 = offs[b], s1 = offs[b + 1];
+  auto prow = [&](int s) { return (static_cast<int64_t>(s) * q_len + t) * H + h; };
   float M = -INFINITY;
-  for (int s = s0; s < s1; ++s) M = fmaxf(M, lse_part[static_cast<int64_t>(s) * H + h]);
+  for (int s = s0; s < s1; ++s) M = fmaxf(M, lse_part[prow(s)]);
   float Z = 0.f;
-  for (int s = s0; s < s1; ++s) Z += expf(lse_part[static_cast<int64_t>(s) * H + h] - M);
+  for (int s = s0; s < s1; ++s) Z += expf(lse_part[prow(s)] - M);
   const float inv = 1.f / Z;
   for (int c = threadIdx.x; c < dc; c += kThreads) {
     float acc = 0.f;
-    for (int s = s0; s < s1; ++s)
-      acc = fmaf(expf(lse_part[static_cast<int64_t>(s) * H + h] - M),
-                 o_part[(static_cast<int64_t>(s) * H + h) * dc + c], acc);
-    o_latent[(static_cast<int64_t>(b) * H + h) * dc + c] = acc * inv;
+    for (int s = s0; s < s1; ++s) acc = fmaf(expf(lse_part[prow(s)] - M), o_part[prow(s) * dc + c], acc);
+    o_latent[(static_cast<int64_t>(r) * H + h) * dc + c] = acc * inv;
   }
-  if (lse && threadIdx.x == 0) lse[static_cast<int64_t>(b) * H + h] = M + logf(Z);
+  if (lse && threadIdx.x == 0) lse[static_cast<int64_t>(r) * H + h] = M + logf(Z);
 }
 
 // out[b][h][d] = sum_c W^UV[h*dh + d][c] * o_latent[b][h][c]; one wave per output row.
@@ -180,23 +188,26 @@ hipError_t absorb_generic(const mla_dims& d, int batch, const void* q_nope, cons
   return hipGetLastError();
 }
 
-hipError_t decode_generic(const mla_dims& d, const void* q_abs, const void* kv_cache,
+hipError_t decode_generic(const mla_dims& d, int q_len, const void* q_abs, const void* kv_cache,
                           const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                           const int32_t* items, int num_items, float* o_part, float* lse_part,
                           hipStream_t stream) {
   const bool bf = d.dtype == MLA_BF16;
   const size_t sm = (d.d_latent + d.d_rope + kThreads + 8) * sizeof(float) + kThreads * sizeof(int64_t);
-  hipLaunchKernelGGL(decode_generic_kernel, dim3(num_items, d.n_heads), dim3(kThreads), sm, stream,
-                     d.n_heads, d.d_latent, d.d_rope, d.page_size, d.softmax_scale, bf, q_abs,
+  const int64_t blocks = static_cast<int64_t>(num_items) * q_len;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_generic_kernel, dim3(static_cast<uint32_t>(blocks), d.n_heads),
+                     dim3(kThreads), sm, stream, d.n_heads, d.d_latent, d.d_rope, d.page_size, q_len,
+                     d.softmax_scale, bf, q_abs,
                      kv_cache, block_table, max_pages, seq_lens, items, o_part, lse_part);
   return hipGetLastError();
 }
 
-hipError_t combine_generic(const mla_dims& d, int batch, const int32_t* split_offsets,
+hipError_t combine_generic(const mla_dims& d, int batch, int q_len, const int32_t* split_offsets,
                            const float* o_part, const float* lse_part, float* o_latent, float* lse,
                            hipStream_t stream) {
-  hipLaunchKernelGGL(combine_generic_kernel, dim3(batch, d.n_heads), dim3(kThreads), 0, stream,
-                     d.n_heads, d.d_latent, split_offsets, o_part, lse_part, o_latent, lse);
+  hipLaunchKernelGGL(combine_generic_kernel, dim3(batch * q_len, d.n_heads), dim3(kThreads), 0, stream,
+                     d.n_heads, d.d_latent, q_len, split_offsets, o_part, lse_part, o_latent, lse);
   return hipGetLastError();
 }
 

@@ -101,27 +101,76 @@ mla_status mla_plan_splits(const mla_dims* dims, int32_t batch, const int32_t* s
                      split_offsets_host, num_items, dims->n_heads);
 }
 
-mla_status mla_decode_splitkv(const mla_dims* dims, int32_t batch, const void* q_abs,
-                              const void* kv_cache, int32_t num_pages, const int32_t* block_table,
-                              int32_t max_pages_per_seq, const int32_t* seq_lens,
-                              const int32_t* items, int32_t num_items, float* o_part,
-                              float* lse_part, void* stream) {
+namespace {
+
+mla_status decode_splitkv_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_abs,
+                               const void* kv_cache, int32_t num_pages, const int32_t* block_table,
+                               int32_t max_pages_per_seq, const int32_t* seq_lens,
+                               const int32_t* items, int32_t num_items, float* o_part,
+                               float* lse_part, void* stream) {
   mla_status s = check_dims(dims);
   if (s != MLA_OK) return s;
-  if (batch < 1 || num_pages < 1 || max_pages_per_seq < 1 || num_items < 1) return MLA_ERR_INVALID_ARG;
+  if (batch < 1 || q_len < 1 || num_pages < 1 || max_pages_per_seq < 1 || num_items < 1)
+    return MLA_ERR_INVALID_ARG;
   if (!q_abs || !kv_cache || !block_table || !seq_lens || !items || !o_part || !lse_part)
     return MLA_ERR_INVALID_ARG;
   if (!al16(q_abs) || !al16(kv_cache) || !al16(o_part) || !al4(lse_part) || !al4(block_table) ||
       !al4(seq_lens) || !al4(items))
     return MLA_ERR_INVALID_ARG;
+  // partial rows and workgroup counts stay within 32-bit grid limits
+  if (static_cast<int64_t>(num_items) * q_len * 2 > INT32_MAX ||
+      static_cast<int64_t>(batch) * q_len * dims->n_heads > (int64_t{1} << 31))
+    return MLA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
   if (is_fast_shape(*dims))
-    return launched(decode_fast(*dims, q_abs, kv_cache, block_table, max_pages_per_seq, seq_lens,
-                                items, num_items, o_part, lse_part, nullptr, nullptr, nullptr,
-                                nullptr, st));
-  return launched(decode_generic(*dims, q_abs, kv_cache, block_table, max_pages_per_seq, seq_lens,
-                                 items, num_items, o_part, lse_part, st));
+    return launched(decode_fast(*dims, q_len, q_abs, kv_cache, block_table, max_pages_per_seq,
+                                seq_lens, items, num_items, o_part, lse_part, nullptr, nullptr,
+                                nullptr, nullptr, st));
+  return launched(decode_generic(*dims, q_len, q_abs, kv_cache, block_table, max_pages_per_seq,
+                                 seq_lens, items, num_items, o_part, lse_part, st));
+}
+
+mla_status combine_impl(const mla_dims* dims, int32_t batch, int32_t q_len,
+                        const int32_t* split_offsets, const float* o_part, const float* lse_part,
+                        float* o_latent, float* lse, void* stream) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  if (batch < 1 || q_len < 1 || !split_offsets || !o_part || !lse_part || !o_latent)
+    return MLA_ERR_INVALID_ARG;
+  if (!al16(o_part) || !al16(o_latent) || !al4(lse_part) || !al4(split_offsets) ||
+      (lse && !al4(lse)))
+    return MLA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(batch) * q_len * dims->n_heads > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+  if (is_fast_shape(*dims))
+    return launched(combine_fast(*dims, batch, q_len, split_offsets, o_part, lse_part, o_latent, lse,
+                                 st));
+  if (static_cast<int64_t>(batch) * q_len > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  return launched(combine_generic(*dims, batch, q_len, split_offsets, o_part, lse_part, o_latent,
+                                  lse, st));
+}
+
+}  // namespace
+
+mla_status mla_decode_splitkv(const mla_dims* dims, int32_t batch, const void* q_abs,
+                              const void* kv_cache, int32_t num_pages, const int32_t* block_table,
+                              int32_t max_pages_per_seq, const int32_t* seq_lens,
+                              const int32_t* items, int32_t num_items, float* o_part,
+                              float* lse_part, void* stream) {
+  return decode_splitkv_impl(dims, batch, 1, q_abs, kv_cache, num_pages, block_table,
+                             max_pages_per_seq, seq_lens, items, num_items, o_part, lse_part, stream);
+}
+
+mla_status mla_decode_splitkv_multi(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                    const void* q_abs, const void* kv_cache, int32_t num_pages,
+                                    const int32_t* block_table, int32_t max_pages_per_seq,
+                                    const int32_t* seq_lens, const int32_t* items,
+                                    int32_t num_items, float* o_part, float* lse_part,
+                                    void* stream) {
+  return decode_splitkv_impl(dims, batch, q_len, q_abs, kv_cache, num_pages, block_table,
+                             max_pages_per_seq, seq_lens, items, num_items, o_part, lse_part, stream);
 }
 
 mla_status mla_decode_merged(const mla_dims* dims, int32_t batch, const void* q_abs,
@@ -143,31 +192,26 @@ mla_status mla_decode_merged(const mla_dims* dims, int32_t batch, const void* q_
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
   if (is_fast_shape(*dims))
-    return launched(decode_fast(*dims, q_abs, kv_cache, block_table, max_pages_per_seq, seq_lens,
-                                items, num_items, o_part, lse_part, split_offsets, tickets,
-                                o_latent, lse, st));
-  if (batch > 65535) return MLA_ERR_UNSUPPORTED;
-  mla_status r = launched(decode_generic(*dims, q_abs, kv_cache, block_table, max_pages_per_seq,
+    return launched(decode_fast(*dims, 1, q_abs, kv_cache, block_table, max_pages_per_seq,
+                                seq_lens, items, num_items, o_part, lse_part, split_offsets,
+                                tickets, o_latent, lse, st));
+  mla_status r = launched(decode_generic(*dims, 1, q_abs, kv_cache, block_table, max_pages_per_seq,
                                          seq_lens, items, num_items, o_part, lse_part, st));
   if (r != MLA_OK) return r;
-  return launched(combine_generic(*dims, batch, split_offsets, o_part, lse_part, o_latent, lse, st));
+  return launched(combine_generic(*dims, batch, 1, split_offsets, o_part, lse_part, o_latent, lse,
+                                  st));
 }
 
 mla_status mla_combine(const mla_dims* dims, int32_t batch, const int32_t* split_offsets,
                        const float* o_part, const float* lse_part, float* o_latent, float* lse,
                        void* stream) {
-  mla_status s = check_dims(dims);
-  if (s != MLA_OK) return s;
-  if (batch < 1 || !split_offsets || !o_part || !lse_part || !o_latent) return MLA_ERR_INVALID_ARG;
-  if (!al16(o_part) || !al16(o_latent) || !al4(lse_part) || !al4(split_offsets) ||
-      (lse && !al4(lse)))
-    return MLA_ERR_INVALID_ARG;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
-  if (is_fast_shape(*dims))
-    return launched(combine_fast(*dims, batch, split_offsets, o_part, lse_part, o_latent, lse, st));
-  if (batch > 65535) return MLA_ERR_UNSUPPORTED;
-  return launched(combine_generic(*dims, batch, split_offsets, o_part, lse_part, o_latent, lse, st));
+  return combine_impl(dims, batch, 1, split_offsets, o_part, lse_part, o_latent, lse, stream);
+}
+
+mla_status mla_combine_multi(const mla_dims* dims, int32_t batch, int32_t q_len,
+                             const int32_t* split_offsets, const float* o_part,
+                             const float* lse_part, float* o_latent, float* lse, void* stream) {
+  return combine_impl(dims, batch, q_len, split_offsets, o_part, lse_part, o_latent, lse, stream);
 }
 
 int64_t mla_append_kv_workspace_bytes(const mla_dims* dims, int32_t d_model, int32_t batch) {

@@ -21,11 +21,11 @@ bool is_fast_shape(const mla_dims& d);
 hipError_t absorb_generic(const mla_dims& d, int batch, const void* q_nope, const void* q_pe,
                           const int32_t* positions, const void* w_uk, void* q_abs,
                           hipStream_t stream);
-hipError_t decode_generic(const mla_dims& d, const void* q_abs, const void* kv_cache,
+hipError_t decode_generic(const mla_dims& d, int q_len, const void* q_abs, const void* kv_cache,
                           const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                           const int32_t* items, int num_items, float* o_part, float* lse_part,
                           hipStream_t stream);
-hipError_t combine_generic(const mla_dims& d, int batch, const int32_t* split_offsets,
+hipError_t combine_generic(const mla_dims& d, int batch, int q_len, const int32_t* split_offsets,
                            const float* o_part, const float* lse_part, float* o_latent, float* lse,
                            hipStream_t stream);
 hipError_t out_proj_generic(const mla_dims& d, int batch, const float* o_latent, const void* w_uv,
@@ -35,13 +35,15 @@ hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const v
                        const int32_t* positions, const void* w_uk, void* q_abs,
                        hipStream_t stream);
 // With tickets == nullptr: partials only.  Otherwise also the merge of every
-// sequence's partials into o_latent / lse_out (split_offsets as for combine).
-hipError_t decode_fast(const mla_dims& d, const void* q_abs, const void* kv_cache,
+// sequence's partials into o_latent / lse_out (split_offsets as for combine;
+// q_len 1 only).  q_len query tokens per sequence: q_abs rows b * q_len + t,
+// partial rows item * q_len + t.
+hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const void* kv_cache,
                        const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                        const int32_t* items, int num_items, float* o_part, float* lse_part,
                        const int32_t* split_offsets, int32_t* tickets, float* o_latent,
                        float* lse_out, hipStream_t stream);
-hipError_t combine_fast(const mla_dims& d, int batch, const int32_t* split_offsets,
+hipError_t combine_fast(const mla_dims& d, int batch, int q_len, const int32_t* split_offsets,
                         const float* o_part, const float* lse_part, float* o_latent, float* lse,
                         hipStream_t stream);
 hipError_t out_proj_fast(const mla_dims& d, int batch, const float* o_latent, const void* w_uv,

@@ -236,6 +236,49 @@ def decode_workload(wl, seqs: Optional[Iterable[int]] = None, heads=None) -> Dic
     return {k: np.stack(v) for k, v in res.items()}
 
 
+def multi_decode_seq(c: np.ndarray, k_rope: np.ndarray, q_nope: np.ndarray, q_pe: np.ndarray,
+                     w_uk: np.ndarray, w_uv: np.ndarray, scale: float, rope_base: float,
+                     heads: Optional[Iterable[int]] = None) -> Dict[str, np.ndarray]:
+    """T query tokens of one sequence whose L cached rows already hold them.
+
+    Query t sits at position p_t = L - T + t and attends causally to tokens
+    0 .. p_t (the current token is cached before attention, [两张账] "第一张账";
+    a token never attends to later ones).  q_nope [T, n_h, d_h], q_pe
+    [T, n_h, d_h^R].  Each token is the single-query naive path over its prefix.
+    Returns arrays with a leading T axis.
+    """
+    L = c.shape[0]
+    T = q_nope.shape[0]
+    res = {k: [] for k in ("o", "o_latent", "lse", "q_abs")}
+    for t in range(T):
+        p = L - T + t
+        r = naive_decode_seq(c[:p + 1], k_rope[:p + 1], q_nope[t], q_pe[t], p, w_uk, w_uv, scale,
+                             rope_base, heads=heads)
+        for k in res:
+            res[k].append(r[k])
+    return {k: np.stack(v) for k, v in res.items()}
+
+
+def multi_decode_workload(wl, q_nope: np.ndarray, q_pe: np.ndarray,
+                          seqs: Optional[Iterable[int]] = None, heads=None) -> Dict[str, np.ndarray]:
+    """multi_decode_seq over the selected sequences of a workload; q_nope
+    [B, T, n_h, d_h] and q_pe [B, T, n_h, d_h^R] in the workload's storage type."""
+    cfg = wl.cfg
+    bf = cfg.dtype == "bf16"
+    seqs = range(cfg.batch) if seqs is None else list(seqs)
+    w_uk = to_f64(wl.w_uk, bf)
+    w_uv = to_f64(wl.w_uv, bf)
+    scale = softmax_scale(cfg.d_head, cfg.d_rope)
+    res = {k: [] for k in ("o", "o_latent", "lse", "q_abs")}
+    for b in seqs:
+        rows = to_f64(gather_rows(wl.cache, wl.block_table[b], int(wl.seq_lens[b]), cfg.page_size), bf)
+        r = multi_decode_seq(rows[:, :cfg.d_latent], rows[:, cfg.d_latent:], to_f64(q_nope[b], bf),
+                             to_f64(q_pe[b], bf), w_uk, w_uv, scale, cfg.rope_base, heads=heads)
+        for k in res:
+            res[k].append(r[k])
+    return {k: np.stack(v) for k, v in res.items()}
+
+
 # ----------------------------------------------------------------------------
 # deriving the cache and the query from hidden states (the full recipe)
 # ----------------------------------------------------------------------------

@@ -130,6 +130,15 @@ def query(cfg: MLAConfig, b: int) -> tuple[np.ndarray, np.ndarray]:
     return _store(cfg, qn), _store(cfg, qp)
 
 
+def query_multi(cfg: MLAConfig, b: int, q_len: int) -> tuple[np.ndarray, np.ndarray]:
+    """q^C [q_len, n_h, d_h] and q^R [q_len, n_h, d_h^R] (not yet encoded) of the
+    q_len newest tokens of sequence b, in the storage type; N(0, 1)."""
+    r = _rng(cfg, 5, b)
+    qn = r.standard_normal((q_len, cfg.n_heads, cfg.d_head), dtype=np.float32)
+    qp = r.standard_normal((q_len, cfg.n_heads, cfg.d_rope), dtype=np.float32)
+    return _store(cfg, qn), _store(cfg, qp)
+
+
 def token_chunk(cfg: MLAConfig, b: int, chunk: int, n: int) -> np.ndarray:
     """Rows [n, d_c + d_h^R] for tokens chunk*2048 .. chunk*2048 + n - 1 of sequence b."""
     r = _rng(cfg, 2, b, chunk)

@@ -30,7 +30,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"mla_absorb_q", "mla_plan_splits", "mla_decode_splitkv", "mla_combine",
-            "mla_decode_merged", "mla_append_kv", "mla_out_proj"} <= set(names)
+            "mla_decode_merged", "mla_append_kv", "mla_out_proj", "mla_decode_splitkv_multi",
+            "mla_combine_multi"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -95,6 +96,37 @@ def test_decode_rejects_bad_arguments(lib):
     args = list(good)
     args[8] = A + 4                                # o_part misaligned
     assert f(_d(), 2, *args) == INVALID
+
+
+def test_decode_multi_rejects_bad_arguments(lib):
+    f = lib.mla_decode_splitkv_multi
+    # q_abs kv_cache num_pages bt max_pages seq_lens items num_items o_part lse_part stream
+    good = [A, A, 10, A, 4, A, A, 3, A, A, None]
+    assert f(_d(), 0, 2, *good) == INVALID         # batch < 1
+    assert f(_d(), 2, 0, *good) == INVALID         # q_len < 1
+    assert f(_d(), 2, -3, *good) == INVALID
+    for i in (0, 1, 3, 5, 6, 8, 9):                # each pointer argument set to NULL
+        args = list(good)
+        args[i] = None
+        assert f(_d(), 2, 4, *args) == INVALID, i
+    for i, bad in ((2, 0), (4, 0), (7, 0)):        # num_pages, max_pages, num_items < 1
+        args = list(good)
+        args[i] = bad
+        assert f(_d(), 2, 4, *args) == INVALID, i
+    for i, bad in ((0, MIS), (1, MIS), (8, A + 4), (9, A + 2)):
+        args = list(good)                          # misaligned q_abs, cache, o_part, lse_part
+        args[i] = bad
+        assert f(_d(), 2, 4, *args) == INVALID, i
+    args = list(good)
+    args[7] = 2 ** 30                              # num_items * q_len * 2 beyond the grid
+    assert f(_d(), 2, 4, *args) == UNSUPPORTED
+    c = lib.mla_combine_multi
+    assert c(_d(), 0, 2, A, A, A, A, A, None) == INVALID
+    assert c(_d(), 2, 0, A, A, A, A, A, None) == INVALID
+    assert c(_d(), 2, 2, None, A, A, A, A, None) == INVALID
+    assert c(_d(), 2, 2, A, MIS, A, A, A, None) == INVALID
+    assert c(_d(), 2, 2, A, A, A, A, A + 2, None) == INVALID   # lse misaligned
+    assert c(_d(), 2 ** 20, 2 ** 10, A, A, A, A, None, None) == UNSUPPORTED
 
 
 def test_decode_merged_rejects_bad_arguments(lib):

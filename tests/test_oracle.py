@@ -365,6 +365,99 @@ def _lse_merge_unweighted(o_parts, lse_parts):
     return np.mean(o_parts, axis=0), np.max(lse_parts, axis=0)
 
 
+# ---------------------------------------------------------------------------
+# multi-token queries (several new tokens of a sequence decoded at once)
+# ---------------------------------------------------------------------------
+def _multi_case(T, lens=(37, 5)):
+    from synth import query_multi
+    cfg = small(TINY, "multi", len(lens))
+    wl = generate(cfg, lens=np.array(lens, np.int32))
+    qs = [query_multi(cfg, b, T) for b in range(cfg.batch)]
+    return wl, np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs])
+
+
+def check_multi_single_token():
+    """T = 1 is the single-query path at position L - 1."""
+    wl, qn, qp = _multi_case(1)
+    m = O.multi_decode_workload(wl, qn, qp)
+    wl.q_nope, wl.q_pe = qn[:, 0], qp[:, 0]
+    wl.positions = wl.seq_lens - 1
+    ref = O.decode_workload(wl)
+    for k in ("o", "o_latent", "lse", "q_abs"):
+        np.testing.assert_allclose(m[k][:, 0], ref[k], rtol=0, atol=0)
+
+
+def check_multi_causal():
+    """Token t never sees cached rows after its own position."""
+    T = 3
+    wl, qn, qp = _multi_case(T)
+    a = O.multi_decode_workload(wl, qn, qp)
+    L = int(wl.seq_lens[0])
+    for j in range(L - T + 1, L):          # rows after token 0's position (positions L-2, L-1)
+        page, slot = wl.block_table[0, j // 64], j % 64
+        wl.cache[page, slot] = (wl.cache[page, slot] * 3.0 + 1.0).astype(wl.cache.dtype)
+    b = O.multi_decode_workload(wl, qn, qp)
+    np.testing.assert_allclose(b["o"][0, 0], a["o"][0, 0], rtol=0, atol=0)
+    np.testing.assert_allclose(b["lse"][0, 0], a["lse"][0, 0], rtol=0, atol=0)
+    assert not np.allclose(b["o"][0, T - 1], a["o"][0, T - 1])
+
+
+def check_multi_last_token():
+    """The newest token attends to every cached row, like a single query."""
+    T = 4
+    wl, qn, qp = _multi_case(T)
+    m = O.multi_decode_workload(wl, qn, qp)
+    wl.q_nope, wl.q_pe = qn[:, T - 1], qp[:, T - 1]
+    wl.positions = wl.seq_lens - 1
+    ref = O.decode_workload(wl)
+    np.testing.assert_allclose(m["o"][:, T - 1], ref["o"], rtol=0, atol=0)
+
+
+def test_multi_single_token():
+    check_multi_single_token()
+
+
+def test_multi_causal():
+    check_multi_causal()
+
+
+def test_multi_last_token():
+    check_multi_last_token()
+
+
+def _multi_not_causal(c, k_rope, q_nope, q_pe, w_uk, w_uv, scale, rope_base, heads=None):
+    T = q_nope.shape[0]
+    res = {k: [] for k in ("o", "o_latent", "lse", "q_abs")}
+    for t in range(T):
+        r = O.naive_decode_seq(c, k_rope, q_nope[t], q_pe[t], c.shape[0] - T + t, w_uk, w_uv, scale,
+                               rope_base, heads=heads)
+        for k in res:
+            res[k].append(r[k])
+    return {k: np.stack(v) for k, v in res.items()}
+
+
+def _multi_wrong_position(c, k_rope, q_nope, q_pe, w_uk, w_uv, scale, rope_base, heads=None):
+    T = q_nope.shape[0]
+    res = {k: [] for k in ("o", "o_latent", "lse", "q_abs")}
+    for t in range(T):
+        p = c.shape[0] - 1
+        r = O.naive_decode_seq(c[:p + 1], k_rope[:p + 1], q_nope[t], q_pe[t], p, w_uk, w_uv, scale,
+                               rope_base, heads=heads)
+        for k in res:
+            res[k].append(r[k])
+    return {k: np.stack(v) for k, v in res.items()}
+
+
+@pytest.mark.parametrize("target,replacement,check", [
+    ("multi_decode_seq", _multi_not_causal, check_multi_causal),
+    ("multi_decode_seq", _multi_wrong_position, check_multi_causal),
+])
+def test_planted_multi_mistake_is_caught(monkeypatch, target, replacement, check):
+    monkeypatch.setattr(O, target, replacement)
+    with pytest.raises(AssertionError):
+        check()
+
+
 @pytest.mark.parametrize("target,replacement,check", [
     ("rope", _wrong_sign_rope, check_rope_planar),
     ("rope_theta", _half_split_theta, check_rope_pairing),
