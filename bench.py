@@ -1,15 +1,17 @@
 """Benchmark of one MLA decode step on one MI355X.
 
 A step is one pass of the whole path over a batch: mla_absorb_q ->
-mla_decode_splitkv -> mla_combine -> mla_out_proj, on synthetic inputs already
-resident in HBM (the split plan is made once per batch shape, before timing).
-With --merged the decode and the merge run as one launch, mla_decode_merged.
-With --q-len T every sequence decodes its T newest tokens at once (causal among
-them): absorb and out_proj on B*T rows, mla_decode_splitkv_multi and
-mla_combine_multi in between.
+mla_decode_splitkv -> mla_combine_out_proj (the log-sum-exp merge and the W^UV
+product in one launch), on synthetic inputs already resident in HBM (the split
+plan is made once per batch shape, before timing).  --unfused runs
+mla_combine and mla_out_proj as two launches instead; --merged fuses the merge
+into the decode (mla_decode_merged) and runs mla_out_proj after it.  With
+--q-len T every sequence decodes its T newest tokens at once (causal among
+them): absorb on B*T rows, mla_decode_splitkv_multi, then the merge and W^UV
+on B*T rows.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--merged]
-                    [--q-len T] [--no-flush] [--no-cpu-baseline] [--copy-probe]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--merged | --unfused]
+                    [--q-len T] [--slots N] [--no-flush] [--no-cpu-baseline] [--copy-probe]
 
 Prints ONE JSON line on stdout; progress goes to stderr.  The step time comes
 from HIP events at the step boundaries; a second pass over the same steps with
@@ -118,8 +120,12 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--merged", action="store_true",
                     help="decode and merge in one launch (mla_decode_merged)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="merge and W^UV product as two launches (mla_combine, mla_out_proj)")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per sequence (multi-token decode)")
+    ap.add_argument("--slots", type=int, default=0,
+                    help="workgroup slots the split plan aims at (default: the CU count)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -129,8 +135,9 @@ def main():
               "(the path does not shard across GPUs in this build)", file=sys.stderr)
         sys.exit(2)
     T = args.q_len
-    if T < 1 or (T > 1 and args.merged):
-        print("--q-len must be >= 1, and 1 with --merged", file=sys.stderr)
+    if T < 1 or (T > 1 and args.merged) or (args.merged and args.unfused):
+        print("--q-len must be >= 1, and 1 with --merged; --merged and --unfused exclude "
+              "each other", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -167,11 +174,12 @@ def main():
     dims = mla.Dims(cfg.n_heads, cfg.d_head, cfg.d_latent, cfg.d_rope, cfg.page_size,
                     rope_base=cfg.rope_base, dtype=mla.BF16 if bf else mla.F32)
     props = torch.cuda.get_device_properties(0)
-    slots = int(props.multi_processor_count)
+    slots = args.slots or int(props.multi_processor_count)
     # each item is decoded once per query token: plan for the CUs over T
     items_h, offs_h = mla.plan_splits(dims, wl.seq_lens, max(1, slots // T))
     items, offs = torch.from_numpy(items_h).cuda(), torch.from_numpy(offs_h).cuda()
-    log(f"[bench] {props.name} {getattr(props, 'gcnArchName', '')}, {slots} CUs; "
+    log(f"[bench] {props.name} {getattr(props, 'gcnArchName', '')}, {props.multi_processor_count} CUs, "
+        f"plan for {slots} slots; "
         f"{len(items_h)} work items, q_len {T}")
 
     W = len(items_h)
@@ -197,18 +205,38 @@ def main():
         if flush is not None:
             torch.sum(flush, dim=0, keepdim=True, out=sink)
 
-    if T > 1:
+    absorb = lambda: mla.absorb_q(dims, q_nope, q_pe, positions, w_uk, bufs["q_abs"], stream)  # noqa: E731
+    q4 = bufs["q_abs"].view(B, T, H, dims.row)
+    ol4 = bufs["o_latent"].view(B, T, H, cfg.d_latent)
+    lse3 = bufs["lse"].view(B, T, H)
+    out4 = bufs["out"].view(B, T, H, cfg.d_head)
+    if T > 1 and args.unfused:
         names = ["absorb_q", "decode_splitkv_multi", "combine_multi", "out_proj"]
-        q4 = bufs["q_abs"].view(B, T, H, dims.row)
-        ol4 = bufs["o_latent"].view(B, T, H, cfg.d_latent)
-        lse3 = bufs["lse"].view(B, T, H)
         launches = [
-            lambda: mla.absorb_q(dims, q_nope, q_pe, positions, w_uk, bufs["q_abs"], stream),
+            absorb,
             lambda: mla.decode_splitkv_multi(dims, q4, cache, block_table, seq_lens, items,
                                              bufs["o_part"], bufs["lse_part"], stream),
             lambda: mla.combine_multi(dims, offs, bufs["o_part"], bufs["lse_part"], B, ol4, lse3,
                                       stream),
             lambda: mla.out_proj(dims, bufs["o_latent"], w_uv, bufs["out"], stream),
+        ]
+    elif T > 1:
+        names = ["absorb_q", "decode_splitkv_multi", "combine_out_proj"]
+        launches = [
+            absorb,
+            lambda: mla.decode_splitkv_multi(dims, q4, cache, block_table, seq_lens, items,
+                                             bufs["o_part"], bufs["lse_part"], stream),
+            lambda: mla.combine_out_proj(dims, offs, bufs["o_part"], bufs["lse_part"], w_uv, B,
+                                         out4, stream=stream),
+        ]
+    elif not args.merged and not args.unfused:
+        names = ["absorb_q", "decode_splitkv", "combine_out_proj"]
+        launches = [
+            absorb,
+            lambda: mla.decode_splitkv(dims, bufs["q_abs"], cache, block_table, seq_lens, items,
+                                       bufs["o_part"], bufs["lse_part"], stream),
+            lambda: mla.combine_out_proj(dims, offs, bufs["o_part"], bufs["lse_part"], w_uv, B,
+                                         bufs["out"], stream=stream),
         ]
     elif not args.merged:
         names = ["absorb_q", "decode_splitkv", "combine", "out_proj"]

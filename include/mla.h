@@ -16,6 +16,7 @@
  *                       the same for q_len query tokens per sequence (causal)
  *   mla_append_kv       write the decoded token's [c^KV | RoPE(k^R)] row into the cache
  *   mla_out_proj        o_i = W^UV_i o~_i                                    (per head i)
+ *   mla_combine_out_proj  mla_combine and mla_out_proj in one launch
  *
  * Pages describing the method (titles as published):
  *   "DeepSeek V2 技术解析：多头潜在注意力（MLA）与混合专家模型（MoE）的创新实践",
@@ -229,6 +230,25 @@ mla_status mla_decode_merged(const mla_dims* dims, int32_t batch, const void* q_
  * Errors: MLA_ERR_INVALID_ARG for null pointers, batch < 1 or misalignment. */
 mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const float* o_latent,
                         const void* w_uv, float* out, void* stream);
+
+/* mla_combine_multi followed by mla_out_proj on the batch * q_len rows, in one
+ * launch on the gfx950 fast path: each workgroup merges the partials of its rows
+ * (the combine's arithmetic and order, so o_latent is bit-identical to
+ * mla_combine's) and feeds the merged rows to the W^UV product without writing
+ * them out first.  Cites as mla_combine and mla_out_proj.
+ *   split_offsets, o_part, lse_part  as for mla_combine_multi (q_len = 1: as for
+ *             mla_combine)
+ *   out       float32 [batch][q_len][n_heads][d_head]
+ *   o_latent  float32 [batch][q_len][n_heads][d_latent] or NULL on the fast path;
+ *             on other shapes it is required (the two kernels run with it between them)
+ *   lse       float32 [batch][q_len][n_heads] or NULL
+ * Errors: MLA_ERR_INVALID_ARG for null required pointers, batch or q_len < 1 or
+ * misalignment; MLA_ERR_UNSUPPORTED for sizes out of range or a NULL o_latent
+ * on a shape off the fast path. */
+mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                const int32_t* split_offsets, const float* o_part,
+                                const float* lse_part, const void* w_uv, float* out,
+                                float* o_latent, float* lse, void* stream);
 
 /* Write the token being decoded into the paged latent cache, one per sequence.
  * Page "DeepSeek V2 技术解析" 2.2.1.1 (only c^KV = W^DKV h_t is kept for the keys

@@ -7,7 +7,7 @@ been built -- there is no fallback.
 
 Entry points mirror include/mla.h:
     absorb_q, plan_splits, decode_splitkv, combine, decode_merged, out_proj, append_kv,
-    decode_splitkv_multi, combine_multi
+    decode_splitkv_multi, combine_multi, combine_out_proj
 plus `decode_step`, which runs the four device steps in order.
 """
 from __future__ import annotations
@@ -20,7 +20,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = ["MlaError", "Dims", "load", "lib_path", "absorb_q", "plan_splits", "decode_splitkv",
-           "decode_merged", "append_kv", "decode_splitkv_multi", "combine_multi",
+           "decode_merged", "append_kv", "decode_splitkv_multi", "combine_multi", "combine_out_proj",
            "combine", "out_proj", "decode_step", "fast_path", "version", "BF16", "F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -100,6 +100,7 @@ def load():
         "mla_decode_merged": (i32, [pd, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp, vp, vp,
                                      vp, vp]),
         "mla_out_proj": (i32, [pd, i32, vp, vp, vp, vp]),
+        "mla_combine_out_proj": (i32, [pd, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
         "mla_append_kv": (i32, [pd, i32, i32, vp, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, i32,
                                  vp, ctypes.c_int64, vp]),
         "mla_append_kv_workspace_bytes": (ctypes.c_int64, [pd, i32, i32]),
@@ -361,6 +362,35 @@ def out_proj(dims: Dims, o_latent, w_uv, out=None, stream=None):
         ctypes.byref(dims.c()), B, _ptr(o_latent, torch.float32, (B, H, dims.d_latent), "o_latent"),
         _ptr(w_uv, dt, (H * dims.d_head, dims.d_latent), "w_uv"),
         _ptr(out, torch.float32, (B, H, dims.d_head), "out"), _stream(stream)), "mla_out_proj")
+    return out
+
+
+def combine_out_proj(dims: Dims, split_offsets, o_part, lse_part, w_uv, batch: int, out=None,
+                     o_latent=None, lse=None, stream=None):
+    """combine (or combine_multi) and out_proj in one launch.
+
+    o_part [W, H, d_c] (one query token) or [W, T, H, d_c]; returns out
+    [B, H, d_h] or [B, T, H, d_h].  o_latent and lse are written only when
+    given (on shapes off the fast path o_latent is required).
+    """
+    torch = _torch()
+    H = dims.n_heads
+    dt = _store_dtype(dims)
+    multi = o_part.dim() == 4
+    W = o_part.shape[0]
+    T = o_part.shape[1] if multi else 1
+    lead = (batch, T) if multi else (batch,)
+    if out is None:
+        out = torch.empty((*lead, H, dims.d_head), dtype=torch.float32, device=o_part.device)
+    _check(load().mla_combine_out_proj(
+        ctypes.byref(dims.c()), batch, T,
+        _ptr(split_offsets, torch.int32, (batch + 1,), "split_offsets"),
+        _ptr(o_part, torch.float32, (W, *lead[1:], H, dims.d_latent), "o_part"),
+        _ptr(lse_part, torch.float32, (W, *lead[1:], H), "lse_part"),
+        _ptr(w_uv, dt, (H * dims.d_head, dims.d_latent), "w_uv"),
+        _ptr(out, torch.float32, (*lead, H, dims.d_head), "out"),
+        _ptr(o_latent, torch.float32, (*lead, H, dims.d_latent), "o_latent"),
+        _ptr(lse, torch.float32, (*lead, H), "lse"), _stream(stream)), "mla_combine_out_proj")
     return out
 
 

@@ -114,8 +114,11 @@ __device__ __forceinline__ float rows_sum(float x) {
 // 16 bytes per lane from `base + voff` into LDS at m0 + 16 * lane.  (The
 // instruction's immediate offset is left at 0: it would move the LDS
 // destination as well.)
+#ifndef MLA_DMA_POLICY
+#define MLA_DMA_POLICY ""
+#endif
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr)
+  asm volatile("global_load_lds_dwordx4 %0, %1" MLA_DMA_POLICY ::"v"(voff), "s"(base), "{m0}"(lds_addr)
                : "memory");
 }
 

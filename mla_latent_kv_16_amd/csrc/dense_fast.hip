@@ -138,77 +138,152 @@ __global__ __launch_bounds__(256) void absorb_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// out_proj: o^T[64 x b] = W^UV_h[64 rows x 512] . o~^T[512 x b], one workgroup
-// per (head, half of the 128 output rows, 64 sequences); the two halves of a
-// head run on one XCD and share its o~ through the L2.  The float32 o~ of the
-// 64 sequences is staged once in LDS as bf16 hi + lo (lo = bf16(x - hi)),
-// rows of 1 KiB with 16-byte chunk c at position c ^ 2 (b % 8): the B-operand
-// reads (16 sequences x one chunk per quarter-wave) then hit distinct bank
-// groups.  Wave w owns output rows 16w .. 16w+15 of the half for all 64
-// sequences (four accumulators), W^UV rows straight from global memory.
+// out_proj: o^T[128 x r] = W^UV_h[128 x 512] . o~^T[512 x r], one workgroup of
+// eight waves per (head, 32 query rows).  Blocks (h, group) and (h, group')
+// run on one XCD (grid x = heads, a multiple of 8), so W^UV_h comes from HBM
+// once and from that XCD's L2 for the other groups.  The float32 o~ of the
+// 32 rows is staged once in LDS as bf16 hi + lo (lo = bf16(x - hi)), rows of
+// 1 KiB with 16-byte chunk c at position c ^ 2 (r % 8): the B-operand reads
+// (16 rows x one chunk per quarter-wave) then hit distinct bank groups.  Wave
+// w owns output rows 16w .. 16w+15 for all 32 rows (two accumulators), its
+// W^UV rows read straight from global memory.
+//
+// With kMerge the workgroup first merges the split-KV partials of its rows
+// (the log-sum-exp combine, same arithmetic and order as combine_512_kernel,
+// so o~ is bit-identical) and stages the merged o~ instead of reading it; it
+// also writes o~ and lse when those pointers are set.  Rows are query rows
+// r = b * q_len + t; item s holds row r's partial at s * q_len + t.
 // ---------------------------------------------------------------------------
-constexpr int kOutSeq = 64;
-constexpr int kOutHalfBytes = kOutSeq * kDc * 2;  // one bf16 copy of the staged o~
+constexpr int kOutRows = 32;
+constexpr int kOutHalfBytes = kOutRows * kDc * 2;  // one bf16 copy of the staged o~
+constexpr int kOutThreads = 512;
+constexpr int kOutF4 = kOutRows * (kDc / 4) / kOutThreads;  // float4 per thread: 8
 
-__global__ __launch_bounds__(256) void out_proj_kernel(int batch, int H,
-                                                       const float* __restrict__ o_lat,
-                                                       const uint16_t* __restrict__ w_uv,
-                                                       float* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * kOutHalfBytes];  // [hi | lo][b][512]
-  int h, half;
-  xcd_split(blockIdx.x, 2, h, half);
+template <bool kMerge>
+__global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, int q_len,
+                                                               const int32_t* __restrict__ offs,
+                                                               const float* __restrict__ o_part,
+                                                               const float* __restrict__ lse_part,
+                                                               float* __restrict__ o_lat,
+                                                               float* __restrict__ lse_out,
+                                                               const uint16_t* __restrict__ w_uv,
+                                                               float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kOutHalfBytes];  // [hi | lo][r][512]
+  const int h = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, q = lane & 15;
-  const int b0 = blockIdx.y * kOutSeq;
-  const int nb = min(kOutSeq, batch - b0);
+  const int r0 = blockIdx.y * kOutRows;
+  const int nr = min(kOutRows, rows - r0);
 
-  // A operand: W^UV row 64 half + 16w + q, values 32ks + 8g .. +8
-  const int drow = 64 * half + 16 * w + q;
-  const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * kDh + drow) * kDc + 8 * g;
+  // A operand: W^UV row 16w + q, values 32ks + 8g .. +8
+  const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * kDh + 16 * w + q) * kDc + 8 * g;
   bf16x8 a[16];
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(wrow + 32 * ks);
 
-  // stage o~: float4 f = t + 256 i covers sequence f / 128, values 4 (f % 128) .. +4
+  // thread t stages float4 column 4 (t % 128) of rows t / 128 + 4 i, i < 8
+  const int c4 = 4 * (threadIdx.x & 127);
+  const int rl0 = threadIdx.x >> 7;
+  float4_t v[kOutF4];
+  if constexpr (kMerge) {
+    // Row rl = rl0 + 4i has items s0[i] .. s1[i].  The partials of its first
+    // two items are loaded before anything waits (16 loads in flight per
+    // thread); later items, if any, are loaded one at a time.  M, Z and the
+    // weighted sum follow the combine's arithmetic in item order, so every
+    // thread of a row computes the same M and Z.
+    constexpr int kPre = 2;
+    int s0[kOutF4], ns[kOutF4], tq[kOutF4];
+    float4_t x[kPre][kOutF4];
+    float lv[kPre][kOutF4];
 #pragma unroll
-  for (int i0 = 0; i0 < 32; i0 += 8) {
-    float4_t v[8];
+    for (int i = 0; i < kOutF4; ++i) {
+      const int rl = rl0 + 4 * i;
+      const int r = r0 + min(rl, nr - 1);
+      const int b = r / q_len;
+      tq[i] = r % q_len;
+      s0[i] = offs[b];
+      ns[i] = rl < nr ? offs[b + 1] - s0[i] : 0;
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int f = threadIdx.x + 256 * (i0 + i);
-      const int bl = f >> 7;
-      v[i] = bl < nb ? *reinterpret_cast<const float4_t*>(
-                           o_lat + (static_cast<int64_t>(b0 + bl) * H + h) * kDc + 4 * (f & 127))
+    for (int k = 0; k < kPre; ++k) {
+#pragma unroll
+      for (int i = 0; i < kOutF4; ++i) {
+        const bool ok = k < ns[i];
+        const int64_t pr = (static_cast<int64_t>(s0[i] + k) * q_len + tq[i]) * H + h;
+        x[k][i] = ok ? *reinterpret_cast<const float4_t*>(o_part + pr * kDc + c4) : float4_t{0.f, 0.f, 0.f, 0.f};
+        lv[k][i] = ok ? lse_part[pr] : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kOutF4; ++i) {
+      const int rl = rl0 + 4 * i;
+      auto lse_of = [&](int k) -> float {
+        return k < kPre ? lv[k < kPre ? k : 0][i]
+                        : lse_part[(static_cast<int64_t>(s0[i] + k) * q_len + tq[i]) * H + h];
+      };
+      float M = -INFINITY;
+      for (int k = 0; k < ns[i]; ++k) M = fmaxf(M, lse_of(k));
+      float Z = 0.f;
+      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < ns[i]; ++k) {
+        const float wgt = expf(lse_of(k) - M);
+        Z += wgt;
+        const float4_t xv =
+            k < kPre ? x[k < kPre ? k : 0][i]
+                     : *reinterpret_cast<const float4_t*>(
+                           o_part + ((static_cast<int64_t>(s0[i] + k) * q_len + tq[i]) * H + h) * kDc + c4);
+        acc[0] = fmaf(wgt, xv[0], acc[0]);
+        acc[1] = fmaf(wgt, xv[1], acc[1]);
+        acc[2] = fmaf(wgt, xv[2], acc[2]);
+        acc[3] = fmaf(wgt, xv[3], acc[3]);
+      }
+      v[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+      if (rl < nr) {
+        const float inv = 1.f / Z;
+        acc[0] *= inv;
+        acc[1] *= inv;
+        acc[2] *= inv;
+        acc[3] *= inv;
+        v[i] = acc;
+        const int64_t ro = static_cast<int64_t>(r0 + rl) * H + h;
+        if (o_lat) *reinterpret_cast<float4_t*>(o_lat + ro * kDc + c4) = acc;
+        if (lse_out && c4 == 0) lse_out[ro] = M + logf(Z);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kOutF4; ++i) {
+      const int rl = rl0 + 4 * i;
+      v[i] = rl < nr ? *reinterpret_cast<const float4_t*>(o_lat + (static_cast<int64_t>(r0 + rl) * H + h) * kDc + c4)
                      : float4_t{0.f, 0.f, 0.f, 0.f};
     }
+  }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int f = threadIdx.x + 256 * (i0 + i);
-      const int bl = f >> 7, c = 4 * (f & 127);
-      const uint32_t off = bl * (kDc * 2) + 16 * ((c >> 3) ^ (2 * (bl & 7))) + 2 * (c & 7);
-      uint32_t hi[2], lo[2];
+  for (int i = 0; i < kOutF4; ++i) {
+    const int rl = rl0 + 4 * i;
+    const uint32_t off = rl * (kDc * 2) + 16 * ((c4 >> 3) ^ (2 * (rl & 7))) + 2 * (c4 & 7);
+    uint32_t hi[2], lo[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        hi[j] = pack_bf16x2(v[i][2 * j], v[i][2 * j + 1]);
-        lo[j] = pack_bf16x2(v[i][2 * j] - __uint_as_float(hi[j] << 16),
-                            v[i][2 * j + 1] - __uint_as_float(hi[j] & 0xffff0000u));
-      }
-      *reinterpret_cast<uint64_t*>(lds + off) = (static_cast<uint64_t>(hi[1]) << 32) | hi[0];
-      *reinterpret_cast<uint64_t*>(lds + kOutHalfBytes + off) = (static_cast<uint64_t>(lo[1]) << 32) | lo[0];
+    for (int j = 0; j < 2; ++j) {
+      hi[j] = pack_bf16x2(v[i][2 * j], v[i][2 * j + 1]);
+      lo[j] = pack_bf16x2(v[i][2 * j] - __uint_as_float(hi[j] << 16),
+                          v[i][2 * j + 1] - __uint_as_float(hi[j] & 0xffff0000u));
     }
+    *reinterpret_cast<uint64_t*>(lds + off) = (static_cast<uint64_t>(hi[1]) << 32) | hi[0];
+    *reinterpret_cast<uint64_t*>(lds + kOutHalfBytes + off) = (static_cast<uint64_t>(lo[1]) << 32) | lo[0];
   }
   __syncthreads();
 
-  // B operand: sequence 16bb + q, values 32ks + 8g .. +8 (chunk 4ks + g)
-  float4_t acc[4] = {};
+  // B operand: row 16bb + q, values 32ks + 8g .. +8 (chunk 4ks + g)
+  float4_t acc[2] = {};
   const uint32_t brow = q * (kDc * 2);
   const int bsw = 2 * (q & 7);
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
     const uint32_t col = 16 * ((4 * ks + g) ^ bsw);
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
+    for (int bb = 0; bb < 2; ++bb) {
       const uint32_t off = bb * 16 * (kDc * 2) + brow + col;
       const bf16x8 bh = *reinterpret_cast<const bf16x8*>(lds + off);
       const bf16x8 bl = *reinterpret_cast<const bf16x8*>(lds + kOutHalfBytes + off);
@@ -216,13 +291,12 @@ __global__ __launch_bounds__(256) void out_proj_kernel(int batch, int H,
       acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], bl, acc[bb], 0, 0, 0);
     }
   }
-  // lane holds o[b0 + 16bb + q][h][64 half + 16w + 4g + i]
+  // lane holds o[r0 + 16bb + q][h][16w + 4g + i]
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) {
-    const int bl = 16 * bb + q;
-    if (bl < nb)
-      *reinterpret_cast<float4_t*>(out + (static_cast<int64_t>(b0 + bl) * H + h) * kDh + 64 * half +
-                                   16 * w + 4 * g) = acc[bb];
+  for (int bb = 0; bb < 2; ++bb) {
+    const int rl = 16 * bb + q;
+    if (rl < nr)
+      *reinterpret_cast<float4_t*>(out + (static_cast<int64_t>(r0 + rl) * H + h) * kDh + 16 * w + 4 * g) = acc[bb];
   }
 }
 
@@ -242,10 +316,23 @@ hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const v
 
 hipError_t out_proj_fast(const mla_dims& d, int batch, const float* o_latent, const void* w_uv,
                          float* out, hipStream_t stream) {
-  const int groups = (batch + 63) / 64;
+  const int groups = (batch + kOutRows - 1) / kOutRows;
   if (groups > 65535 || d.n_heads % 8 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(out_proj_kernel, dim3(d.n_heads * 2, groups), dim3(256), 0, stream, batch,
-                     d.n_heads, o_latent, static_cast<const uint16_t*>(w_uv), out);
+  hipLaunchKernelGGL(out_proj_kernel<false>, dim3(d.n_heads, groups), dim3(kOutThreads), 0, stream, batch,
+                     d.n_heads, 1, nullptr, nullptr, nullptr, const_cast<float*>(o_latent), nullptr,
+                     static_cast<const uint16_t*>(w_uv), out);
+  return hipGetLastError();
+}
+
+hipError_t combine_out_proj_fast(const mla_dims& d, int batch, int q_len, const int32_t* split_offsets,
+                                 const float* o_part, const float* lse_part, const void* w_uv,
+                                 float* out, float* o_latent, float* lse, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(batch) * q_len;
+  const int64_t groups = (rows + kOutRows - 1) / kOutRows;
+  if (groups > 65535 || d.n_heads % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(out_proj_kernel<true>, dim3(d.n_heads, static_cast<uint32_t>(groups)), dim3(kOutThreads),
+                     0, stream, static_cast<int>(rows), d.n_heads, q_len, split_offsets, o_part, lse_part,
+                     o_latent, lse, static_cast<const uint16_t*>(w_uv), out);
   return hipGetLastError();
 }
 

@@ -257,4 +257,34 @@ mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const float* o_late
   return launched(out_proj_generic(*dims, batch, o_latent, w_uv, out, st));
 }
 
+mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t q_len,
+                                const int32_t* split_offsets, const float* o_part,
+                                const float* lse_part, const void* w_uv, float* out,
+                                float* o_latent, float* lse, void* stream) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  if (batch < 1 || q_len < 1 || !split_offsets || !o_part || !lse_part || !w_uv || !out)
+    return MLA_ERR_INVALID_ARG;
+  if (!al16(o_part) || !al4(lse_part) || !al4(split_offsets) || !al16(w_uv) || !al16(out) ||
+      (o_latent && !al16(o_latent)) || (lse && !al4(lse)))
+    return MLA_ERR_INVALID_ARG;
+  const int64_t rows = static_cast<int64_t>(batch) * q_len;
+  if (rows * dims->n_heads > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (is_fast_shape(*dims)) {
+    if ((rows + 63) / 64 > 65535) return MLA_ERR_UNSUPPORTED;
+    (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+    return launched(combine_out_proj_fast(*dims, batch, q_len, split_offsets, o_part, lse_part, w_uv,
+                                          out, o_latent, lse, st));
+  }
+  // other shapes: the two kernels, with o_latent as the buffer between them
+  if (!o_latent) return MLA_ERR_UNSUPPORTED;
+  if (rows > 65535) return MLA_ERR_UNSUPPORTED;
+  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+  mla_status r = launched(combine_generic(*dims, batch, q_len, split_offsets, o_part, lse_part,
+                                          o_latent, lse, st));
+  if (r != MLA_OK) return r;
+  return launched(out_proj_generic(*dims, static_cast<int>(rows), o_latent, w_uv, out, st));
+}
+
 }  // extern "C"

@@ -48,6 +48,11 @@ hipError_t combine_fast(const mla_dims& d, int batch, int q_len, const int32_t* 
                         hipStream_t stream);
 hipError_t out_proj_fast(const mla_dims& d, int batch, const float* o_latent, const void* w_uv,
                          float* out, hipStream_t stream);
+// combine + out_proj in one launch (the merged o~ staged in LDS, never read
+// back); o_latent and lse are written when not null.
+hipError_t combine_out_proj_fast(const mla_dims& d, int batch, int q_len, const int32_t* split_offsets,
+                                 const float* o_part, const float* lse_part, const void* w_uv,
+                                 float* out, float* o_latent, float* lse, hipStream_t stream);
 
 // Cache write of one token per sequence (append.hip); `ws` holds
 // append_slices(d_model) x batch x (d_latent + d_rope) floats.

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"mla_absorb_q", "mla_plan_splits", "mla_decode_splitkv", "mla_combine",
             "mla_decode_merged", "mla_append_kv", "mla_out_proj", "mla_decode_splitkv_multi",
-            "mla_combine_multi"} <= set(names)
+            "mla_combine_multi", "mla_combine_out_proj"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -183,6 +183,25 @@ def test_combine_and_out_proj_reject_bad_arguments(lib):
     assert lib.mla_out_proj(_d(), 0, A, A, A, None) == INVALID
     assert lib.mla_out_proj(_d(), 2, A, None, A, None) == INVALID
     assert lib.mla_out_proj(_d(), 2, A, A, MIS, None) == INVALID
+
+
+def test_combine_out_proj_rejects_bad_arguments(lib):
+    f = lib.mla_combine_out_proj
+    # offs o_part lse_part w_uv out o_latent lse stream
+    good = [A, A, A, A, A, None, None, None]
+    assert f(_d(), 0, 1, *good) == INVALID
+    assert f(_d(), 2, 0, *good) == INVALID
+    for i in range(5):                             # each required pointer set to NULL
+        args = list(good)
+        args[i] = None
+        assert f(_d(), 2, 1, *args) == INVALID, i
+    for i, bad in ((0, A + 2), (1, MIS), (2, A + 2), (3, MIS), (4, MIS), (5, MIS), (6, A + 2)):
+        args = list(good)                          # misaligned
+        args[i] = bad
+        assert f(_d(), 2, 1, *args) == INVALID, i
+    assert f(_d(), 2 ** 20, 2 ** 10, *good) == UNSUPPORTED
+    # off the fast path the two kernels need o_latent between them
+    assert f(_d(mla.Dims(64, 128, 512, 64)), 2, 1, *good) == UNSUPPORTED
 
 
 def test_plan_rejects_bad_arguments(lib):
