@@ -1,29 +1,40 @@
 """Benchmark of one MLA decode step on one MI355X.
 
-A step is one pass of the whole path over a batch: mla_absorb_q ->
-mla_decode_splitkv -> mla_combine_out_proj (the log-sum-exp merge and the W^UV
-product in one launch), on synthetic inputs already resident in HBM (the split
-plan is made once per batch shape, before timing).  --unfused runs
-mla_combine and mla_out_proj as two launches instead; --merged fuses the merge
-into the decode (mla_decode_merged) and runs mla_out_proj after it.  With
---q-len T every sequence decodes its T newest tokens at once (causal among
-them): absorb on B*T rows, mla_decode_splitkv_multi, then the merge and W^UV
-on B*T rows.
+A step is one pass of the whole path over a batch for one attention layer:
+mla_absorb_q -> mla_decode_splitkv -> mla_combine_out_proj (the log-sum-exp
+merge and the W^UV product in one launch), on synthetic inputs already resident
+in HBM; the split plan is made once per batch shape, before timing.
+--unfused runs mla_combine and mla_out_proj as two launches instead; --merged
+fuses the merge into the decode (mla_decode_merged) and runs mla_out_proj after
+it.  With --q-len T every sequence decodes its T newest tokens at once (causal
+among them): absorb on B*T rows, mla_decode_splitkv_multi, then the merge and
+W^UV on B*T rows.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--merged | --unfused]
-                    [--q-len T] [--slots N] [--no-flush] [--no-cpu-baseline] [--copy-probe]
+                    [--q-len T] [--slots N] [--back-to-back] [--no-cpu-baseline] [--copy-probe]
 
-Prints ONE JSON line on stdout; progress goes to stderr.  The step time comes
-from HIP events at the step boundaries; a second pass over the same steps with
-an event between every two kernels gives the per-kernel times (those events
-add a few microseconds each, so the breakdown sums to more than the step).
-Before every step a
-512 MiB buffer is read (a reduction, untimed), so the 256 MB last-level cache
-holds other data, as after the other layers of a model, and the step reads its
-cache rows from HBM.  The flush reads rather than writes so that the step does
-not also pay for writing back dirty flush lines.  All events are recorded on
-the stream the kernels run on.
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+Timing.  Before every step a 512 MiB buffer is read (a reduction, untimed), so
+the 256 MB last-level cache holds other data and the step reads its cache rows
+from HBM; each step is timed between two HIP events recorded at its
+boundaries, and ms_per_step is their mean.  (The flush reads rather than
+writes so that the step does not also pay for writing back dirty lines.)  A
+second pass with an event between every two kernels gives the per-kernel
+breakdown (each event adds a few microseconds, so it sums to more than the
+step); a third pass times the decode launch alone in the same way, for the
+roofline of the decode kernel.
+
+--back-to-back instead runs the steps back to back, as the layers of a model
+do, cycling over the inputs of several layers (latent caches, weights and
+queries of the same shapes in different memory; enough layers that together
+they hold more than twice the last-level cache) with no flush, and times all K
+steps (and, in the third pass, K decode launches) between two events: the
+sustained rate, in which the chip runs at the clock its power limit allows
+under continuous decode.  All events are recorded on the stream the kernels
+run on.
 """
+
 from __future__ import annotations
 
 import argparse
@@ -117,7 +128,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v2_b64_l8192")
-    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--back-to-back", action="store_true",
+                    help="no flush: steps back to back over several layers' inputs, two events")
     ap.add_argument("--merged", action="store_true",
                     help="decode and merge in one launch (mla_decode_merged)")
     ap.add_argument("--unfused", action="store_true",
@@ -168,8 +180,13 @@ def main():
         q_pe = dev(np.stack([p for _, p in qs]).reshape(B * T, H, cfg.d_rope), bf)
         pos = wl.seq_lens[:, None].astype(np.int64) - T + np.arange(T)[None, :]
         positions = dev(pos.reshape(-1).astype(np.int32), False)
-    w_uk, w_uv = dev(wl.w_uk, bf), dev(wl.w_uv, bf)
-    cache = dev(wl.cache, bf)
+    layer0 = {"q_nope": q_nope, "q_pe": q_pe, "w_uk": dev(wl.w_uk, bf), "w_uv": dev(wl.w_uv, bf),
+              "cache": dev(wl.cache, bf)}
+    # further layers: the same values in other memory (what matters for the
+    # timing is that their rows, weights and queries are not where layer 0's are)
+    args.flush = not args.back_to_back
+    n_layers = 1 if args.flush else max(2, -(-(512 << 20) // wl.cache.nbytes) + 1)
+    layers = [layer0] + [{k: v.clone() for k, v in layer0.items()} for _ in range(n_layers - 1)]
     block_table, seq_lens = dev(wl.block_table, False), dev(wl.seq_lens, False)
     dims = mla.Dims(cfg.n_heads, cfg.d_head, cfg.d_latent, cfg.d_rope, cfg.page_size,
                     rope_base=cfg.rope_base, dtype=mla.BF16 if bf else mla.F32)
@@ -179,8 +196,7 @@ def main():
     items_h, offs_h = mla.plan_splits(dims, wl.seq_lens, max(1, slots // T))
     items, offs = torch.from_numpy(items_h).cuda(), torch.from_numpy(offs_h).cuda()
     log(f"[bench] {props.name} {getattr(props, 'gcnArchName', '')}, {props.multi_processor_count} CUs, "
-        f"plan for {slots} slots; "
-        f"{len(items_h)} work items, q_len {T}")
+        f"plan for {slots} slots; {len(items_h)} work items, q_len {T}, {n_layers} layer(s)")
 
     W = len(items_h)
     bufs = {
@@ -195,114 +211,145 @@ def main():
     if T == 1:
         for k in ("o_part", "lse_part"):
             bufs[k] = bufs[k].view(W, *bufs[k].shape[2:])
-    flush = None
-    if not args.no_flush:
+    stream = torch.cuda.current_stream()
+    q4 = bufs["q_abs"].view(B, T, H, dims.row)
+    ol4 = bufs["o_latent"].view(B, T, H, cfg.d_latent)
+    lse3 = bufs["lse"].view(B, T, H)
+    out4 = bufs["out"].view(B, T, H, cfg.d_head)
+
+    def launches_for(L):
+        absorb = lambda: mla.absorb_q(dims, L["q_nope"], L["q_pe"], positions, L["w_uk"],  # noqa: E731
+                                      bufs["q_abs"], stream)
+        if T > 1 and args.unfused:
+            names = ["absorb_q", "decode_splitkv_multi", "combine_multi", "out_proj"]
+            fns = [absorb,
+                   lambda: mla.decode_splitkv_multi(dims, q4, L["cache"], block_table, seq_lens, items,
+                                                    bufs["o_part"], bufs["lse_part"], stream),
+                   lambda: mla.combine_multi(dims, offs, bufs["o_part"], bufs["lse_part"], B, ol4,
+                                             lse3, stream),
+                   lambda: mla.out_proj(dims, bufs["o_latent"], L["w_uv"], bufs["out"], stream)]
+        elif T > 1:
+            names = ["absorb_q", "decode_splitkv_multi", "combine_out_proj"]
+            fns = [absorb,
+                   lambda: mla.decode_splitkv_multi(dims, q4, L["cache"], block_table, seq_lens, items,
+                                                    bufs["o_part"], bufs["lse_part"], stream),
+                   lambda: mla.combine_out_proj(dims, offs, bufs["o_part"], bufs["lse_part"],
+                                                L["w_uv"], B, out4, stream=stream)]
+        elif args.merged:
+            names = ["absorb_q", "decode_merged", "out_proj"]
+            fns = [absorb,
+                   lambda: mla.decode_merged(dims, bufs["q_abs"], L["cache"], block_table, seq_lens,
+                                             items, offs, bufs["tickets"], bufs["o_part"],
+                                             bufs["lse_part"], bufs["o_latent"], bufs["lse"], stream),
+                   lambda: mla.out_proj(dims, bufs["o_latent"], L["w_uv"], bufs["out"], stream)]
+        elif args.unfused:
+            names = ["absorb_q", "decode_splitkv", "combine", "out_proj"]
+            fns = [absorb,
+                   lambda: mla.decode_splitkv(dims, bufs["q_abs"], L["cache"], block_table, seq_lens,
+                                              items, bufs["o_part"], bufs["lse_part"], stream),
+                   lambda: mla.combine(dims, offs, bufs["o_part"], bufs["lse_part"], B,
+                                       bufs["o_latent"], bufs["lse"], stream),
+                   lambda: mla.out_proj(dims, bufs["o_latent"], L["w_uv"], bufs["out"], stream)]
+        else:
+            names = ["absorb_q", "decode_splitkv", "combine_out_proj"]
+            fns = [absorb,
+                   lambda: mla.decode_splitkv(dims, bufs["q_abs"], L["cache"], block_table, seq_lens,
+                                              items, bufs["o_part"], bufs["lse_part"], stream),
+                   lambda: mla.combine_out_proj(dims, offs, bufs["o_part"], bufs["lse_part"],
+                                                L["w_uv"], B, bufs["out"], stream=stream)]
+        return names, fns
+
+    per_layer = [launches_for(L) for L in layers]
+    names = per_layer[0][0]
+    n_k = len(names)
+    flush = sink = None
+    if args.flush:
         flush = torch.full((128 << 20,), 1.0, dtype=torch.float32, device="cuda")  # 512 MiB
         sink = torch.empty(1, dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
 
     def evict():
         if flush is not None:
             torch.sum(flush, dim=0, keepdim=True, out=sink)
 
-    absorb = lambda: mla.absorb_q(dims, q_nope, q_pe, positions, w_uk, bufs["q_abs"], stream)  # noqa: E731
-    q4 = bufs["q_abs"].view(B, T, H, dims.row)
-    ol4 = bufs["o_latent"].view(B, T, H, cfg.d_latent)
-    lse3 = bufs["lse"].view(B, T, H)
-    out4 = bufs["out"].view(B, T, H, cfg.d_head)
-    if T > 1 and args.unfused:
-        names = ["absorb_q", "decode_splitkv_multi", "combine_multi", "out_proj"]
-        launches = [
-            absorb,
-            lambda: mla.decode_splitkv_multi(dims, q4, cache, block_table, seq_lens, items,
-                                             bufs["o_part"], bufs["lse_part"], stream),
-            lambda: mla.combine_multi(dims, offs, bufs["o_part"], bufs["lse_part"], B, ol4, lse3,
-                                      stream),
-            lambda: mla.out_proj(dims, bufs["o_latent"], w_uv, bufs["out"], stream),
-        ]
-    elif T > 1:
-        names = ["absorb_q", "decode_splitkv_multi", "combine_out_proj"]
-        launches = [
-            absorb,
-            lambda: mla.decode_splitkv_multi(dims, q4, cache, block_table, seq_lens, items,
-                                             bufs["o_part"], bufs["lse_part"], stream),
-            lambda: mla.combine_out_proj(dims, offs, bufs["o_part"], bufs["lse_part"], w_uv, B,
-                                         out4, stream=stream),
-        ]
-    elif not args.merged and not args.unfused:
-        names = ["absorb_q", "decode_splitkv", "combine_out_proj"]
-        launches = [
-            absorb,
-            lambda: mla.decode_splitkv(dims, bufs["q_abs"], cache, block_table, seq_lens, items,
-                                       bufs["o_part"], bufs["lse_part"], stream),
-            lambda: mla.combine_out_proj(dims, offs, bufs["o_part"], bufs["lse_part"], w_uv, B,
-                                         bufs["out"], stream=stream),
-        ]
-    elif not args.merged:
-        names = ["absorb_q", "decode_splitkv", "combine", "out_proj"]
-        launches = [
-            lambda: mla.absorb_q(dims, q_nope, q_pe, positions, w_uk, bufs["q_abs"], stream),
-            lambda: mla.decode_splitkv(dims, bufs["q_abs"], cache, block_table, seq_lens, items,
-                                       bufs["o_part"], bufs["lse_part"], stream),
-            lambda: mla.combine(dims, offs, bufs["o_part"], bufs["lse_part"], B, bufs["o_latent"],
-                                bufs["lse"], stream),
-            lambda: mla.out_proj(dims, bufs["o_latent"], w_uv, bufs["out"], stream),
-        ]
-    else:
-        names = ["absorb_q", "decode_merged", "out_proj"]
-        launches = [
-            lambda: mla.absorb_q(dims, q_nope, q_pe, positions, w_uk, bufs["q_abs"], stream),
-            lambda: mla.decode_merged(dims, bufs["q_abs"], cache, block_table, seq_lens, items, offs,
-                                      bufs["tickets"], bufs["o_part"], bufs["lse_part"],
-                                      bufs["o_latent"], bufs["lse"], stream),
-            lambda: mla.out_proj(dims, bufs["o_latent"], w_uv, bufs["out"], stream),
-        ]
-    n_k = len(launches)
-
-    def step(ev=None):
-        for i, launch in enumerate(launches):
+    def step(k, ev=None):
+        fns = per_layer[k % n_layers][1]
+        for i, launch in enumerate(fns):
             if ev is not None:
                 ev[i].record(stream)
             launch()
         if ev is not None:
             ev[n_k].record(stream)
 
-    for _ in range(args.warmup):
-        evict()
-        step()
-    torch.cuda.synchronize()
+    def new_events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
-    # Timed region: K steps, HIP events on the kernels' stream at the step
-    # boundaries only (an event between two kernels adds several microseconds
-    # of its own to the step).
-    step_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for k in range(args.warmup):
+        evict()
+        step(k)
+    torch.cuda.synchronize()
+    k0 = args.warmup   # the first timed step uses the layer the last warmup step did not
+
+    # Timed region: K steps.
     torch.cuda.synchronize()
     w0 = time.perf_counter()
-    for k in range(args.steps):
-        evict()
-        step_ev[k][0].record(stream)
-        step()
-        step_ev[k][1].record(stream)
-    torch.cuda.synchronize()
+    if args.flush:
+        step_ev = [new_events(2) for _ in range(args.steps)]
+        for k in range(args.steps):
+            evict()
+            step_ev[k][0].record(stream)
+            step(k0 + k)
+            step_ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        step_ms = np.array([e[0].elapsed_time(e[1]) for e in step_ev])
+        ms = float(step_ms.mean())
+        spread = f"p10 {np.percentile(step_ms, 10):.4f}  p90 {np.percentile(step_ms, 90):.4f}"
+    else:
+        e0, e1 = new_events(2)
+        e0.record(stream)
+        for k in range(args.steps):
+            step(k0 + k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        spread = f"{args.steps} steps back to back"
     wall = time.perf_counter() - w0
-    step_ms = np.array([e[0].elapsed_time(e[1]) for e in step_ev])
-    ms = float(step_ms.mean())
-    # Per-kernel breakdown (and the decode launch time for the roofline): the
-    # same K steps again with an event between every two kernels.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_k + 1)] for _ in range(args.steps)]
+
+    # Per-kernel breakdown: the same steps with an event between every two kernels.
+    evs = [new_events(n_k + 1) for _ in range(args.steps)]
     for k in range(args.steps):
         evict()
-        step(evs[k])
+        step(k0 + k, evs[k])
     torch.cuda.synchronize()
     t = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(n_k)] for e in evs])  # ms
     k_ms = t.mean(axis=0)
-    log("[bench] per-kernel mean ms: " + ", ".join(f"{n} {v:.4f}" for n, v in zip(names, k_ms)))
-    log(f"[bench] step ms: mean {ms:.4f}  p10 {np.percentile(step_ms, 10):.4f}  "
-        f"p90 {np.percentile(step_ms, 90):.4f}; wall incl. flushes {wall * 1e3 / args.steps:.3f} ms/step")
+
+    # The decode kernel alone, K launches back to back (cycling over the layers).
+    dec = [fns[1] for _, fns in per_layer]
+    if args.flush:
+        d_ev = [new_events(2) for _ in range(args.steps)]
+        for k in range(args.steps):
+            evict()
+            d_ev[k][0].record(stream)
+            dec[0]()
+            d_ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in d_ev]))
+    else:
+        e0, e1 = new_events(2)
+        e0.record(stream)
+        for k in range(args.steps):
+            dec[(k0 + k) % n_layers]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / args.steps
+    log("[bench] per-kernel mean ms (event between kernels): " +
+        ", ".join(f"{n} {v:.4f}" for n, v in zip(names, k_ms)))
+    log(f"[bench] step ms: {ms:.4f} ({spread}); decode launch ms: {dec_ms:.4f}; "
+        f"wall {wall * 1e3 / args.steps:.3f} ms/step")
     assert torch.isfinite(bufs["out"]).all().item(), "non-finite output"
 
     work = algorithmic(cfg, wl.seq_lens, T)
-    dec_s = float(k_ms[1]) * 1e-3
+    dec_s = dec_ms * 1e-3
     achieved = work["decode_bytes"] / dec_s / 1e9
     traffic = measured_traffic(cfg.name) if T == 1 and not args.merged else None
     result = {
@@ -321,11 +368,13 @@ def main():
         "config": {"workload": cfg.name, "batch": B, "seq_len": int(wl.seq_lens.max()),
                    "total_tokens": int(wl.seq_lens.sum()), "n_heads": H, "d_head": cfg.d_head,
                    "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "page_size": cfg.page_size,
-                   "work_items": int(len(items_h)), "mall_flushed": flush is not None,
-                   "decode_entry": names[1], "q_len": T},
+                   "work_items": int(len(items_h)), "q_len": T, "decode_entry": names[1],
+                   "timing": ("per-step events, 512 MiB read flush before each step" if args.flush
+                              else f"back to back, cycling over {n_layers} layers' inputs")},
         "latent_cache_GBps": round(work["cache_bytes"] / (ms * 1e-3) / 1e9, 1),
         "tokens_per_s": round(B * T / (ms * 1e-3), 1),
         "kernel_ms": {n: round(float(v), 5) for n, v in zip(names, k_ms)},
+        "decode_ms": round(dec_ms, 5),
         "decode_TFLOPs": round(work["decode_flop"] / dec_s / 1e12, 2),
         "decode_mfma_frac": round(work["decode_flop"] / dec_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": {"kernel": names[1], "bound": "hbm",
@@ -334,25 +383,25 @@ def main():
                      "algorithmic_bytes_per_launch": work["decode_bytes"]},
     }
     # The cache write of the next token of every sequence (mla_append_kv), timed
-    # on its own: it precedes the step in a model and is not part of `value`.
+    # on its own (per-launch events): it precedes the step in a model and is not
+    # part of `value`.
     from synth import append_recipe, f32_to_bf16_bits
     ar = append_recipe(cfg, B)
     conv = (lambda a: f32_to_bf16_bits(a.astype(np.float32))) if bf else (lambda a: a.astype(np.float32))
     h_d, wdkv_d, wkr_d = dev(conv(ar["h"]), bf), dev(conv(ar["w_dkv"]), bf), dev(conv(ar["w_kr"]), bf)
     app_pos = torch.from_numpy(np.minimum(wl.seq_lens, wl.block_table.shape[1] * cfg.page_size - 1)
                                .astype(np.int32)).cuda()
-    cache_bak = cache  # the rows written (one slot per sequence) are rewritten identically each launch
+    cache0 = layers[0]["cache"]  # the rows written (one slot per sequence) are rewritten identically
     a_ms = []
     for k in range(args.warmup + args.steps):
-        evict()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        mla.append_kv(dims, h_d, wdkv_d, wkr_d, app_pos, cache_bak, block_table, rms_norm=cfg.rms_norm_latent,
-                      stream=stream)
-        e1.record(stream)
+        ea, eb = new_events(2)
+        ea.record(stream)
+        mla.append_kv(dims, h_d, wdkv_d, wkr_d, app_pos, cache0, block_table,
+                      rms_norm=cfg.rms_norm_latent, stream=stream)
+        eb.record(stream)
         torch.cuda.synchronize()
         if k >= args.warmup:
-            a_ms.append(e0.elapsed_time(e1))
+            a_ms.append(ea.elapsed_time(eb))
     a_ms = float(np.mean(a_ms))
     esz = 2 if bf else 4
     D = cfg.d_latent + cfg.d_rope
