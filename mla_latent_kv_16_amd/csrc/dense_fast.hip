@@ -72,26 +72,8 @@ __global__ __launch_bounds__(256) void absorb_kernel(
 
   const int b0 = blockIdx.y * 64;
   const int nb = min(64, batch - b0);
-  // RoPE part, float64 angle, float32 rotation.  The four quarter-workgroups
-  // of a head share the (sequence, pair) list; thread t keeps pair k = t % 32.
-  {
-    const int k = threadIdx.x & (kDr / 2 - 1);
-    const double theta = pow(rope_base, -2.0 * k / kDr);
-    for (int bi = quarter * 8 + (threadIdx.x >> 5); bi < nb; bi += 32) {
-      const int bb = b0 + bi;
-      double sd, cd;
-      sincos(static_cast<double>(positions[bb]) * theta, &sd, &cd);
-      const float c = static_cast<float>(cd), sn = static_cast<float>(sd);
-      const int64_t r = static_cast<int64_t>(bb) * H + h;
-      const uint32_t xy = *reinterpret_cast<const uint32_t*>(q_pe + r * kDr + 2 * k);
-      const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(xy & 0xffffu));
-      const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(xy >> 16));
-      *reinterpret_cast<uint32_t*>(q_abs + r * kDq + kDc + 2 * k) =
-          pack_bf16x2(x0 * c - x1 * sn, x0 * sn + x1 * c);
-    }
-  }
-
   // B operand: q^C of sequence b = b0 + 16w + q, values 32ks + 8g .. +8
+  // (loaded before the RoPE part so that both latencies overlap)
   const int b = b0 + 16 * w + q;
   const bool bvalid = b < batch;
   bf16x8 qn[4];
@@ -103,6 +85,37 @@ __global__ __launch_bounds__(256) void absorb_kernel(
     else
       qn[ks] = bf16x8{};
   }
+  // RoPE part, float64 angle, float32 rotation.  The four quarter-workgroups
+  // of a head share the (sequence, pair) list; thread t keeps pair k = t % 32
+  // of sequences bi0 and bi0 + 32 (its loads issued before any math).
+  {
+    const int k = threadIdx.x & (kDr / 2 - 1);
+    const int bi0 = quarter * 8 + (threadIdx.x >> 5);
+    int pos[2];
+    uint32_t xy[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int bi = bi0 + 32 * j;
+      const int64_t r = static_cast<int64_t>(b0 + bi) * H + h;
+      pos[j] = bi < nb ? positions[b0 + bi] : 0;
+      xy[j] = bi < nb ? *reinterpret_cast<const uint32_t*>(q_pe + r * kDr + 2 * k) : 0u;
+    }
+    const double theta = pow(rope_base, -2.0 * k / kDr);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int bi = bi0 + 32 * j;
+      if (bi >= nb) continue;
+      double sd, cd;
+      sincos(static_cast<double>(pos[j]) * theta, &sd, &cd);
+      const float c = static_cast<float>(cd), sn = static_cast<float>(sd);
+      const int64_t r = static_cast<int64_t>(b0 + bi) * H + h;
+      const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(xy[j] & 0xffffu));
+      const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(xy[j] >> 16));
+      *reinterpret_cast<uint32_t*>(q_abs + r * kDq + kDc + 2 * k) =
+          pack_bf16x2(x0 * c - x1 * sn, x0 * sn + x1 * c);
+    }
+  }
+
   __builtin_amdgcn_s_waitcnt(MLA_VMCNT0);
   __syncthreads();
   if (16 * w >= nb) return;  // no sequence for this wave (no barrier follows)
