@@ -19,6 +19,11 @@
 //    ch ^ swz(t) (see swz).  Each lane picks which global chunk it fetches,
 //    so the swizzle costs nothing at load time, and one per-lane offset plus
 //    a scalar base address every tile of a wave.
+//  * The LDS holds only four slots, so the stream is deepened through the L2:
+//    the V waves without DMA touch one 4-byte word of every 128-byte line of
+//    the slice MLA_PREFETCH_D ahead (the even lines in one workgroup of the
+//    pair, the odd ones in the other), with a load whose data lands in a junk
+//    LDS line; by the time that slice's DMA is issued its rows are in the L2.
 //  * QK^T operands: a lane reads 16 contiguous bytes (8 latent values of one
 //    token) with ds_read_b128.
 //  * PV operands: C^T needs 8 tokens of one latent column per lane; two
@@ -122,6 +127,19 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t 
                : "memory");
 }
 
+// 4 bytes per lane from `base + voff` into LDS at m0 + 4 * lane: used only to
+// pull rows into the L2 ahead of their DMA (the LDS bytes are never read).  No
+// register receives the data, so nothing waits for it until the epilogue.
+__device__ __forceinline__ void touch4(const char* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
+}
+// How many slices ahead of the one being scored the V waves without DMA pull
+// rows into the L2 (0: off).  The four-slot LDS ring keeps only two slices in
+// flight; these touches keep HBM reads of a third in flight as well.
+#ifndef MLA_PREFETCH_D
+#define MLA_PREFETCH_D 3
+#endif
+
 __device__ __forceinline__ bf16x8 lds_read128(const char* lds, uint32_t off) {
   return *reinterpret_cast<const bf16x8*>(lds + off);
 }
@@ -162,7 +180,7 @@ constexpr int kHeadsWG = 64;
 constexpr int kHeadBlocksWG = kHeadsWG / 16;        // 4
 constexpr int kPBytesWG = kHeadBlocksWG * 64 * 16;  // 4 KiB of weights per slice
 constexpr int kSWaves = 8;
-static_assert(kStages * kSlotBytes + 2 * kPBytesWG + kSWaves * 4 + 4 * kHeadsWG * 4 <= 163840,
+static_assert(kStages * kSlotBytes + 2 * kPBytesWG + 256 + kSWaves * 4 + 4 * kHeadsWG * 4 + 4 <= 163840,
               "LDS budget");
 
 __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
@@ -173,6 +191,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
   constexpr int H = 128;
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes + 2 * kPBytesWG];
+  __shared__ __attribute__((aligned(16))) char junk[256];
   __shared__ int ticket_lds;
   __shared__ int votes[kSWaves];          // after a pass: jump flags of the S waves
   __shared__ float mref_x[2][kHeadsWG];   // per token half: a head's maximum
@@ -412,6 +431,21 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
 #pragma unroll
       for (int j = 0; j < kLoadsPerWave; ++j) dma16(src + 128 * j, voff, dst + 1024 * j);
     };
+    // L2 prefetch of slice n: the 288 128-byte lines of its 32 rows, the even
+    // ones by half 0 of the pair and the odd ones by half 1 (the pair shares
+    // the L2), one 4-byte load per line from the V waves without DMA
+    const uint32_t junk_lds = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)junk));
+    auto prefetch = [&](int n) {
+      if (MLA_PREFETCH_D <= 0 || dma || n >= n_slices) return;
+      const int tok0 = t_begin + n * kSliceTok;
+      const int page = bt[tok0 >> 6];
+      const char* src = cache + static_cast<int64_t>(page) * (kPage * kRowBytes) +
+                        (tok0 & (kPage - 1)) * kRowBytes;
+      const int nv = t_end - tok0;
+      const int li = 2 * ((u - kDmaWaves) * 64 + lane) + hh;  // line of the slice
+      if (li < 288 && li / 9 < nv) touch4(src, static_cast<uint32_t>(li * 128), junk_lds);
+    };
     // wait for this wave's part of slice k (slice k+1 may stay in flight)
     auto wait_slice = [&](int k) {
       if (k + 1 < n_slices)
@@ -465,10 +499,12 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       __syncthreads();
       if (dma && 2 < n_slices) issue(2);
       __syncthreads();  // the S waves' first-slice maximum exchange
+      for (int n = 2; n <= MLA_PREFETCH_D; ++n) prefetch(n);
       for (int k = 1; k <= n_slices; ++k) {
         if (dma && k < n_slices) wait_slice(k);
         __syncthreads();
         if (dma && k + 2 < n_slices) issue(k + 2);
+        prefetch(k + MLA_PREFETCH_D);
         accumulate(slot_of(k - 1), pbuf_of(k - 1));
       }
       // vote (written by the S waves)
@@ -499,6 +535,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     }
     // epilogue: normalise by the row sums of the S waves and write the partial
     // (or, for a sequence with one item in merged mode, o~ itself)
+    if (MLA_PREFETCH_D > 0 && !dma) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));  // prefetches landed
     __syncthreads();
 #pragma unroll
     for (int hb = 0; hb < kHeadBlocksWG; ++hb) {
