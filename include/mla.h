@@ -63,7 +63,10 @@
  *   out         [batch][n_heads][d_head]                 float32: o_i
  * Alignment: device pointers of dtype or float32 arrays must be 16-byte aligned.
  * Numerics: bf16 operands with float32 accumulation; softmax in float32; RoPE
- *   angles p * theta_k and their sine/cosine in float64, the rotation in float32.
+ *   angles p * theta_k in float64 and the rotation in float32.  The sine/cosine
+ *   are float64 except in the gfx950 fast absorb, which reduces the float64
+ *   angle to [-pi, pi] in float64 and takes them in float32 (within about one
+ *   float32 ulp of the float64 values).
  *   The fast decode kernel weighs tokens against each work item's first-slice
  *   score maximum; if a later maximum exceeds it by more than 2^20 it recomputes
  *   the item against exact maxima.  The environment variable

@@ -46,12 +46,31 @@ __device__ __forceinline__ void xcd_split(int i, int per, int& head, int& sub) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int tsw(int row) { return ((row & 3) << 1) | (((row >> 3) & 1) << 3); }
 
+// theta_k = rope_base^(-2k / d_h^R), k < 32, computed on the host in float64
+struct RopeTheta {
+  double t[kDr / 2];
+};
+
+// sin and cos of the float64 angle x: x reduced to [-pi, pi] in float64 (two-term
+// Cody-Waite with fused multiply-adds, error ~1e-15 for |x| < 2^20), then sin/cos
+// of the reduced angle in float32 (about 1 float32 ulp from the float64 result
+// rounded to float32)
+__device__ __forceinline__ void sincos_reduced(double x, float& sn, float& cs) {
+  constexpr double kTwoPiHi = 6.283185307179586, kTwoPiLo = 2.4492935982947064e-16;
+  const double n = rint(x * (1.0 / kTwoPiHi));
+  double r = fma(-n, kTwoPiHi, x);
+  r = fma(-n, kTwoPiLo, r);
+  sincosf(static_cast<float>(r), &sn, &cs);
+}
+
 __global__ __launch_bounds__(256) void absorb_kernel(
-    int batch, int H, double rope_base, const uint16_t* __restrict__ q_nope,
+    int batch, int H, RopeTheta theta_k, const uint16_t* __restrict__ q_nope,
     const uint16_t* __restrict__ q_pe, const int32_t* __restrict__ positions,
     const char* __restrict__ w_uk, uint16_t* __restrict__ q_abs) {
   constexpr int kCols = 128, kTileRow = kCols * 2;  // 256 bytes
+  constexpr int kStageRow = kTileRow + 16;          // output staging row, padded
   __shared__ __attribute__((aligned(1024))) char lds[kDh * kTileRow];
+  __shared__ __attribute__((aligned(16))) char stage[4 * 16 * kStageRow];
   const uint32_t lds_base = static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
   int h, quarter;
@@ -100,14 +119,13 @@ __global__ __launch_bounds__(256) void absorb_kernel(
       pos[j] = bi < nb ? positions[b0 + bi] : 0;
       xy[j] = bi < nb ? *reinterpret_cast<const uint32_t*>(q_pe + r * kDr + 2 * k) : 0u;
     }
-    const double theta = pow(rope_base, -2.0 * k / kDr);
+    const double theta = theta_k.t[k];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int bi = bi0 + 32 * j;
       if (bi >= nb) continue;
-      double sd, cd;
-      sincos(static_cast<double>(pos[j]) * theta, &sd, &cd);
-      const float c = static_cast<float>(cd), sn = static_cast<float>(sd);
+      float sn, c;
+      sincos_reduced(static_cast<double>(pos[j]) * theta, sn, c);
       const int64_t r = static_cast<int64_t>(b0 + bi) * H + h;
       const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(xy[j] & 0xffffu));
       const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(xy[j] >> 16));
@@ -124,7 +142,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(
   // source-lane role q -> row 8g + q/4 of the k block, chunk 2cb + (q%4)/2.
   const int arow = 8 * g + (q >> 2);
   const int sw0 = tsw(arow), sw1 = tsw(arow + 4);
-  uint16_t* qrow = q_abs + (static_cast<int64_t>(b) * H + h) * kDq + c0 + 4 * g;
+  float4_t accs[kCols / 16];
 #pragma unroll
   for (int cb = 0; cb < kCols / 16; ++cb) {
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -141,12 +159,25 @@ __global__ __launch_bounds__(256) void absorb_kernel(
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qn[ks], acc, 0, 0, 0);
     }
-    // lane holds q~[c0 + 16cb + 4g + i] of sequence b
-    if (bvalid) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(qrow + 16 * cb);
-      dst[0] = pack_bf16x2(acc[0], acc[1]);
-      dst[1] = pack_bf16x2(acc[2], acc[3]);
-    }
+    accs[cb] = acc;  // q~[c0 + 16cb + 4g + i] of sequence b
+  }
+  // Through a wave-private LDS block (16 sequences x 128 columns, rows padded to
+  // 272 bytes) so that the stores write whole 256-byte row segments, 16 bytes
+  // per lane.  LDS accesses of one wave complete in order: no barrier.
+  char* st = stage + w * (16 * kStageRow);
+#pragma unroll
+  for (int cb = 0; cb < kCols / 16; ++cb) {
+    const uint32_t lo = pack_bf16x2(accs[cb][0], accs[cb][1]);
+    const uint32_t hi = pack_bf16x2(accs[cb][2], accs[cb][3]);
+    *reinterpret_cast<uint64_t*>(st + q * kStageRow + 32 * cb + 8 * g) = (static_cast<uint64_t>(hi) << 32) | lo;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rr = (lane >> 4) + 4 * j, c = lane & 15;
+    const float4_t v = *reinterpret_cast<const float4_t*>(st + rr * kStageRow + 16 * c);
+    const int bb = b0 + 16 * w + rr;
+    if (bb < batch)
+      *reinterpret_cast<float4_t*>(q_abs + (static_cast<int64_t>(bb) * H + h) * kDq + c0 + 8 * c) = v;
   }
 }
 
@@ -320,8 +351,10 @@ hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const v
                        hipStream_t stream) {
   const int groups = (batch + 63) / 64;
   if (groups > 65535 || d.n_heads % 8 != 0) return hipErrorInvalidValue;
+  RopeTheta theta;
+  for (int k = 0; k < kDr / 2; ++k) theta.t[k] = pow(d.rope_base, -2.0 * k / kDr);
   hipLaunchKernelGGL(absorb_kernel, dim3(d.n_heads * 4, groups), dim3(256), 0, stream, batch,
-                     d.n_heads, d.rope_base, static_cast<const uint16_t*>(q_nope),
+                     d.n_heads, theta, static_cast<const uint16_t*>(q_nope),
                      static_cast<const uint16_t*>(q_pe), positions,
                      static_cast<const char*>(w_uk), static_cast<uint16_t*>(q_abs));
   return hipGetLastError();
