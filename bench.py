@@ -32,7 +32,9 @@ they hold more than twice the last-level cache) with no flush, and times all K
 steps (and, in the third pass, K decode launches) between two events: the
 sustained rate, in which the chip runs at the clock its power limit allows
 under continuous decode.  All events are recorded on the stream the kernels
-run on.
+run on.  They are HIP events created with hipEventDisableSystemFence (timing
+only: recording one does not write back and invalidate the caches);
+--fenced-events uses torch.cuda.Event instead.
 """
 
 from __future__ import annotations
@@ -57,6 +59,49 @@ METRIC = "MLA decode TFLOP/s + latent-cache GB/s (% roofline), B=64 S=8192 H=128
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+class HipTimingEvent:
+    """A HIP event made for timing only: created with hipEventDisableSystemFence,
+    so that recording it performs no system-scope cache write-back and
+    invalidate (which otherwise adds several microseconds to every bracket and
+    slows the work after it).  Same interface as torch.cuda.Event for what the
+    bench uses; it lives in the HIP runtime torch has loaded."""
+    _lib = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if HipTimingEvent._lib is None:
+            import torch  # noqa: F401  (loads the HIP runtime this must share)
+            lib = ctypes.CDLL("libamdhip64.so.7")
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipTimingEvent._lib = lib
+        self._ctypes = ctypes
+        self.ev = ctypes.c_void_p()
+        rc = self._lib.hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = self._lib.hipEventRecord(self.ev, self._ctypes.c_void_p(int(stream.cuda_stream)))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        ms = self._ctypes.c_float(0.0)
+        rc = self._lib.hipEventElapsedTime(self._ctypes.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def __del__(self):
+        if self._lib is not None and self.ev:
+            self._lib.hipEventDestroy(self.ev)
 
 
 def algorithmic(cfg, lens, q_len: int = 1):
@@ -138,6 +183,8 @@ def main():
                     help="query tokens per sequence (multi-token decode)")
     ap.add_argument("--slots", type=int, default=0,
                     help="workgroup slots the split plan aims at (default: the CU count)")
+    ap.add_argument("--fenced-events", action="store_true",
+                    help="time with torch.cuda.Event (each record also writes back and invalidates caches)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -281,7 +328,9 @@ def main():
             ev[n_k].record(stream)
 
     def new_events(n):
-        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        if args.fenced_events:
+            return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        return [HipTimingEvent() for _ in range(n)]
 
     for k in range(args.warmup):
         evict()
