@@ -11,7 +11,8 @@ among them): absorb on B*T rows, mla_decode_splitkv_multi, then the merge and
 W^UV on B*T rows.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--merged | --unfused]
-                    [--q-len T] [--slots N] [--back-to-back] [--no-cpu-baseline] [--copy-probe]
+                    [--q-len T] [--slots N] [--back-to-back] [--prefill T [--prefill-batch B]]
+                    [--fenced-events] [--no-cpu-baseline] [--copy-probe]
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
@@ -167,6 +168,76 @@ def cpu_baseline(wl, budget_s: float = 20.0):
             "seq_per_s": len(done) / t_total}
 
 
+def time_prefill(args, cfg, wl, dims, L0, block_table, seq_lens, stream, new_events, evict, slots):
+    """A T-token prefill of the first sequences (each of length >= T): the
+    materialised-K/V path (mla_prefill_naive) against the absorbed path
+    (absorb on B*T rows, multi-token decode, merge and W^UV on B*T rows)."""
+    import torch
+
+    import mla_latent_kv_16_amd as mla
+    from synth import query_multi
+    T, Bp = args.prefill, min(args.prefill_batch, cfg.batch)
+    H = cfg.n_heads
+    lens = wl.seq_lens[:Bp].astype(np.int64)
+    assert np.all(lens >= T), "every sequence must hold the T prefill tokens"
+    qs = [query_multi(cfg, b, T) for b in range(Bp)]
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).view(torch.int16).view(torch.bfloat16).cuda()
+    qn, qp = dev(np.stack([a for a, _ in qs])), dev(np.stack([p for _, p in qs]))
+    bt, sl = block_table[:Bp].contiguous(), seq_lens[:Bp].contiguous()
+    need = mla.load().mla_prefill_workspace_bytes(__import__("ctypes").byref(dims.c()), Bp, bt.shape[1])
+    ws = torch.empty(need // 2, dtype=torch.int16, device="cuda")
+    out = torch.empty((Bp, T, H, cfg.d_head), dtype=torch.float32, device="cuda")
+    # absorbed path buffers
+    pos = (lens[:, None] - T + np.arange(T)[None, :]).reshape(-1).astype(np.int32)
+    pos_d = torch.from_numpy(pos).cuda()
+    items_h, offs_h = mla.plan_splits(dims, wl.seq_lens[:Bp], max(1, slots // T))
+    items, offs = torch.from_numpy(items_h).cuda(), torch.from_numpy(offs_h).cuda()
+    q_abs = torch.empty((Bp, T, H, dims.row), dtype=torch.bfloat16, device="cuda")
+    o_part = torch.empty((len(items_h), T, H, cfg.d_latent), dtype=torch.float32, device="cuda")
+    lse_part = torch.empty((len(items_h), T, H), dtype=torch.float32, device="cuda")
+    out2 = torch.empty((Bp, T, H, cfg.d_head), dtype=torch.float32, device="cuda")
+
+    def naive():
+        mla.prefill_naive(dims, qn, qp, L0["w_uk"], L0["w_uv"], L0["cache"], bt, sl, out=out,
+                          want_lse=False, workspace=ws, stream=stream)
+
+    def absorbed():
+        mla.absorb_q(dims, qn.view(Bp * T, H, cfg.d_head), qp.view(Bp * T, H, cfg.d_rope), pos_d,
+                     L0["w_uk"], q_abs.view(Bp * T, H, dims.row), stream)
+        mla.decode_splitkv_multi(dims, q_abs, L0["cache"], bt, sl, items, o_part, lse_part, stream)
+        mla.combine_out_proj(dims, offs, o_part, lse_part, L0["w_uv"], Bp, out2, stream=stream)
+
+    res = {"q_len": T, "batch": Bp, "seq_len": int(lens.max())}
+    seen = int(lens.sum()) * T - Bp * T * (T - 1) // 2          # (query, key) pairs
+    for name, fn in (("naive", naive), ("absorbed", absorbed)):
+        for _ in range(2):
+            evict()
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(max(3, min(args.steps, 10))):
+            evict()
+            e0, e1 = new_events(2)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.mean(ts))
+        if name == "naive":
+            flop = 2 * int(lens.sum()) * H * cfg.d_head * cfg.d_latent * 2 + seen * H * 2 * (dims.row - cfg.d_latent + 2 * cfg.d_head)
+        else:
+            flop = seen * H * 2 * (dims.row + cfg.d_latent) + 2 * Bp * T * H * cfg.d_head * cfg.d_latent * 2
+        res[name] = {"ms": round(ms, 4), "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 1),
+                     "tokens_per_s": round(Bp * T / (ms * 1e-3), 1)}
+        log(f"[bench] prefill T={T} B={Bp} {name}: {ms:.3f} ms, {flop / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    d = float(np.linalg.norm((out - out2).cpu().numpy()) / np.linalg.norm(out2.cpu().numpy()))
+    res["rel_l2_naive_vs_absorbed"] = d
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +256,10 @@ def main():
                     help="workgroup slots the split plan aims at (default: the CU count)")
     ap.add_argument("--fenced-events", action="store_true",
                     help="time with torch.cuda.Event (each record also writes back and invalidates caches)")
+    ap.add_argument("--prefill", type=int, default=0, metavar="T",
+                    help="also time a T-token prefill of the first --prefill-batch sequences, "
+                         "materialised-K/V path and absorbed path")
+    ap.add_argument("--prefill-batch", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -458,6 +533,9 @@ def main():
     result["append_kv"] = {"ms": round(a_ms, 5), "algorithmic_bytes": a_bytes,
                            "GBps": round(a_bytes / (a_ms * 1e-3) / 1e9, 1), "d_model": cfg.d_model}
     log(f"[bench] append_kv {a_ms * 1e3:.1f} us for {B} tokens ({a_bytes / 1e6:.2f} MB algorithmic)")
+    if args.prefill > 0:
+        result["prefill"] = time_prefill(args, cfg, wl, dims, layers[0], block_table, seq_lens, stream,
+                                         new_events, evict, slots)
     if args.copy_probe:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -14,6 +14,8 @@
  *   mla_decode_merged   the two above in one launch
  *   mla_decode_splitkv_multi, mla_combine_multi
  *                       the same for q_len query tokens per sequence (causal)
+ *   mla_prefill_naive   q_len query tokens per sequence through the materialised
+ *                       per-head K/V path (for long chunks, where it costs less)
  *   mla_append_kv       write the decoded token's [c^KV | RoPE(k^R)] row into the cache
  *   mla_out_proj        o_i = W^UV_i o~_i                                    (per head i)
  *   mla_combine_out_proj  mla_combine and mla_out_proj in one launch
@@ -201,6 +203,39 @@ mla_status mla_combine(const mla_dims* dims, int32_t batch, const int32_t* split
 mla_status mla_combine_multi(const mla_dims* dims, int32_t batch, int32_t q_len,
                              const int32_t* split_offsets, const float* o_part,
                              const float* lse_part, float* o_latent, float* lse, void* stream);
+
+/* Prefill through the naive path: per-head keys and values are materialised
+ * from the latent, then the q_len newest tokens of each sequence (already in
+ * the cache) attend causally to it.  Page "DeepSeek V2 技术解析" 2.2.1.1
+ * (k^C = W^UK c^KV and v^C = W^UV c^KV recover per-head keys and values),
+ * 2.2.1.2 (a query sees only the tokens up to its own) and 2.2.2 (key
+ * [k^C ; RoPE(k^R)], query [q^C ; RoPE(q^R)]).  For sequence b of length L, head
+ * i and token t at position p = L - q_len + t:
+ *   K_j = [W^UK_i c_j ; kr_j]  (kr_j as cached, already rotated),  V_j = W^UV_i c_j
+ *   q   = [q^C ; RoPE_p(q^R)]   (q^R not yet rotated: the call rotates it)
+ *   out[b][t][i] = sum_{j <= p} softmax_j(softmax_scale * q . K_j) V_j   (float32)
+ *   lse[b][t][i] = log sum_{j <= p} exp(softmax_scale * q . K_j)          (or NULL)
+ * Layouts: q_nope [batch][q_len][n_heads][d_head] bf16; q_pe [batch][q_len]
+ * [n_heads][d_rope] bf16; w_uk, w_uv [n_heads * d_head][d_latent] bf16; cache
+ * and block table as for mla_decode_splitkv; out [batch][q_len][n_heads][d_head]
+ * float32.  K^C and V^C are rounded to bf16 in `workspace` (device memory of at
+ * least mla_prefill_workspace_bytes() bytes, 16-byte aligned, owned by the
+ * caller; contents afterwards unspecified).  Supported shapes: bf16, d_latent
+ * 512, d_rope 64, d_head 128, page 64, any head count.
+ * Device data is not checked: every L_b must be >= q_len.
+ * Errors: MLA_ERR_INVALID_ARG for null pointers, sizes < 1 or misalignment;
+ * MLA_ERR_UNSUPPORTED for other shapes or sizes out of range; MLA_ERR_WORKSPACE
+ * for a short workspace. */
+mla_status mla_prefill_naive(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_nope,
+                             const void* q_pe, const void* w_uk, const void* w_uv,
+                             const void* kv_cache, int32_t num_pages, const int32_t* block_table,
+                             int32_t max_pages_per_seq, const int32_t* seq_lens, void* workspace,
+                             int64_t workspace_bytes, float* out, float* lse, void* stream);
+
+/* Bytes of workspace mla_prefill_naive needs for this batch and block-table
+ * width (K^C and V^C of every row the table can address, bf16); -1 on bad
+ * arguments or an unsupported shape.  Host only. */
+int64_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_pages_per_seq);
 
 /* Split-KV decode with the log-sum-exp merge fused in: the o_latent and lse of
  * mla_combine from one launch (same items and split_offsets as the two calls).

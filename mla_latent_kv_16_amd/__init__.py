@@ -7,7 +7,7 @@ been built -- there is no fallback.
 
 Entry points mirror include/mla.h:
     absorb_q, plan_splits, decode_splitkv, combine, decode_merged, out_proj, append_kv,
-    decode_splitkv_multi, combine_multi, combine_out_proj
+    decode_splitkv_multi, combine_multi, combine_out_proj, prefill_naive
 plus `decode_step`, which runs the four device steps in order.
 """
 from __future__ import annotations
@@ -21,6 +21,7 @@ import numpy as np
 
 __all__ = ["MlaError", "Dims", "load", "lib_path", "absorb_q", "plan_splits", "decode_splitkv",
            "decode_merged", "append_kv", "decode_splitkv_multi", "combine_multi", "combine_out_proj",
+           "prefill_naive",
            "combine", "out_proj", "decode_step", "fast_path", "version", "BF16", "F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -101,6 +102,9 @@ def load():
                                      vp, vp]),
         "mla_out_proj": (i32, [pd, i32, vp, vp, vp, vp]),
         "mla_combine_out_proj": (i32, [pd, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "mla_prefill_naive": (i32, [pd, i32, i32, vp, vp, vp, vp, vp, i32, vp, i32, vp, vp,
+                                     ctypes.c_int64, vp, vp, vp]),
+        "mla_prefill_workspace_bytes": (ctypes.c_int64, [pd, i32, i32]),
         "mla_append_kv": (i32, [pd, i32, i32, vp, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, i32,
                                  vp, ctypes.c_int64, vp]),
         "mla_append_kv_workspace_bytes": (ctypes.c_int64, [pd, i32, i32]),
@@ -392,6 +396,41 @@ def combine_out_proj(dims: Dims, split_offsets, o_part, lse_part, w_uv, batch: i
         _ptr(o_latent, torch.float32, (*lead, H, dims.d_latent), "o_latent"),
         _ptr(lse, torch.float32, (*lead, H), "lse"), _stream(stream)), "mla_combine_out_proj")
     return out
+
+
+def prefill_naive(dims: Dims, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, seq_lens,
+                  out=None, lse=None, workspace=None, stream=None, want_lse: bool = True):
+    """Prefill of the q_len newest tokens of each sequence through the materialised
+    K/V path: q_nope [B, T, H, d_h], q_pe [B, T, H, d_r] (not yet rotated) ->
+    (out [B, T, H, d_h] float32, lse [B, T, H] float32 or None)."""
+    torch = _torch()
+    dt = _store_dtype(dims)
+    B, T, H = q_nope.shape[0], q_nope.shape[1], dims.n_heads
+    dev = q_nope.device
+    max_pages = block_table.shape[1]
+    L = load()
+    need = L.mla_prefill_workspace_bytes(ctypes.byref(dims.c()), B, max_pages)
+    if need < 0:
+        raise MlaError(-2, "mla_prefill_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need // 2, dtype=torch.int16, device=dev)
+    if out is None:
+        out = torch.empty((B, T, H, dims.d_head), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    num_pages = kv_cache.shape[0]
+    _check(L.mla_prefill_naive(
+        ctypes.byref(dims.c()), B, T, _ptr(q_nope, dt, (B, T, H, dims.d_head), "q_nope"),
+        _ptr(q_pe, dt, (B, T, H, dims.d_rope), "q_pe"),
+        _ptr(w_uk, dt, (H * dims.d_head, dims.d_latent), "w_uk"),
+        _ptr(w_uv, dt, (H * dims.d_head, dims.d_latent), "w_uv"),
+        _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
+        _ptr(block_table, torch.int32, None, "block_table"), max_pages,
+        _ptr(seq_lens, torch.int32, (B,), "seq_lens"),
+        _ptr(workspace, None, None, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(out, torch.float32, (B, T, H, dims.d_head), "out"),
+        _ptr(lse, torch.float32, (B, T, H), "lse"), _stream(stream)), "mla_prefill_naive")
+    return out, lse
 
 
 def decode_step(dims: Dims, q_nope, q_pe, positions, w_uk, w_uv, kv_cache, block_table, seq_lens,

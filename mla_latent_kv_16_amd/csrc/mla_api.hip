@@ -257,6 +257,38 @@ mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const float* o_late
   return launched(out_proj_generic(*dims, batch, o_latent, w_uv, out, st));
 }
 
+int64_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t max_pages_per_seq) {
+  if (check_dims(dims) != MLA_OK || batch < 1 || max_pages_per_seq < 1) return -1;
+  if (!is_prefill_shape(*dims)) return -1;
+  return prefill_workspace_bytes(*dims, batch, max_pages_per_seq);
+}
+
+mla_status mla_prefill_naive(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_nope,
+                             const void* q_pe, const void* w_uk, const void* w_uv,
+                             const void* kv_cache, int32_t num_pages, const int32_t* block_table,
+                             int32_t max_pages_per_seq, const int32_t* seq_lens, void* workspace,
+                             int64_t workspace_bytes, float* out, float* lse, void* stream) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  if (batch < 1 || q_len < 1 || num_pages < 1 || max_pages_per_seq < 1) return MLA_ERR_INVALID_ARG;
+  if (!q_nope || !q_pe || !w_uk || !w_uv || !kv_cache || !block_table || !seq_lens || !workspace ||
+      !out)
+    return MLA_ERR_INVALID_ARG;
+  if (!al16(q_nope) || !al16(q_pe) || !al16(w_uk) || !al16(w_uv) || !al16(kv_cache) ||
+      !al16(workspace) || !al16(out) || !al4(block_table) || !al4(seq_lens) || (lse && !al4(lse)))
+    return MLA_ERR_INVALID_ARG;
+  if (!is_prefill_shape(*dims)) return MLA_ERR_UNSUPPORTED;
+  if (2 * static_cast<int64_t>(batch) > 65535 ||
+      static_cast<int64_t>(batch) * q_len * dims->n_heads > (int64_t{1} << 31) ||
+      static_cast<int64_t>(max_pages_per_seq) * 64 > (int64_t{1} << 24))
+    return MLA_ERR_UNSUPPORTED;
+  if (workspace_bytes < prefill_workspace_bytes(*dims, batch, max_pages_per_seq)) return MLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+  return launched(prefill_naive(*dims, batch, q_len, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table,
+                                max_pages_per_seq, seq_lens, workspace, out, lse, st));
+}
+
 mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t q_len,
                                 const int32_t* split_offsets, const float* o_part,
                                 const float* lse_part, const void* w_uv, float* out,

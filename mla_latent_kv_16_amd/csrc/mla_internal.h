@@ -54,6 +54,15 @@ hipError_t combine_out_proj_fast(const mla_dims& d, int batch, int q_len, const 
                                  const float* o_part, const float* lse_part, const void* w_uv,
                                  float* out, float* o_latent, float* lse, hipStream_t stream);
 
+// Prefill through the materialised-K/V path (bf16, d_c 512, d_h^R 64, d_h 128,
+// 64-token pages, any head count).
+bool is_prefill_shape(const mla_dims& d);
+int64_t prefill_workspace_bytes(const mla_dims& d, int batch, int max_pages);
+hipError_t prefill_naive(const mla_dims& d, int batch, int q_len, const void* q_nope, const void* q_pe,
+                         const void* w_uk, const void* w_uv, const void* kv_cache,
+                         const int32_t* block_table, int max_pages, const int32_t* seq_lens,
+                         void* workspace, float* out, float* lse, hipStream_t stream);
+
 // Cache write of one token per sequence (append.hip); `ws` holds
 // append_slices(d_model) x batch x (d_latent + d_rope) floats.
 int append_slices(int d_model);

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
     assert {"mla_absorb_q", "mla_plan_splits", "mla_decode_splitkv", "mla_combine",
             "mla_decode_merged", "mla_append_kv", "mla_out_proj", "mla_decode_splitkv_multi",
-            "mla_combine_multi", "mla_combine_out_proj"} <= set(names)
+            "mla_combine_multi", "mla_combine_out_proj", "mla_prefill_naive"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -202,6 +202,34 @@ def test_combine_out_proj_rejects_bad_arguments(lib):
     assert f(_d(), 2 ** 20, 2 ** 10, *good) == UNSUPPORTED
     # off the fast path the two kernels need o_latent between them
     assert f(_d(mla.Dims(64, 128, 512, 64)), 2, 1, *good) == UNSUPPORTED
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    f = lib.mla_prefill_naive
+    need = lib.mla_prefill_workspace_bytes(_d(), 2, 4)
+    assert need == 2 * 2 * 128 * 4 * 64 * 128 * 2
+    assert lib.mla_prefill_workspace_bytes(_d(), 0, 4) == -1
+    assert lib.mla_prefill_workspace_bytes(_d(mla.Dims(4, 16, 64, 8, dtype=mla.F32)), 2, 4) == -1
+    # q_nope q_pe w_uk w_uv cache num_pages bt max_pages seq_lens ws ws_bytes out lse stream
+    good = [A, A, A, A, A, 10, A, 4, A, A, need, A, None, None]
+    assert f(_d(), 0, 3, *good) == INVALID
+    assert f(_d(), 2, 0, *good) == INVALID
+    for i in (0, 1, 2, 3, 4, 6, 8, 9, 11):         # each required pointer set to NULL
+        args = list(good)
+        args[i] = None
+        assert f(_d(), 2, 3, *args) == INVALID, i
+    for i, bad in ((5, 0), (7, 0)):                # num_pages, max_pages < 1
+        args = list(good)
+        args[i] = bad
+        assert f(_d(), 2, 3, *args) == INVALID, i
+    for i, bad in ((0, MIS), (4, MIS), (9, MIS), (11, MIS), (6, A + 2), (12, A + 2)):
+        args = list(good)                          # misaligned
+        args[i] = bad
+        assert f(_d(), 2, 3, *args) == INVALID, i
+    args = list(good)
+    args[10] = need - 2                            # short workspace
+    assert f(_d(), 2, 3, *args) == WORKSPACE
+    assert f(_d(mla.Dims(4, 16, 64, 8, dtype=mla.F32)), 2, 3, *good) == UNSUPPORTED
 
 
 def test_plan_rejects_bad_arguments(lib):
