@@ -231,15 +231,16 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
   const int rl0 = threadIdx.x >> 7;
   float4_t v[kOutF4];
   if constexpr (kMerge) {
-    // Row rl = rl0 + 4i has items s0[i] .. s1[i].  The partials of its first
-    // two items are loaded before anything waits (16 loads in flight per
-    // thread); later items, if any, are loaded one at a time.  M, Z and the
-    // weighted sum follow the combine's arithmetic in item order, so every
-    // thread of a row computes the same M and Z.
-    constexpr int kPre = 2;
+    // Row rl = rl0 + 4i has items s0[i] .. s0[i] + ns[i] - 1 (the same for
+    // every lane of a wave).  Items go two at a time with the loads of all
+    // eight rows in flight together: the partials and lse of the first two are
+    // loaded before anything waits; a first pass takes M over the lse of the
+    // rest, a second forms Z and the weighted sum.  Each row's arithmetic is
+    // the combine's, in item order, so every thread of a row computes the same
+    // M and Z and o~ matches mla_combine bit for bit.
+    constexpr int kPair = 2;
     int s0[kOutF4], ns[kOutF4], tq[kOutF4];
-    float4_t x[kPre][kOutF4];
-    float lv[kPre][kOutF4];
+    int nsmax = 0;
 #pragma unroll
     for (int i = 0; i < kOutF4; ++i) {
       const int rl = rl0 + 4 * i;
@@ -248,51 +249,83 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
       tq[i] = r % q_len;
       s0[i] = offs[b];
       ns[i] = rl < nr ? offs[b + 1] - s0[i] : 0;
+      nsmax = max(nsmax, ns[i]);
     }
+    auto prow = [&](int i, int k) -> int64_t {
+      return (static_cast<int64_t>(s0[i] + k) * q_len + tq[i]) * H + h;
+    };
+    float4_t x[kPair][kOutF4];
+    float lv[kPair][kOutF4];
+    auto load_pair = [&](int k) {
 #pragma unroll
-    for (int k = 0; k < kPre; ++k) {
+      for (int u = 0; u < kPair; ++u)
 #pragma unroll
-      for (int i = 0; i < kOutF4; ++i) {
-        const bool ok = k < ns[i];
-        const int64_t pr = (static_cast<int64_t>(s0[i] + k) * q_len + tq[i]) * H + h;
-        x[k][i] = ok ? *reinterpret_cast<const float4_t*>(o_part + pr * kDc + c4) : float4_t{0.f, 0.f, 0.f, 0.f};
-        lv[k][i] = ok ? lse_part[pr] : -INFINITY;
-      }
+        for (int i = 0; i < kOutF4; ++i) {
+          const bool ok = k + u < ns[i];
+          x[u][i] = ok ? *reinterpret_cast<const float4_t*>(o_part + prow(i, k + u) * kDc + c4)
+                       : float4_t{0.f, 0.f, 0.f, 0.f};
+          lv[u][i] = ok ? lse_part[prow(i, k + u)] : -INFINITY;
+        }
+    };
+    load_pair(0);
+    float M[kOutF4], Z[kOutF4];
+#pragma unroll
+    for (int i = 0; i < kOutF4; ++i) {
+      M[i] = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kPair; ++u)
+        if (u < ns[i]) M[i] = fmaxf(M[i], lv[u][i]);
+    }
+    for (int k = kPair; k < nsmax; k += kPair) {  // M over the remaining items (lse only)
+      float lm[kPair][kOutF4];
+#pragma unroll
+      for (int u = 0; u < kPair; ++u)
+#pragma unroll
+        for (int i = 0; i < kOutF4; ++i) lm[u][i] = k + u < ns[i] ? lse_part[prow(i, k + u)] : -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kOutF4; ++i)
+#pragma unroll
+        for (int u = 0; u < kPair; ++u)
+          if (k + u < ns[i]) M[i] = fmaxf(M[i], lm[u][i]);
+    }
+    auto accumulate = [&](int k, const float4_t (&xs)[kPair][kOutF4], const float (&ls)[kPair][kOutF4]) {
+#pragma unroll
+      for (int i = 0; i < kOutF4; ++i)
+#pragma unroll
+        for (int u = 0; u < kPair; ++u) {
+          if (k + u >= ns[i]) continue;
+          const float wgt = expf(ls[u][i] - M[i]);
+          Z[i] += wgt;
+          v[i][0] = fmaf(wgt, xs[u][i][0], v[i][0]);
+          v[i][1] = fmaf(wgt, xs[u][i][1], v[i][1]);
+          v[i][2] = fmaf(wgt, xs[u][i][2], v[i][2]);
+          v[i][3] = fmaf(wgt, xs[u][i][3], v[i][3]);
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < kOutF4; ++i) {
+      Z[i] = 0.f;
+      v[i] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    accumulate(0, x, lv);
+    for (int k = kPair; k < nsmax; k += kPair) {  // weighted sum of the remaining items
+      load_pair(k);
+      accumulate(k, x, lv);
     }
 #pragma unroll
     for (int i = 0; i < kOutF4; ++i) {
       const int rl = rl0 + 4 * i;
-      auto lse_of = [&](int k) -> float {
-        return k < kPre ? lv[k < kPre ? k : 0][i]
-                        : lse_part[(static_cast<int64_t>(s0[i] + k) * q_len + tq[i]) * H + h];
-      };
-      float M = -INFINITY;
-      for (int k = 0; k < ns[i]; ++k) M = fmaxf(M, lse_of(k));
-      float Z = 0.f;
-      float4_t acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k = 0; k < ns[i]; ++k) {
-        const float wgt = expf(lse_of(k) - M);
-        Z += wgt;
-        const float4_t xv =
-            k < kPre ? x[k < kPre ? k : 0][i]
-                     : *reinterpret_cast<const float4_t*>(
-                           o_part + ((static_cast<int64_t>(s0[i] + k) * q_len + tq[i]) * H + h) * kDc + c4);
-        acc[0] = fmaf(wgt, xv[0], acc[0]);
-        acc[1] = fmaf(wgt, xv[1], acc[1]);
-        acc[2] = fmaf(wgt, xv[2], acc[2]);
-        acc[3] = fmaf(wgt, xv[3], acc[3]);
-      }
-      v[i] = float4_t{0.f, 0.f, 0.f, 0.f};
       if (rl < nr) {
-        const float inv = 1.f / Z;
-        acc[0] *= inv;
-        acc[1] *= inv;
-        acc[2] *= inv;
-        acc[3] *= inv;
-        v[i] = acc;
+        const float inv = 1.f / Z[i];
+        v[i][0] *= inv;
+        v[i][1] *= inv;
+        v[i][2] *= inv;
+        v[i][3] *= inv;
         const int64_t ro = static_cast<int64_t>(r0 + rl) * H + h;
-        if (o_lat) *reinterpret_cast<float4_t*>(o_lat + ro * kDc + c4) = acc;
-        if (lse_out && c4 == 0) lse_out[ro] = M + logf(Z);
+        if (o_lat) *reinterpret_cast<float4_t*>(o_lat + ro * kDc + c4) = v[i];
+        if (lse_out && c4 == 0) lse_out[ro] = M[i] + logf(Z[i]);
+      } else {
+        v[i] = float4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
   } else {
