@@ -260,6 +260,8 @@ def main():
                     help="also time a T-token prefill of the first --prefill-batch sequences, "
                          "materialised-K/V path and absorbed path")
     ap.add_argument("--prefill-batch", type=int, default=4)
+    ap.add_argument("--graph", action="store_true",
+                    help="replay a HIP graph of each step's launches instead of launching them one by one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -341,45 +343,50 @@ def main():
 
     def launches_for(L):
         absorb = lambda: mla.absorb_q(dims, L["q_nope"], L["q_pe"], positions, L["w_uk"],  # noqa: E731
-                                      bufs["q_abs"], stream)
+                                      bufs["q_abs"], cur())
         if T > 1 and args.unfused:
             names = ["absorb_q", "decode_splitkv_multi", "combine_multi", "out_proj"]
             fns = [absorb,
                    lambda: mla.decode_splitkv_multi(dims, q4, L["cache"], block_table, seq_lens, items,
-                                                    bufs["o_part"], bufs["lse_part"], stream),
+                                                    bufs["o_part"], bufs["lse_part"], cur()),
                    lambda: mla.combine_multi(dims, offs, bufs["o_part"], bufs["lse_part"], B, ol4,
-                                             lse3, stream),
-                   lambda: mla.out_proj(dims, bufs["o_latent"], L["w_uv"], bufs["out"], stream)]
+                                             lse3, cur()),
+                   lambda: mla.out_proj(dims, bufs["o_latent"], L["w_uv"], bufs["out"], cur())]
         elif T > 1:
             names = ["absorb_q", "decode_splitkv_multi", "combine_out_proj"]
             fns = [absorb,
                    lambda: mla.decode_splitkv_multi(dims, q4, L["cache"], block_table, seq_lens, items,
-                                                    bufs["o_part"], bufs["lse_part"], stream),
+                                                    bufs["o_part"], bufs["lse_part"], cur()),
                    lambda: mla.combine_out_proj(dims, offs, bufs["o_part"], bufs["lse_part"],
-                                                L["w_uv"], B, out4, stream=stream)]
+                                                L["w_uv"], B, out4, stream=cur())]
         elif args.merged:
             names = ["absorb_q", "decode_merged", "out_proj"]
             fns = [absorb,
                    lambda: mla.decode_merged(dims, bufs["q_abs"], L["cache"], block_table, seq_lens,
                                              items, offs, bufs["tickets"], bufs["o_part"],
-                                             bufs["lse_part"], bufs["o_latent"], bufs["lse"], stream),
-                   lambda: mla.out_proj(dims, bufs["o_latent"], L["w_uv"], bufs["out"], stream)]
+                                             bufs["lse_part"], bufs["o_latent"], bufs["lse"], cur()),
+                   lambda: mla.out_proj(dims, bufs["o_latent"], L["w_uv"], bufs["out"], cur())]
         elif args.unfused:
             names = ["absorb_q", "decode_splitkv", "combine", "out_proj"]
             fns = [absorb,
                    lambda: mla.decode_splitkv(dims, bufs["q_abs"], L["cache"], block_table, seq_lens,
-                                              items, bufs["o_part"], bufs["lse_part"], stream),
+                                              items, bufs["o_part"], bufs["lse_part"], cur()),
                    lambda: mla.combine(dims, offs, bufs["o_part"], bufs["lse_part"], B,
-                                       bufs["o_latent"], bufs["lse"], stream),
-                   lambda: mla.out_proj(dims, bufs["o_latent"], L["w_uv"], bufs["out"], stream)]
+                                       bufs["o_latent"], bufs["lse"], cur()),
+                   lambda: mla.out_proj(dims, bufs["o_latent"], L["w_uv"], bufs["out"], cur())]
         else:
             names = ["absorb_q", "decode_splitkv", "combine_out_proj"]
             fns = [absorb,
                    lambda: mla.decode_splitkv(dims, bufs["q_abs"], L["cache"], block_table, seq_lens,
-                                              items, bufs["o_part"], bufs["lse_part"], stream),
+                                              items, bufs["o_part"], bufs["lse_part"], cur()),
                    lambda: mla.combine_out_proj(dims, offs, bufs["o_part"], bufs["lse_part"],
-                                                L["w_uv"], B, bufs["out"], stream=stream)]
+                                                L["w_uv"], B, bufs["out"], stream=cur())]
         return names, fns
+
+    def cur():
+        # the stream torch makes current: `stream` when eager, the capture
+        # stream while a graph is being recorded
+        return torch.cuda.current_stream()
 
     per_layer = [launches_for(L) for L in layers]
     names = per_layer[0][0]
@@ -393,7 +400,12 @@ def main():
         if flush is not None:
             torch.sum(flush, dim=0, keepdim=True, out=sink)
 
+    graphs = None
+
     def step(k, ev=None):
+        if ev is None and graphs is not None:
+            graphs[k % n_layers].replay()
+            return
         fns = per_layer[k % n_layers][1]
         for i, launch in enumerate(fns):
             if ev is not None:
@@ -411,6 +423,21 @@ def main():
         evict()
         step(k)
     torch.cuda.synchronize()
+    if args.graph:
+        # one graph per layer: the step's launches, recorded once and replayed
+        # (the kernels and their arguments are those of the eager step)
+        graphs = []
+        for _, fns in per_layer:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for launch in fns:
+                    launch()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for k in range(2):
+            evict()
+            step(k)
+        torch.cuda.synchronize()
     k0 = args.warmup   # the first timed step uses the layer the last warmup step did not
 
     # Timed region: K steps.
@@ -494,7 +521,8 @@ def main():
                    "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "page_size": cfg.page_size,
                    "work_items": int(len(items_h)), "q_len": T, "decode_entry": names[1],
                    "timing": ("per-step events, 512 MiB read flush before each step" if args.flush
-                              else f"back to back, cycling over {n_layers} layers' inputs")},
+                              else f"back to back, cycling over {n_layers} layers' inputs")
+                             + ("; step replayed as a HIP graph" if args.graph else "")},
         "latent_cache_GBps": round(work["cache_bytes"] / (ms * 1e-3) / 1e9, 1),
         "tokens_per_s": round(B * T / (ms * 1e-3), 1),
         "kernel_ms": {n: round(float(v), 5) for n, v in zip(names, k_ms)},

@@ -183,13 +183,13 @@ __global__ __launch_bounds__(256) void absorb_kernel(
 
 // ---------------------------------------------------------------------------
 // out_proj: o^T[128 x r] = W^UV_h[128 x 512] . o~^T[512 x r], one workgroup of
-// eight waves per (head, 32 query rows).  Blocks (h, group) and (h, group')
-// run on one XCD (grid x = heads, a multiple of 8), so W^UV_h comes from HBM
-// once and from that XCD's L2 for the other groups.  The float32 o~ of the
-// 32 rows is staged once in LDS as bf16 hi + lo (lo = bf16(x - hi)), rows of
+// eight waves per (head, kOutRows = 32 or 16 query rows).  Blocks (h, group)
+// and (h, group') run on one XCD (grid x = heads, a multiple of 8), so W^UV_h
+// comes from HBM once and from that XCD's L2 for the other groups.  The
+// float32 o~ of the rows is staged once in LDS as bf16 hi + lo (lo = bf16(x - hi)), rows of
 // 1 KiB with 16-byte chunk c at position c ^ 2 (r % 8): the B-operand reads
 // (16 rows x one chunk per quarter-wave) then hit distinct bank groups.  Wave
-// w owns output rows 16w .. 16w+15 for all 32 rows (two accumulators), its
+// w owns output rows 16w .. 16w+15 for all the rows (an accumulator per 16), its
 // W^UV rows read straight from global memory.
 //
 // With kMerge the workgroup first merges the split-KV partials of its rows
@@ -198,12 +198,9 @@ __global__ __launch_bounds__(256) void absorb_kernel(
 // also writes o~ and lse when those pointers are set.  Rows are query rows
 // r = b * q_len + t; item s holds row r's partial at s * q_len + t.
 // ---------------------------------------------------------------------------
-constexpr int kOutRows = 32;
-constexpr int kOutHalfBytes = kOutRows * kDc * 2;  // one bf16 copy of the staged o~
 constexpr int kOutThreads = 512;
-constexpr int kOutF4 = kOutRows * (kDc / 4) / kOutThreads;  // float4 per thread: 8
 
-template <bool kMerge>
+template <bool kMerge, int kOutRows = 32>
 __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, int q_len,
                                                                const int32_t* __restrict__ offs,
                                                                const float* __restrict__ o_part,
@@ -212,6 +209,9 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
                                                                float* __restrict__ lse_out,
                                                                const uint16_t* __restrict__ w_uv,
                                                                float* __restrict__ out) {
+  constexpr int kOutHalfBytes = kOutRows * kDc * 2;           // one bf16 copy of the staged o~
+  constexpr int kOutF4 = kOutRows * (kDc / 4) / kOutThreads;  // float4 per thread: 8 or 4
+  constexpr int kRowBlocks = kOutRows / 16;
   __shared__ __attribute__((aligned(16))) char lds[2 * kOutHalfBytes];  // [hi | lo][r][512]
   const int h = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(wrow + 32 * ks);
 
-  // thread t stages float4 column 4 (t % 128) of rows t / 128 + 4 i, i < 8
+  // thread t stages float4 column 4 (t % 128) of rows t / 128 + 4 i, i < kOutF4
   const int c4 = 4 * (threadIdx.x & 127);
   const int rl0 = threadIdx.x >> 7;
   float4_t v[kOutF4];
@@ -353,14 +353,14 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
   __syncthreads();
 
   // B operand: row 16bb + q, values 32ks + 8g .. +8 (chunk 4ks + g)
-  float4_t acc[2] = {};
+  float4_t acc[kRowBlocks] = {};
   const uint32_t brow = q * (kDc * 2);
   const int bsw = 2 * (q & 7);
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
     const uint32_t col = 16 * ((4 * ks + g) ^ bsw);
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
+    for (int bb = 0; bb < kRowBlocks; ++bb) {
       const uint32_t off = bb * 16 * (kDc * 2) + brow + col;
       const bf16x8 bh = *reinterpret_cast<const bf16x8*>(lds + off);
       const bf16x8 bl = *reinterpret_cast<const bf16x8*>(lds + kOutHalfBytes + off);
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
   }
   // lane holds o[r0 + 16bb + q][h][16w + 4g + i]
 #pragma unroll
-  for (int bb = 0; bb < 2; ++bb) {
+  for (int bb = 0; bb < kRowBlocks; ++bb) {
     const int rl = 16 * bb + q;
     if (rl < nr)
       *reinterpret_cast<float4_t*>(out + (static_cast<int64_t>(r0 + rl) * H + h) * kDh + 16 * w + 4 * g) = acc[bb];
@@ -395,9 +395,10 @@ hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const v
 
 hipError_t out_proj_fast(const mla_dims& d, int batch, const float* o_latent, const void* w_uv,
                          float* out, hipStream_t stream) {
+  constexpr int kOutRows = 32;
   const int groups = (batch + kOutRows - 1) / kOutRows;
   if (groups > 65535 || d.n_heads % 8 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(out_proj_kernel<false>, dim3(d.n_heads, groups), dim3(kOutThreads), 0, stream, batch,
+  hipLaunchKernelGGL((out_proj_kernel<false, kOutRows>), dim3(d.n_heads, groups), dim3(kOutThreads), 0, stream, batch,
                      d.n_heads, 1, nullptr, nullptr, nullptr, const_cast<float*>(o_latent), nullptr,
                      static_cast<const uint16_t*>(w_uv), out);
   return hipGetLastError();
@@ -407,11 +408,24 @@ hipError_t combine_out_proj_fast(const mla_dims& d, int batch, int q_len, const 
                                  const float* o_part, const float* lse_part, const void* w_uv,
                                  float* out, float* o_latent, float* lse, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(batch) * q_len;
-  const int64_t groups = (rows + kOutRows - 1) / kOutRows;
-  if (groups > 65535 || d.n_heads % 8 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(out_proj_kernel<true>, dim3(d.n_heads, static_cast<uint32_t>(groups)), dim3(kOutThreads),
-                     0, stream, static_cast<int>(rows), d.n_heads, q_len, split_offsets, o_part, lse_part,
-                     o_latent, lse, static_cast<const uint16_t*>(w_uv), out);
+  if (d.n_heads % 8 != 0) return hipErrorInvalidValue;
+  // 32 query rows per workgroup; 16 when that would leave most CUs idle (the
+  // merge reads every item's partial of its rows, so a workgroup's load time
+  // grows with its rows: at 16 heads x 32 rows, 16 workgroups took 26 us)
+  const int64_t groups32 = (rows + 31) / 32;
+  const bool small = d.n_heads * groups32 < 128;
+  const int R = small ? 16 : 32;
+  const int64_t groups = (rows + R - 1) / R;
+  if (groups > 65535) return hipErrorInvalidValue;
+  const dim3 grid(d.n_heads, static_cast<uint32_t>(groups));
+  if (small)
+    hipLaunchKernelGGL((out_proj_kernel<true, 16>), grid, dim3(kOutThreads), 0, stream, static_cast<int>(rows),
+                       d.n_heads, q_len, split_offsets, o_part, lse_part, o_latent, lse,
+                       static_cast<const uint16_t*>(w_uv), out);
+  else
+    hipLaunchKernelGGL((out_proj_kernel<true, 32>), grid, dim3(kOutThreads), 0, stream, static_cast<int>(rows),
+                       d.n_heads, q_len, split_offsets, o_part, lse_part, o_latent, lse,
+                       static_cast<const uint16_t*>(w_uv), out);
   return hipGetLastError();
 }
 
