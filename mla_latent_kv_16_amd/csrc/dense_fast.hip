@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(
 
 // ---------------------------------------------------------------------------
 // out_proj: o^T[128 x r] = W^UV_h[128 x 512] . o~^T[512 x r], one workgroup of
-// eight waves per (head, kOutRows = 32 or 16 query rows).  Blocks (h, group)
+// eight waves per (head, kOutRows = 32, 16 or 8 query rows).  Blocks (h, group)
 // and (h, group') run on one XCD (grid x = heads, a multiple of 8), so W^UV_h
 // comes from HBM once and from that XCD's L2 for the other groups.  The
 // float32 o~ of the rows is staged once in LDS as bf16 hi + lo (lo = bf16(x - hi)), rows of
@@ -209,9 +209,11 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
                                                                float* __restrict__ lse_out,
                                                                const uint16_t* __restrict__ w_uv,
                                                                float* __restrict__ out) {
-  constexpr int kOutHalfBytes = kOutRows * kDc * 2;           // one bf16 copy of the staged o~
-  constexpr int kOutF4 = kOutRows * (kDc / 4) / kOutThreads;  // float4 per thread: 8 or 4
-  constexpr int kRowBlocks = kOutRows / 16;
+  constexpr int kRowBlocks = kOutRows >= 16 ? kOutRows / 16 : 1;
+  // one bf16 copy of the staged o~; at 8 rows the MFMA's 16-row block also
+  // reads rows 8..15, whose outputs are dropped
+  constexpr int kOutHalfBytes = 16 * kRowBlocks * kDc * 2;
+  constexpr int kOutF4 = kOutRows * (kDc / 4) / kOutThreads;  // float4 per thread: 8, 4 or 2
   __shared__ __attribute__((aligned(16))) char lds[2 * kOutHalfBytes];  // [hi | lo][r][512]
   const int h = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -228,18 +230,23 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
 
   // thread t stages float4 column 4 (t % 128) of rows t / 128 + 4 i, i < kOutF4
   const int c4 = 4 * (threadIdx.x & 127);
-  const int rl0 = threadIdx.x >> 7;
+  const int rl0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7);  // the same for a whole wave
   float4_t v[kOutF4];
   if constexpr (kMerge) {
     // Row rl = rl0 + 4i has items s0[i] .. s0[i] + ns[i] - 1 (the same for
-    // every lane of a wave).  Items go two at a time with the loads of all
-    // eight rows in flight together: the partials and lse of the first two are
-    // loaded before anything waits; a first pass takes M over the lse of the
-    // rest, a second forms Z and the weighted sum.  Each row's arithmetic is
+    // every lane of a wave).  Items go kPair at a time (fewer rows per
+    // thread, more items) with the loads of all the thread's rows in flight
+    // together: the partials and lse of the first kPair are loaded before
+    // anything waits; a first pass takes M over the lse of the rest, a
+    // second forms Z and the weighted sum.  Each row's arithmetic is
     // the combine's, in item order, so every thread of a row computes the same
     // M and Z and o~ matches mla_combine bit for bit.
-    constexpr int kPair = 2;
-    int s0[kOutF4], ns[kOutF4], tq[kOutF4];
+    // Loads are unconditional (a row past the end, or an item past a row's
+    // last, reads the row's last item and the value is then replaced), so no
+    // branch separates them and all of them are in flight together; the
+    // planner gives every sequence at least one item.
+    constexpr int kPair = 16 / kOutF4;  // items per load round: 2, 4 or 8
+    int s0[kOutF4], ns[kOutF4], nv[kOutF4], tq[kOutF4];
     int nsmax = 0;
 #pragma unroll
     for (int i = 0; i < kOutF4; ++i) {
@@ -248,11 +255,13 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
       const int b = r / q_len;
       tq[i] = r % q_len;
       s0[i] = offs[b];
-      ns[i] = rl < nr ? offs[b + 1] - s0[i] : 0;
+      nv[i] = offs[b + 1] - s0[i];
+      ns[i] = rl < nr ? nv[i] : 0;
       nsmax = max(nsmax, ns[i]);
     }
-    auto prow = [&](int i, int k) -> int64_t {
-      return (static_cast<int64_t>(s0[i] + k) * q_len + tq[i]) * H + h;
+    auto prow = [&](int i, int k) -> int64_t {  // row of item min(k, last) of row i
+      const int kk = max(0, min(k, nv[i] - 1));
+      return (static_cast<int64_t>(s0[i] + kk) * q_len + tq[i]) * H + h;
     };
     float4_t x[kPair][kOutF4];
     float lv[kPair][kOutF4];
@@ -262,9 +271,10 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
 #pragma unroll
         for (int i = 0; i < kOutF4; ++i) {
           const bool ok = k + u < ns[i];
-          x[u][i] = ok ? *reinterpret_cast<const float4_t*>(o_part + prow(i, k + u) * kDc + c4)
-                       : float4_t{0.f, 0.f, 0.f, 0.f};
-          lv[u][i] = ok ? lse_part[prow(i, k + u)] : -INFINITY;
+          const float4_t xv = *reinterpret_cast<const float4_t*>(o_part + prow(i, k + u) * kDc + c4);
+          const float l = lse_part[prow(i, k + u)];
+          x[u][i] = ok ? xv : float4_t{0.f, 0.f, 0.f, 0.f};
+          lv[u][i] = ok ? l : -INFINITY;
         }
     };
     load_pair(0);
@@ -281,7 +291,10 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
 #pragma unroll
       for (int u = 0; u < kPair; ++u)
 #pragma unroll
-        for (int i = 0; i < kOutF4; ++i) lm[u][i] = k + u < ns[i] ? lse_part[prow(i, k + u)] : -INFINITY;
+        for (int i = 0; i < kOutF4; ++i) {
+          const float l = lse_part[prow(i, k + u)];
+          lm[u][i] = k + u < ns[i] ? l : -INFINITY;
+        }
 #pragma unroll
       for (int i = 0; i < kOutF4; ++i)
 #pragma unroll
@@ -409,23 +422,31 @@ hipError_t combine_out_proj_fast(const mla_dims& d, int batch, int q_len, const 
                                  float* out, float* o_latent, float* lse, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(batch) * q_len;
   if (d.n_heads % 8 != 0) return hipErrorInvalidValue;
-  // 32 query rows per workgroup; 16 when that would leave most CUs idle (the
-  // merge reads every item's partial of its rows, so a workgroup's load time
-  // grows with its rows: at 16 heads x 32 rows, 16 workgroups took 26 us)
-  const int64_t groups32 = (rows + 31) / 32;
-  const bool small = d.n_heads * groups32 < 128;
-  const int R = small ? 16 : 32;
+  // Query rows per workgroup: the largest of 32, 16, 8 that still gives
+  // 256 workgroups (one per CU), else 8.  A workgroup pulls every item's
+  // partial of its rows through one CU, so few large workgroups are slow: at
+  // 16 heads x 32 rows, 16 workgroups of 32 rows took 26 us.
+  int R = 8;
+  for (int cand : {32, 16}) {
+    if (d.n_heads * ((rows + cand - 1) / cand) >= 256) {
+      R = cand;
+      break;
+    }
+  }
   const int64_t groups = (rows + R - 1) / R;
   if (groups > 65535) return hipErrorInvalidValue;
   const dim3 grid(d.n_heads, static_cast<uint32_t>(groups));
-  if (small)
-    hipLaunchKernelGGL((out_proj_kernel<true, 16>), grid, dim3(kOutThreads), 0, stream, static_cast<int>(rows),
-                       d.n_heads, q_len, split_offsets, o_part, lse_part, o_latent, lse,
-                       static_cast<const uint16_t*>(w_uv), out);
+  const int nrows = static_cast<int>(rows);
+  const uint16_t* w = static_cast<const uint16_t*>(w_uv);
+  if (R == 32)
+    hipLaunchKernelGGL((out_proj_kernel<true, 32>), grid, dim3(kOutThreads), 0, stream, nrows, d.n_heads, q_len,
+                       split_offsets, o_part, lse_part, o_latent, lse, w, out);
+  else if (R == 16)
+    hipLaunchKernelGGL((out_proj_kernel<true, 16>), grid, dim3(kOutThreads), 0, stream, nrows, d.n_heads, q_len,
+                       split_offsets, o_part, lse_part, o_latent, lse, w, out);
   else
-    hipLaunchKernelGGL((out_proj_kernel<true, 32>), grid, dim3(kOutThreads), 0, stream, static_cast<int>(rows),
-                       d.n_heads, q_len, split_offsets, o_part, lse_part, o_latent, lse,
-                       static_cast<const uint16_t*>(w_uv), out);
+    hipLaunchKernelGGL((out_proj_kernel<true, 8>), grid, dim3(kOutThreads), 0, stream, nrows, d.n_heads, q_len,
+                       split_offsets, o_part, lse_part, o_latent, lse, w, out);
   return hipGetLastError();
 }
 

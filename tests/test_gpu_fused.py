@@ -4,8 +4,9 @@ Against the two separate calls on the same partials: o_latent and lse must be
 the same bits (the merge repeats the combine's arithmetic in its order) and
 out the same bits as mla_out_proj on that o_latent; with o_latent and lse left
 NULL, out must not change.  Covers 128 and 16 heads, many-split plans, more
-than 64 rows (two row groups), q_len > 1 and the fp32 generic shapes; at 16
-heads the workgroups take 16 rows each, including a ragged last group.
+than 64 rows (two row groups), q_len > 1 and the fp32 generic shapes, and
+each workgroup size the launch picks (32, 16 or 8 rows, with a ragged last
+group).
 """
 import numpy as np
 import pytest
@@ -45,6 +46,7 @@ def partials(wl, dev, slots, T):
     ("h128", small(V2, "f128", 6, permute_pages=True), [1, 64, 65, 777, 5000, 8205], 256, 1),
     ("h128_many_rows", small(V2, "f128b", 70, lens=(1, 3000), permute_pages=True), None, 2048, 1),
     ("h128_T3", small(V2, "f128c", 4, permute_pages=True), [3, 100, 4097, 9000], 2048, 3),
+    ("h128_rows20", small(V2, "f128d", 20, lens=(1, 2000), permute_pages=True), None, 512, 1),
     ("h16", small(LITE, "f16", 5, permute_pages=True), [1, 100, 4096, 4097, 700], 2048, 1),
     ("h16_T2_many_rows", small(LITE, "f16b", 40, lens=(2, 2000), permute_pages=True), None, 512, 2),
     ("h16_ragged_rows", small(LITE, "f16c", 21, lens=(1, 3000), permute_pages=True), None, 512, 1),
