@@ -80,57 +80,60 @@ __global__ __launch_bounds__(256) void absorb_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, q = lane & 15;
 
-  // stage W^UK_h[:, c0:c0+128]: LDS chunk p = row * 16 + pc holds chunk pc ^ tsw(row)
-  const char* wh = w_uk + static_cast<int64_t>(h) * kDh * (kDc * 2) + c0 * 2;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int p = (8 * w + i) * 64 + lane;
-    const int row = p >> 4, pc = p & 15;
-    dma16(wh, row * (kDc * 2) + 16 * (pc ^ tsw(row)), lds_base + (8 * w + i) * 1024);
-  }
-
   const int b0 = blockIdx.y * 64;
   const int nb = min(64, batch - b0);
-  // B operand: q^C of sequence b = b0 + 16w + q, values 32ks + 8g .. +8
-  // (loaded before the RoPE part so that both latencies overlap)
-  const int b = b0 + 16 * w + q;
-  const bool bvalid = b < batch;
+  // B operand: q^C of sequence b = b0 + 16w + q, values 32ks + 8g .. +8 (a
+  // clamped index past the batch; those columns are not stored)
+  const int b = min(b0 + 16 * w + q, batch - 1);
+  const uint16_t* qrow = q_nope + (static_cast<int64_t>(b) * H + h) * kDh + 8 * g;
   bf16x8 qn[4];
+  if (w < 2) {
+    // Waves 0 and 1 stage W^UK_h[:, c0:c0+128], rows 64w .. 64w+63: LDS chunk
+    // p = row * 16 + pc holds chunk pc ^ tsw(row).
+    const char* wh = w_uk + static_cast<int64_t>(h) * kDh * (kDc * 2) + c0 * 2;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    if (bvalid)
-      qn[ks] = *reinterpret_cast<const bf16x8*>(q_nope + (static_cast<int64_t>(b) * H + h) * kDh +
-                                                32 * ks + 8 * g);
-    else
-      qn[ks] = bf16x8{};
-  }
-  // RoPE part, float64 angle, float32 rotation.  The four quarter-workgroups
-  // of a head share the (sequence, pair) list; thread t keeps pair k = t % 32
-  // of sequences bi0 and bi0 + 32 (its loads issued before any math).
-  {
-    const int k = threadIdx.x & (kDr / 2 - 1);
-    const int bi0 = quarter * 8 + (threadIdx.x >> 5);
-    int pos[2];
-    uint32_t xy[2];
+    for (int i = 0; i < 16; ++i) {
+      const int p = (16 * w + i) * 64 + lane;
+      const int row = p >> 4, pc = p & 15;
+      dma16(wh, row * (kDc * 2) + 16 * (pc ^ tsw(row)), lds_base + (16 * w + i) * 1024);
+    }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int bi = bi0 + 32 * j;
+    for (int ks = 0; ks < 4; ++ks) qn[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+  } else {
+    // Waves 2 and 3: the RoPE part, float64 angle, float32 rotation, while the
+    // tile is in flight (the load counter is per wave, so waiting for these
+    // loads does not wait for the tile).  The four quarter-workgroups of a head
+    // share the (sequence, pair) list: thread t keeps pair k = t % 32 of four
+    // sequences.  Loads are unconditional, from a clamped sequence index, so
+    // that no branch forces a wait between them.
+    // (q^C first: the rotation's wait then covers it too, and no load of
+    // these waves is left pending where the two roles' code joins)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qn[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    const int t = threadIdx.x - 128;
+    const int k = t & (kDr / 2 - 1);
+    const int bi0 = quarter * 8 + (t >> 5);
+    constexpr int kPer = 4;
+    int pos[kPer];
+    uint32_t xy[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int bi = min(bi0 + 4 * (j & 1) + 32 * (j >> 1), nb - 1);
       const int64_t r = static_cast<int64_t>(b0 + bi) * H + h;
-      pos[j] = bi < nb ? positions[b0 + bi] : 0;
-      xy[j] = bi < nb ? *reinterpret_cast<const uint32_t*>(q_pe + r * kDr + 2 * k) : 0u;
+      pos[j] = positions[b0 + bi];
+      xy[j] = *reinterpret_cast<const uint32_t*>(q_pe + r * kDr + 2 * k);
     }
     const double theta = theta_k.t[k];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int bi = bi0 + 32 * j;
-      if (bi >= nb) continue;
+    for (int j = 0; j < kPer; ++j) {
+      const int bi = bi0 + 4 * (j & 1) + 32 * (j >> 1);
       float sn, c;
       sincos_reduced(static_cast<double>(pos[j]) * theta, sn, c);
       const int64_t r = static_cast<int64_t>(b0 + bi) * H + h;
       const float x0 = bf16_bits_to_f32(static_cast<uint16_t>(xy[j] & 0xffffu));
       const float x1 = bf16_bits_to_f32(static_cast<uint16_t>(xy[j] >> 16));
-      *reinterpret_cast<uint32_t*>(q_abs + r * kDq + kDc + 2 * k) =
-          pack_bf16x2(x0 * c - x1 * sn, x0 * sn + x1 * c);
+      const uint32_t y = pack_bf16x2(x0 * c - x1 * sn, x0 * sn + x1 * c);
+      if (bi < nb) *reinterpret_cast<uint32_t*>(q_abs + r * kDq + kDc + 2 * k) = y;
     }
   }
 
