@@ -262,6 +262,9 @@ def main():
     ap.add_argument("--prefill-batch", type=int, default=4)
     ap.add_argument("--graph", action="store_true",
                     help="replay a HIP graph of each step's launches instead of launching them one by one")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="before the warm-up steps, keep the GPU (and this process) busy this long "
+                         "with the flush kernel: out of idle, the first steps run up to 10%% slower")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -401,16 +404,20 @@ def main():
             torch.sum(flush, dim=0, keepdim=True, out=sink)
 
     graphs = None
+    recorded = None   # per layer, per kernel: the library calls, marshalled once
 
     def step(k, ev=None):
         if ev is None and graphs is not None:
             graphs[k % n_layers].replay()
             return
-        fns = per_layer[k % n_layers][1]
-        for i, launch in enumerate(fns):
+        launches = recorded[k % n_layers] if recorded is not None else per_layer[k % n_layers][1]
+        for i, launch in enumerate(launches):
             if ev is not None:
                 ev[i].record(stream)
-            launch()
+            if recorded is not None:
+                mla.replay_calls(launch)
+            else:
+                launch()
         if ev is not None:
             ev[n_k].record(stream)
 
@@ -419,10 +426,28 @@ def main():
             return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         return [HipTimingEvent() for _ in range(n)]
 
+    if args.settle_ms > 0:
+        t_s = time.perf_counter()
+        while (time.perf_counter() - t_s) * 1e3 < args.settle_ms:
+            for _ in range(8):
+                evict()
+            torch.cuda.synchronize()
     for k in range(args.warmup):
         evict()
         step(k)
     torch.cuda.synchronize()
+    # The timed passes issue the same library calls with their arguments
+    # marshalled once (the binding's checks ran in the warm-up): a step's
+    # host-side cost then stays well below its GPU time, so the kernels run
+    # back to back instead of waiting for their launches.
+    recorded = []
+    for _, fns in per_layer:
+        per_kernel = []
+        for launch in fns:
+            with mla.record_calls() as calls:
+                launch()
+            per_kernel.append(calls)
+        recorded.append(per_kernel)
     if args.graph:
         # one graph per layer: the step's launches, recorded once and replayed
         # (the kernels and their arguments are those of the eager step)
@@ -475,7 +500,7 @@ def main():
     k_ms = t.mean(axis=0)
 
     # The decode kernel alone, K launches back to back (cycling over the layers).
-    dec = [fns[1] for _, fns in per_layer]
+    dec = [(lambda c=calls[1]: mla.replay_calls(c)) for calls in recorded]
     if args.flush:
         d_ev = [new_events(2) for _ in range(args.steps)]
         for k in range(args.steps):
@@ -522,6 +547,8 @@ def main():
                    "work_items": int(len(items_h)), "q_len": T, "decode_entry": names[1],
                    "timing": ("per-step events, 512 MiB read flush before each step" if args.flush
                               else f"back to back, cycling over {n_layers} layers' inputs")
+                             + (f"; {args.settle_ms:g} ms of the flush kernel before the warm-up"
+                                if args.settle_ms > 0 else "")
                              + ("; step replayed as a HIP graph" if args.graph else "")},
         "latent_cache_GBps": round(work["cache_bytes"] / (ms * 1e-3) / 1e9, 1),
         "tokens_per_s": round(B * T / (ms * 1e-3), 1),

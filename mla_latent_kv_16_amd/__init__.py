@@ -12,6 +12,7 @@ plus `decode_step`, which runs the four device steps in order.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -22,7 +23,8 @@ import numpy as np
 __all__ = ["MlaError", "Dims", "load", "lib_path", "absorb_q", "plan_splits", "decode_splitkv",
            "decode_merged", "append_kv", "decode_splitkv_multi", "combine_multi", "combine_out_proj",
            "prefill_naive",
-           "combine", "out_proj", "decode_step", "fast_path", "version", "BF16", "F32"]
+           "combine", "out_proj", "decode_step", "fast_path", "version", "record_calls", "replay_calls",
+           "BF16", "F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 BF16, F32 = 0, 1
@@ -120,6 +122,43 @@ def load():
     return L
 
 
+_recording = None  # a list while record_calls() is active
+
+
+def _launch(name: str, *args):
+    """Issue one enqueueing library call (or, inside record_calls(), keep it)."""
+    f = getattr(load(), name)
+    if _recording is not None:
+        _recording.append((f, args, name))
+        return
+    _check(f(*args), name)
+
+
+@contextlib.contextmanager
+def record_calls():
+    """Inside the block the enqueueing functions below marshal and check their
+    arguments as usual but do not call the library; the yielded list then
+    holds the calls, with their arguments (device pointers, sizes and the
+    stream, fixed at this point), for replay_calls().  For callers that
+    enqueue the same work on the same buffers many times and want to skip
+    the per-call marshalling."""
+    global _recording
+    if _recording is not None:
+        raise RuntimeError("record_calls() does not nest")
+    calls = []
+    _recording = calls
+    try:
+        yield calls
+    finally:
+        _recording = None
+
+
+def replay_calls(calls):
+    """Issue recorded calls again, in order, checking every status."""
+    for f, args, name in calls:
+        _check(f(*args), name)
+
+
 def _check(status: int, where: str):
     if status != 0:
         detail = ""
@@ -178,12 +217,12 @@ def absorb_q(dims: Dims, q_nope, q_pe, positions, w_uk, q_abs=None, stream=None)
     H = dims.n_heads
     if q_abs is None:
         q_abs = torch.empty((B, H, dims.row), dtype=dt, device=q_nope.device)
-    _check(load().mla_absorb_q(
+    _launch("mla_absorb_q",
         ctypes.byref(dims.c()), B,
         _ptr(q_nope, dt, (B, H, dims.d_head), "q_nope"), _ptr(q_pe, dt, (B, H, dims.d_rope), "q_pe"),
         _ptr(positions, torch.int32, (B,), "positions"),
         _ptr(w_uk, dt, (H * dims.d_head, dims.d_latent), "w_uk"),
-        _ptr(q_abs, dt, (B, H, dims.row), "q_abs"), _stream(stream)), "mla_absorb_q")
+        _ptr(q_abs, dt, (B, H, dims.row), "q_abs"), _stream(stream))
     return q_abs
 
 
@@ -219,13 +258,13 @@ def decode_splitkv(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items,
     if lse_part is None:
         lse_part = torch.empty((W, H), dtype=torch.float32, device=dev)
     num_pages = kv_cache.shape[0]
-    _check(load().mla_decode_splitkv(
+    _launch("mla_decode_splitkv",
         ctypes.byref(dims.c()), B, _ptr(q_abs, dt, (B, H, dims.row), "q_abs"),
         _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
         _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
         _ptr(seq_lens, torch.int32, (B,), "seq_lens"), _ptr(items, torch.int32, (W, 4), "items"), W,
         _ptr(o_part, torch.float32, (W, H, dims.d_latent), "o_part"),
-        _ptr(lse_part, torch.float32, (W, H), "lse_part"), _stream(stream)), "mla_decode_splitkv")
+        _ptr(lse_part, torch.float32, (W, H), "lse_part"), _stream(stream))
     return o_part, lse_part
 
 
@@ -240,12 +279,12 @@ def combine(dims: Dims, split_offsets, o_part, lse_part, batch: int, o_latent=No
     if lse is None and want_lse:
         lse = torch.empty((batch, H), dtype=torch.float32, device=dev)
     W = o_part.shape[0]
-    _check(load().mla_combine(
+    _launch("mla_combine",
         ctypes.byref(dims.c()), batch, _ptr(split_offsets, torch.int32, (batch + 1,), "split_offsets"),
         _ptr(o_part, torch.float32, (W, H, dims.d_latent), "o_part"),
         _ptr(lse_part, torch.float32, (W, H), "lse_part"),
         _ptr(o_latent, torch.float32, (batch, H, dims.d_latent), "o_latent"),
-        _ptr(lse, torch.float32, (batch, H), "lse"), _stream(stream)), "mla_combine")
+        _ptr(lse, torch.float32, (batch, H), "lse"), _stream(stream))
     return o_latent, lse
 
 
@@ -264,14 +303,13 @@ def decode_splitkv_multi(dims: Dims, q_abs, kv_cache, block_table, seq_lens, ite
     if lse_part is None:
         lse_part = torch.empty((W, T, H), dtype=torch.float32, device=dev)
     num_pages = kv_cache.shape[0]
-    _check(load().mla_decode_splitkv_multi(
+    _launch("mla_decode_splitkv_multi",
         ctypes.byref(dims.c()), B, T, _ptr(q_abs, dt, (B, T, H, dims.row), "q_abs"),
         _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
         _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
         _ptr(seq_lens, torch.int32, (B,), "seq_lens"), _ptr(items, torch.int32, (W, 4), "items"), W,
         _ptr(o_part, torch.float32, (W, T, H, dims.d_latent), "o_part"),
-        _ptr(lse_part, torch.float32, (W, T, H), "lse_part"), _stream(stream)),
-        "mla_decode_splitkv_multi")
+        _ptr(lse_part, torch.float32, (W, T, H), "lse_part"), _stream(stream))
     return o_part, lse_part
 
 
@@ -286,13 +324,13 @@ def combine_multi(dims: Dims, split_offsets, o_part, lse_part, batch: int, o_lat
         o_latent = torch.empty((batch, T, H, dims.d_latent), dtype=torch.float32, device=dev)
     if lse is None and want_lse:
         lse = torch.empty((batch, T, H), dtype=torch.float32, device=dev)
-    _check(load().mla_combine_multi(
+    _launch("mla_combine_multi",
         ctypes.byref(dims.c()), batch, T,
         _ptr(split_offsets, torch.int32, (batch + 1,), "split_offsets"),
         _ptr(o_part, torch.float32, (W, T, H, dims.d_latent), "o_part"),
         _ptr(lse_part, torch.float32, (W, T, H), "lse_part"),
         _ptr(o_latent, torch.float32, (batch, T, H, dims.d_latent), "o_latent"),
-        _ptr(lse, torch.float32, (batch, T, H), "lse"), _stream(stream)), "mla_combine_multi")
+        _ptr(lse, torch.float32, (batch, T, H), "lse"), _stream(stream))
     return o_latent, lse
 
 
@@ -317,7 +355,7 @@ def decode_merged(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items, spl
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     num_pages = kv_cache.shape[0]
-    _check(load().mla_decode_merged(
+    _launch("mla_decode_merged",
         ctypes.byref(dims.c()), B, _ptr(q_abs, dt, (B, H, dims.row), "q_abs"),
         _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
         _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
@@ -327,7 +365,7 @@ def decode_merged(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items, spl
         _ptr(lse_part, torch.float32, (W, H), "lse_part"),
         _ptr(tickets, torch.int32, (2 * B,), "tickets"),
         _ptr(o_latent, torch.float32, (B, H, dims.d_latent), "o_latent"),
-        _ptr(lse, torch.float32, (B, H), "lse"), _stream(stream)), "mla_decode_merged")
+        _ptr(lse, torch.float32, (B, H), "lse"), _stream(stream))
     return o_latent, lse
 
 
@@ -362,10 +400,10 @@ def out_proj(dims: Dims, o_latent, w_uv, out=None, stream=None):
     dt = _store_dtype(dims)
     if out is None:
         out = torch.empty((B, H, dims.d_head), dtype=torch.float32, device=o_latent.device)
-    _check(load().mla_out_proj(
+    _launch("mla_out_proj",
         ctypes.byref(dims.c()), B, _ptr(o_latent, torch.float32, (B, H, dims.d_latent), "o_latent"),
         _ptr(w_uv, dt, (H * dims.d_head, dims.d_latent), "w_uv"),
-        _ptr(out, torch.float32, (B, H, dims.d_head), "out"), _stream(stream)), "mla_out_proj")
+        _ptr(out, torch.float32, (B, H, dims.d_head), "out"), _stream(stream))
     return out
 
 
@@ -386,7 +424,7 @@ def combine_out_proj(dims: Dims, split_offsets, o_part, lse_part, w_uv, batch: i
     lead = (batch, T) if multi else (batch,)
     if out is None:
         out = torch.empty((*lead, H, dims.d_head), dtype=torch.float32, device=o_part.device)
-    _check(load().mla_combine_out_proj(
+    _launch("mla_combine_out_proj",
         ctypes.byref(dims.c()), batch, T,
         _ptr(split_offsets, torch.int32, (batch + 1,), "split_offsets"),
         _ptr(o_part, torch.float32, (W, *lead[1:], H, dims.d_latent), "o_part"),
@@ -394,7 +432,7 @@ def combine_out_proj(dims: Dims, split_offsets, o_part, lse_part, w_uv, batch: i
         _ptr(w_uv, dt, (H * dims.d_head, dims.d_latent), "w_uv"),
         _ptr(out, torch.float32, (*lead, H, dims.d_head), "out"),
         _ptr(o_latent, torch.float32, (*lead, H, dims.d_latent), "o_latent"),
-        _ptr(lse, torch.float32, (*lead, H), "lse"), _stream(stream)), "mla_combine_out_proj")
+        _ptr(lse, torch.float32, (*lead, H), "lse"), _stream(stream))
     return out
 
 

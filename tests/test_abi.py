@@ -248,3 +248,15 @@ def test_plan_rejects_bad_arguments(lib):
     assert lib.mla_plan_max_items(_d(), 3, lens.ctypes.data_as(pi32)) == 3
     lens[1] = -1
     assert lib.mla_plan_max_items(_d(), 3, lens.ctypes.data_as(pi32)) == -1
+
+
+def test_record_calls_does_not_nest():
+    import mla_latent_kv_16_amd as mla
+    with mla.record_calls() as calls:
+        assert calls == []
+        with pytest.raises(RuntimeError):
+            with mla.record_calls():
+                pass
+    # the outer block ended cleanly: a new recording starts empty
+    with mla.record_calls() as again:
+        assert again == []

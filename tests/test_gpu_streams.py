@@ -98,3 +98,23 @@ def test_graph_replays_match_eager(gpu_lib):
         ref = bufs["out"].cpu().numpy()
         assert np.all(np.isfinite(got)), f"replay {r}: non-finite"
         assert np.array_equal(got, ref), f"replay {r} differs from the eager step"
+
+
+def test_recorded_calls_replay(gpu_lib):
+    """record_calls() keeps the step's library calls (arguments marshalled once);
+    replaying them gives the bits of the step issued through the binding."""
+    import torch
+    say("[streams: recorded calls]")
+    wl, dev, dims, bufs = _setup()
+    _step(dims, dev, bufs)
+    torch.cuda.synchronize()
+    ref = bufs["out"].cpu().numpy().copy()
+    with mla.record_calls() as calls:
+        _step(dims, dev, bufs)   # nothing is enqueued here
+    assert [name for _, _, name in calls] == ["mla_absorb_q", "mla_decode_splitkv", "mla_combine_out_proj"]
+    bufs["out"].fill_(float("nan"))
+    torch.cuda.synchronize()
+    for _ in range(2):
+        mla.replay_calls(calls)
+    torch.cuda.synchronize()
+    assert np.array_equal(bufs["out"].cpu().numpy(), ref)
