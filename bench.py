@@ -12,14 +12,16 @@ W^UV on B*T rows.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--merged | --unfused]
                     [--q-len T] [--slots N] [--back-to-back] [--prefill T [--prefill-batch B]]
-                    [--fenced-events] [--no-cpu-baseline] [--copy-probe]
+                    [--settle-ms MS] [--graph] [--fenced-events] [--no-cpu-baseline]
+                    [--copy-probe]
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
 Timing.  Before every step a 512 MiB buffer is read (a reduction, untimed), so
 the 256 MB last-level cache holds other data and the step reads its cache rows
 from HBM; each step is timed between two HIP events recorded at its
-boundaries, and ms_per_step is their mean.  (The flush reads rather than
+boundaries, and ms_per_step is their mean (the JSON line also gives p10,
+median and p90).  (The flush reads rather than
 writes so that the step does not also pay for writing back dirty lines.)  A
 second pass with an event between every two kernels gives the per-kernel
 breakdown (each event adds a few microseconds, so it sums to more than the
@@ -36,6 +38,12 @@ under continuous decode.  All events are recorded on the stream the kernels
 run on.  They are HIP events created with hipEventDisableSystemFence (timing
 only: recording one does not write back and invalidate the caches);
 --fenced-events uses torch.cuda.Event instead.
+
+Before the warm-up the flush kernel runs for --settle-ms (100 ms): straight
+out of idle the first steps run up to 10% slower.  The timed passes issue the
+library calls recorded once per layer after the warm-up (mla.record_calls),
+so that the host's per-step cost stays below the GPU's and the kernels of a
+step run back to back.  --graph replays a HIP graph of the step instead.
 """
 
 from __future__ import annotations
@@ -241,8 +249,8 @@ def time_prefill(args, cfg, wl, dims, L0, block_table, seq_lens, stream, new_eve
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="v2_b64_l8192")
     ap.add_argument("--back-to-back", action="store_true",
                     help="no flush: steps back to back over several layers' inputs, two events")
@@ -477,6 +485,9 @@ def main():
             step_ev[k][1].record(stream)
         torch.cuda.synchronize()
         step_ms = np.array([e[0].elapsed_time(e[1]) for e in step_ev])
+        pct = {"step_ms_p10": round(float(np.percentile(step_ms, 10)), 5),
+               "step_ms_median": round(float(np.median(step_ms)), 5),
+               "step_ms_p90": round(float(np.percentile(step_ms, 90)), 5)}
         ms = float(step_ms.mean())
         spread = f"p10 {np.percentile(step_ms, 10):.4f}  p90 {np.percentile(step_ms, 90):.4f}"
     else:
@@ -488,6 +499,7 @@ def main():
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / args.steps
         spread = f"{args.steps} steps back to back"
+        pct = {}
     wall = time.perf_counter() - w0
 
     # Per-kernel breakdown: the same steps with an event between every two kernels.
@@ -536,6 +548,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        **pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
