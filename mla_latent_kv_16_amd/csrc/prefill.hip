@@ -18,8 +18,9 @@
 //    wave at a time: D^T[128 x 16 rows] = W_i[128 x 512] . c^T[512 x 16 rows]
 //    with v_mfma_f32_16x16x32_bf16, the latent rows read straight from the
 //    paged cache, float32 accumulation rounded to bf16.
-//  * attention: one workgroup of four waves per (64 query tokens, head,
-//    sequence), one wave per 16 queries; keys in tiles of 32 staged in LDS for
+//  * attention: one workgroup of four waves per (128 query tokens, head,
+//    sequence), one wave per 32 queries (two blocks of 16, so that every K or
+//    V fragment read from LDS feeds two MFMAs); keys in tiles of 32 staged in LDS for
 //    all four waves (K row-major, V transposed), with an online softmax in base
 //    2: S^T[16 keys x 16 queries] on MFMA (K rows as A, the query tile as B, 6
 //    steps over the 192 dimensions), then O^T[128 x 16 queries] += V^T . P^T
@@ -33,7 +34,8 @@
 namespace mla {
 namespace {
 
-constexpr int kQTile = 16;     // query tokens per attention wave
+constexpr int kQB = 2;             // 16-query blocks per attention wave
+constexpr int kQWave = 16 * kQB;   // query tokens per attention wave
 constexpr int kKeyTile = 32;   // keys per attention iteration
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr float kLn2F = 0.6931471805599453f;
@@ -136,7 +138,7 @@ __device__ __forceinline__ uint64_t lds_tr4(const char* lds, uint32_t off) {
   return __builtin_bit_cast(uint64_t, v);
 }
 
-__global__ __launch_bounds__(64 * kAttnWaves) void prefill_attn_kernel(
+__global__ __launch_bounds__(64 * kAttnWaves, 2) void prefill_attn_kernel(
     int H, int q_len, int max_rows, float scale, PrefillTheta theta,
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const uint16_t* __restrict__ cache, const int32_t* __restrict__ block_table, int max_pages,
@@ -149,21 +151,30 @@ __global__ __launch_bounds__(64 * kAttnWaves) void prefill_attn_kernel(
   const int g = lane >> 4, q = lane & 15;
   const int L = seq_lens[b];
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
-  const int t0 = (blockIdx.x * kAttnWaves + w) * kQTile;   // this wave's first query
-  const int t = t0 + q;                                    // this lane's query (B operand column)
-  const bool tvalid = t < q_len;
-  const int pos = L - q_len + (tvalid ? t : q_len - 1);    // its position
+  const int t0 = (blockIdx.x * kAttnWaves + w) * kQWave;   // this wave's first query
+  // query block qb: tokens t0 + 16qb .. +15; this lane's token (B operand column)
+  int pos[kQB];
+  bool tvalid[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int t = t0 + 16 * qb + q;
+    tvalid[qb] = t < q_len;
+    pos[qb] = L - q_len + (tvalid[qb] ? t : q_len - 1);
+  }
   // last position of this wave's and of the workgroup's queries (-1: none)
-  const int p_wave = t0 < q_len ? L - q_len + min(t0 + kQTile, q_len) - 1 : -1;
-  const int tw_end = min((blockIdx.x + 1) * kAttnWaves * kQTile, q_len);
+  const int p_wave = t0 < q_len ? L - q_len + min(t0 + kQWave, q_len) - 1 : -1;
+  const int tw_end = min((blockIdx.x + 1) * kAttnWaves * kQWave, q_len);
   const int p_wg = L - q_len + tw_end - 1;
 
-  // Query tile as the B operand: dimensions 32ks + 8g .. +8 of token t
-  bf16x8 qf[6];
-  {
-    const int64_t row = (static_cast<int64_t>(b) * q_len + (tvalid ? t : 0)) * H + h;
+  // Query tiles as the B operand: dimensions 32ks + 8g .. +8 of the lane's token
+  bf16x8 qf[kQB][6];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(q_nope + row * kDh + 32 * ks + 8 * g);
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int t = t0 + 16 * qb + q;
+    const int64_t row = (static_cast<int64_t>(b) * q_len + (tvalid[qb] ? t : 0)) * H + h;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qf[qb][ks] = *reinterpret_cast<const bf16x8*>(q_nope + row * kDh + 32 * ks + 8 * g);
 #pragma unroll
     for (int ks = 4; ks < 6; ++ks) {
       const int d0 = 32 * (ks - 4) + 8 * g;  // rope dimensions d0 .. d0+7: pairs d0/2 .. d0/2+3
@@ -172,21 +183,26 @@ __global__ __launch_bounds__(64 * kAttnWaves) void prefill_attn_kernel(
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         float sn, cs;
-        sincos_reduced(static_cast<double>(pos) * theta.t[d0 / 2 + m], sn, cs);
+        sincos_reduced(static_cast<double>(pos[qb]) * theta.t[d0 / 2 + m], sn, cs);
         const float x0 = static_cast<float>(x[2 * m]), x1 = static_cast<float>(x[2 * m + 1]);
         pk[m] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
       }
-      qf[ks] = __builtin_bit_cast(bf16x8, pk);
+      qf[qb][ks] = __builtin_bit_cast(bf16x8, pk);
     }
   }
 
   const float c2 = scale * kLog2eF;
   const uint16_t* kh = kc + (static_cast<int64_t>(b) * H + h) * max_rows * kDh;
   const uint16_t* vh = vc + (static_cast<int64_t>(b) * H + h) * max_rows * kDh;
-  float4_t o[kDh / 16];
+  float4_t o[kQB][kDh / 16];
+  float m_run[kQB], l_run[kQB];
 #pragma unroll
-  for (int db = 0; db < kDh / 16; ++db) o[db] = float4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int qb = 0; qb < kQB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < kDh / 16; ++db) o[qb][db] = float4_t{0.f, 0.f, 0.f, 0.f};
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
 
   // Tile staging, software-pipelined: the 256 threads load the next tile into
   // registers (K^C and V: keys i/16 and 16 + i/16, chunk i%16; k^R: key i/8,
@@ -221,71 +237,92 @@ __global__ __launch_bounds__(64 * kAttnWaves) void prefill_attn_kernel(
     __syncthreads();
     if (k0 > p_wave) continue;  // every key of the tile lies after this wave's queries
 
-    // S^T for keys k0 + 16kb + row, queries q: lane holds keys 16kb + 4g + i
-    float s[2][4];
+    // S^T for keys k0 + 16kb + row, queries of block qb: lane holds keys
+    // 16kb + 4g + i.  Each row fragment read from LDS feeds one MFMA per
+    // query block.
+    float s[kQB][2][4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const char* krow = ks_lds + (16 * kb + q) * kKRowB + 16 * g;
-      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+      float4_t acc[kQB];
 #pragma unroll
-      for (int ks = 0; ks < 6; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(krow + 64 * ks), qf[ks],
-                                                      acc, 0, 0, 0);
+      for (int qb = 0; qb < kQB; ++qb) acc[qb] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + 16 * kb + 4 * g + i;
-        s[kb][i] = key <= pos ? acc[i] * c2 : -INFINITY;
+      for (int ks = 0; ks < 6; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + 64 * ks);
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb)
+          acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[qb][ks], acc[qb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 16 * kb + 4 * g + i;
+          s[qb][kb][i] = key <= pos[qb] ? acc[qb][i] * c2 : -INFINITY;
+        }
       }
     }
-    const float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                           fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    // finite: key 0 <= pos, and m_run is finite after the first tile
-    const float m_new = fmaxf(m_run, rows4_max(mx));
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float p[2][4], psum = 0.f;
+    float alpha[kQB];
+    bf16x8 pf[kQB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float mx = fmaxf(fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3])),
+                             fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3])));
+      // finite: key 0 <= pos, and m_run is finite after the first tile
+      const float m_new = fmaxf(m_run[qb], rows4_max(mx));
+      alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+      float p[2][4], psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[kb][i] = __builtin_amdgcn_exp2f(s[kb][i] - m_new);
-        psum += p[kb][i];
-      }
-    l_run = l_run * alpha + rows4_sum(psum);
-    m_run = m_new;
-    // P^T as the B operand: reduction index 8g + jj = key 4g + jj (jj < 4) or 16 + 4g + jj - 4
-    const uint32_t pk[4] = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
-                            pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
-    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[kb][i] = __builtin_amdgcn_exp2f(s[qb][kb][i] - m_new);
+          psum += p[kb][i];
+        }
+      l_run[qb] = l_run[qb] * alpha[qb] + rows4_sum(psum);
+      m_run[qb] = m_new;
+      // P^T as the B operand: reduction index 8g + jj = key 4g + jj (jj < 4) or 16 + 4g + jj - 4
+      const uint32_t pk[4] = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                              pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+      pf[qb] = __builtin_bit_cast(bf16x8, pk);
+    }
 #pragma unroll
     for (int db = 0; db < kDh / 16; ++db) {
-      o[db][0] *= alpha;
-      o[db][1] *= alpha;
-      o[db][2] *= alpha;
-      o[db][3] *= alpha;
       // V^T as the A operand: dimension 16db + q, keys 4g .. 4g+3 and 16 + 4g ..
       // 16 + 4g+3, two transposed reads: lane q of group g addresses key
       // 4g + q/4 (or 16 + 4g + q/4), dimensions 16db + 4(q%4) .. +3
       const uint32_t voff = (4 * g + (q >> 2)) * kVRowB + 2 * (16 * db + 4 * (q & 3));
       const uint64_t vv[2] = {lds_tr4(v_lds, voff), lds_tr4(v_lds, voff + 16 * kVRowB)};
-      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pf, o[db], 0, 0, 0);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        o[qb][db][0] *= alpha[qb];
+        o[qb][db][1] *= alpha[qb];
+        o[qb][db][2] *= alpha[qb];
+        o[qb][db][3] *= alpha[qb];
+        o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], o[qb][db], 0, 0, 0);
+      }
     }
   }
 
-  // lane holds O^T[16db + 4g + i][query q]
-  if (tvalid) {
-    const float inv = 1.f / l_run;
-    const int64_t row = (static_cast<int64_t>(b) * q_len + t) * H + h;
+  // lane holds O^T[16db + 4g + i][query of block qb]
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    if (!tvalid[qb]) continue;
+    const float inv = 1.f / l_run[qb];
+    const int64_t row = (static_cast<int64_t>(b) * q_len + t0 + 16 * qb + q) * H + h;
     float* orow = out + row * kDh + 4 * g;
 #pragma unroll
     for (int db = 0; db < kDh / 16; ++db) {
-      float4_t v = o[db];
+      float4_t v = o[qb][db];
       v[0] *= inv;
       v[1] *= inv;
       v[2] *= inv;
       v[3] *= inv;
       *reinterpret_cast<float4_t*>(orow + 16 * db) = v;
     }
-    if (lse && g == 0) lse[row] = (m_run + log2f(l_run)) * kLn2F;
+    if (lse && g == 0) lse[row] = (m_run[qb] + log2f(l_run[qb])) * kLn2F;
   }
 }
 
@@ -315,7 +352,7 @@ hipError_t prefill_naive(const mla_dims& d, int batch, int q_len, const void* q_
   if (e != hipSuccess) return e;
   PrefillTheta theta;
   for (int k = 0; k < kDr / 2; ++k) theta.t[k] = pow(d.rope_base, -2.0 * k / kDr);
-  const int wg_tokens = kAttnWaves * kQTile;
+  const int wg_tokens = kAttnWaves * kQWave;
   hipLaunchKernelGGL(prefill_attn_kernel, dim3((q_len + wg_tokens - 1) / wg_tokens, d.n_heads, batch),
                      dim3(64 * kAttnWaves), 0,
                      stream, d.n_heads, q_len, max_rows, d.softmax_scale, theta,
