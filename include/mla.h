@@ -57,7 +57,8 @@
  *               are attended (seq_lens[b] >= 1)
  *   items       [num_items][4]                           int32: (b, split, page_begin, page_end)
  *   split_offsets [batch + 1]                            int32: items of sequence b are
- *               split_offsets[b] .. split_offsets[b+1]-1, in token order
+ *               split_offsets[b] .. split_offsets[b+1]-1, in token order; every
+ *               sequence has at least one item (as mla_plan_splits makes them)
  *   o_part      [num_items][n_heads][d_latent]           float32
  *   lse_part    [num_items][n_heads]                     float32 (natural log)
  *   o_latent    [batch][n_heads][d_latent]               float32: o~_i
@@ -273,7 +274,9 @@ mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const float* o_late
  * launch on the gfx950 fast path: each workgroup merges the partials of its rows
  * (the combine's arithmetic and order, so o_latent is bit-identical to
  * mla_combine's) and feeds the merged rows to the W^UV product without writing
- * them out first.  Cites as mla_combine and mla_out_proj.
+ * them out first.  Cites as mla_combine and mla_out_proj.  A workgroup takes
+ * 32, 16 or 8 query rows of one head (fewer when 32 would leave CUs idle); the
+ * result does not depend on that choice.
  *   split_offsets, o_part, lse_part  as for mla_combine_multi (q_len = 1: as for
  *             mla_combine)
  *   out       float32 [batch][q_len][n_heads][d_head]
