@@ -475,15 +475,16 @@ def main():
 
     # Timed region: K steps.
     torch.cuda.synchronize()
+    step_ev = [new_events(2) for _ in range(args.steps)] if args.flush else None
     w0 = time.perf_counter()
     if args.flush:
-        step_ev = [new_events(2) for _ in range(args.steps)]
         for k in range(args.steps):
             evict()
             step_ev[k][0].record(stream)
             step(k0 + k)
             step_ev[k][1].record(stream)
         torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
         step_ms = np.array([e[0].elapsed_time(e[1]) for e in step_ev])
         pct = {"step_ms_p10": round(float(np.percentile(step_ms, 10)), 5),
                "step_ms_median": round(float(np.median(step_ms)), 5),
@@ -497,10 +498,10 @@ def main():
             step(k0 + k)
         e1.record(stream)
         torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
         ms = e0.elapsed_time(e1) / args.steps
         spread = f"{args.steps} steps back to back"
         pct = {}
-    wall = time.perf_counter() - w0
 
     # Per-kernel breakdown: the same steps with an event between every two kernels.
     evs = [new_events(n_k + 1) for _ in range(args.steps)]
