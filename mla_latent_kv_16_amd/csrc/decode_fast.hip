@@ -675,13 +675,9 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
   const bool direct = merged && nsplit == 1;
 
   // Q fragments (B operand of the scores): head q, values 32ks + 8g .. +8
+  // (staged through the LDS below, so that the first slices' DMA does not
+  // wait for them)
   bf16x8 qf[18];
-  {
-    const uint16_t* qrow = q_abs + (qrow0 + q) * kDq + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
-  }
-  __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
 
   // DMA: rows 8w .. 8w+7 of a slice (see the 128-head kernel)
   const int drow = 8 * w + (lane >> 3);
@@ -789,12 +785,12 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
 
   // Full pass (see the softmax note at the top); every wave computes the same
   // scores, the vote only keeps the waves' control flow provably identical.
-  auto full_pass = [&](bool first) -> bool {
+  auto full_pass = [&](bool first, bool started) -> bool {
 #pragma unroll
     for (int c = 0; c < 8; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
     l_run = 0.f;
     float m_lane = -INFINITY;
-    start();
+    if (!started) start();
     for (int n = 0; n < n_slices; ++n) {
       enter(n);
       float s[2][4];
@@ -816,7 +812,30 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     return !any;
   };
 
-  if (!full_pass(true)) {
+  // The 16 Q rows of this item (18 KiB, contiguous in q_abs) go to ring slot 3
+  // by DMA, ahead of the first three slices; slot 3 receives slice 3 only
+  // after the barrier in enter(0), when every wave holds its fragments.
+  {
+    const char* qsrc = reinterpret_cast<const char*>(q_abs + qrow0 * kDq);
+    const uint32_t qdst = lds_base + (kStages - 1) * kSlotBytes;
+    for (int j = w; j < 18; j += 4) dma16(qsrc + 1024 * j, 16 * lane, qdst + 1024 * j);
+  }
+  start();
+  // this wave's Q loads are done once only the slices' DMA may be outstanding
+  switch (kLoadsPerWave * min(kStages - 1, n_slices)) {
+    case 27: __builtin_amdgcn_s_waitcnt(MLA_VMCNT(27)); break;
+    case 18: __builtin_amdgcn_s_waitcnt(MLA_VMCNT(18)); break;
+    case 9: __builtin_amdgcn_s_waitcnt(MLA_VMCNT(9)); break;
+    default: __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0)); break;
+  }
+  __syncthreads();
+  {
+    const char* qlds = lds + (kStages - 1) * kSlotBytes + q * kRowBytes + 16 * g;
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qlds + 64 * ks);
+  }
+
+  if (!full_pass(true, true)) {
     float m_lane = -INFINITY;
     start();
     for (int n = 0; n < n_slices; ++n) {
@@ -827,7 +846,7 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     }
     __syncthreads();
     m_ref = rows_max(m_lane);
-    full_pass(false);
+    full_pass(false, false);
   }
 
   const float l = rows_sum(l_run);
