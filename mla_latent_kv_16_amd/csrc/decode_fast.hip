@@ -33,13 +33,16 @@
 //    accumulators of a lane already hold the P^T operand of the same lane.
 //
 // Work split, H = 128: two workgroups per work item, one per half of the
-// heads (see decode_h128_kernel), each with eight waves in two roles:
-//  * S waves: scores of 16 heads over every token (Q fragments stay in 72
-//    VGPRs), turned into bf16 weights and put in a 4 KiB LDS exchange buffer;
-//  * V waves: the DMA and the latent PV of 128 columns for the workgroup's 64
-//    heads (128 accumulators), so each transposed C^T fragment feeds 4 MFMAs.
+// heads (see decode_h128_kernel), each with sixteen waves in two roles:
+//  * eight S waves: scores of 16 heads over one 16-token half of every slice
+//    (Q fragments stay in 72 VGPRs), turned into bf16 weights and put in a
+//    4 KiB LDS exchange buffer;
+//  * eight V waves: the latent PV of 64 columns for the workgroup's 64 heads
+//    (64 accumulators), so each transposed C^T fragment feeds 4 MFMAs; four
+//    of them also run the DMA, the other four the L2 prefetch.
 //  The V waves run one slice behind the S waves; one workgroup barrier per
-//  slice.
+//  slice.  H = 16 (decode_h16_kernel): one workgroup of four waves per item,
+//  each scoring all 16 heads itself.
 //
 // Softmax in base 2 against a fixed reference per head: the maximum of the
 // item's first slice.  Weights 2^(x - m_ref) may exceed 1 by up to 2^20, which
@@ -616,7 +619,8 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
 // accumulators are then already the P^T operand of its own PV MFMAs (token
 // order sigma(g, .), as above) and no weights cross between waves.  Wave w
 // owns latent columns 128w .. 128w+127 of the PV (32 accumulators) and the DMA
-// of row group w.  A ring of four slots keeps three slices in flight.
+// of row group w.  A ring of four slots keeps three slices in flight; the
+// item's Q rows arrive through the fourth slot before the first slices.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
