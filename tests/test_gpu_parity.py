@@ -9,7 +9,7 @@ import pytest
 
 from synth import CONFIGS, generate, small
 
-from gpu_util import assert_close, assert_lse, compare_with_oracle, dims_of, run, say
+from gpu_util import assert_close, assert_lse, compare_with_oracle, dims_of, run, say, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -123,6 +123,15 @@ def test_full_size_sampled(mla, name, seqs, heads):
         order = np.argsort(wl.seq_lens)
         seqs = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
     say(f"[full {name}] running; checking sequences {seqs}")
-    out = run(wl)
+    dev = upload(wl)
+    out = run(wl, dev=dev)
     assert np.all(np.isfinite(out["out"])) and np.all(np.isfinite(out["lse"]))
     compare_with_oracle(wl, out, seqs, heads=heads)
+    # the step the bench times merges and projects in one launch: on the same
+    # partials it must give the bits of mla_combine + mla_out_proj above
+    import torch
+    fused = mla.combine_out_proj(dims_of(cfg), torch.from_numpy(out["offs"]).cuda(),
+                                 torch.from_numpy(out["o_part"]).cuda(), torch.from_numpy(out["lse_part"]).cuda(),
+                                 dev["w_uv"], cfg.batch)
+    torch.cuda.synchronize()
+    assert np.array_equal(fused.cpu().numpy(), out["out"]), "combine_out_proj differs from combine + out_proj"
