@@ -97,6 +97,75 @@ def test_rope_pairing():
     check_rope_pairing()
 
 
+def test_cache_rows_from_hidden_properties():
+    """The cache-write recipe against properties that hold whatever its code:
+    the normalised latent keeps the direction of W^DKV h and has mean square
+    ms / (ms + eps) (ms that of W^DKV h); without the norm it is W^DKV h; the
+    key part is W^KR h at position 0 and has its norm at every position."""
+    rng = np.random.default_rng(5)
+    T, dm, dc, dr = 6, 40, 16, 8
+    h = rng.standard_normal((T, dm))
+    w_dkv = rng.standard_normal((dc, dm)) / np.sqrt(dm)
+    w_kr = rng.standard_normal((dr, dm)) / np.sqrt(dm)
+    pos = np.array([0, 1, 7, 100, 4095, 131071])
+    eps = 1e-6
+    raw_c = np.einsum("cd,td->tc", w_dkv, h)
+    raw_k = np.einsum("rd,td->tr", w_kr, h)
+    rows = O.cache_rows_from_hidden(h, w_dkv, w_kr, pos, 1e4, rms_norm=True, eps=eps)
+    c, kr = rows[:, :dc], rows[:, dc:]
+    ms = (raw_c ** 2).mean(axis=1)
+    assert np.allclose((c ** 2).mean(axis=1), ms / (ms + eps), rtol=1e-13, atol=0)
+    ratio = c / raw_c
+    assert np.all(ratio > 0) and np.allclose(ratio, ratio[:, :1], rtol=1e-12, atol=0)
+    assert np.array_equal(kr[0], raw_k[0]) or rel(kr[0], raw_k[0]) < 1e-15
+    assert np.allclose(np.linalg.norm(kr, axis=1), np.linalg.norm(raw_k, axis=1), rtol=1e-13, atol=0)
+    plain = O.cache_rows_from_hidden(h, w_dkv, w_kr, pos, 1e4, rms_norm=False)
+    assert rel(plain[:, :dc], raw_c) < 1e-14
+    assert rel(plain[:, dc:], kr) < 1e-14   # the norm of c does not touch the key part
+    # one hidden state at several positions: the key part is rotated by the
+    # position (it moves away from W^KR h), and the inner product of two
+    # encodings depends only on the difference of their positions
+    hp = np.repeat(h[:1], 4, axis=0)
+    same = O.cache_rows_from_hidden(hp, w_dkv, w_kr, np.array([3, 4, 50, 51]), 1e4, rms_norm=True)[:, dc:]
+    assert rel(same[1], raw_k[0]) > 1e-3 and rel(same[0], same[1]) > 1e-3
+    assert abs(same[0] @ same[1] - same[2] @ same[3]) < 1e-12 * (raw_k[0] @ raw_k[0])
+
+
+def check_cache_rows_from_hidden():
+    test_cache_rows_from_hidden_properties()
+
+
+def _cache_rows_norm_over_tokens(h, w_dkv, w_kr, positions, rope_base, rms_norm, eps=1e-6):
+    c = np.asarray(h, np.float64) @ np.asarray(w_dkv, np.float64).T
+    if rms_norm:
+        c = c / np.sqrt((c * c).mean(axis=0, keepdims=True) + eps)
+    kr = O.rope(np.asarray(h, np.float64) @ np.asarray(w_kr, np.float64).T, np.asarray(positions), rope_base)
+    return np.concatenate([c, kr], axis=1)
+
+
+def _cache_rows_unrotated(h, w_dkv, w_kr, positions, rope_base, rms_norm, eps=1e-6):
+    c = np.asarray(h, np.float64) @ np.asarray(w_dkv, np.float64).T
+    if rms_norm:
+        c = c / np.sqrt((c * c).mean(axis=1, keepdims=True) + eps)
+    return np.concatenate([c, np.asarray(h, np.float64) @ np.asarray(w_kr, np.float64).T], axis=1)
+
+
+def _cache_rows_first_position(h, w_dkv, w_kr, positions, rope_base, rms_norm, eps=1e-6):
+    c = np.asarray(h, np.float64) @ np.asarray(w_dkv, np.float64).T
+    if rms_norm:
+        c = c / np.sqrt((c * c).mean(axis=1, keepdims=True) + eps)
+    kr = O.rope(np.asarray(h, np.float64) @ np.asarray(w_kr, np.float64).T, np.asarray(positions)[0], rope_base)
+    return np.concatenate([c, kr], axis=1)
+
+
+@pytest.mark.parametrize("replacement", [_cache_rows_norm_over_tokens, _cache_rows_unrotated,
+                                         _cache_rows_first_position])
+def test_planted_cache_row_mistake_is_caught(monkeypatch, replacement):
+    monkeypatch.setattr(O, "cache_rows_from_hidden", replacement)
+    with pytest.raises(AssertionError):
+        check_cache_rows_from_hidden()
+
+
 def test_rope_identities():
     check_rope_identities()
 
