@@ -20,9 +20,11 @@
 //    paged cache, float32 accumulation rounded to bf16.
 //  * attention: one workgroup of four waves per (128 query tokens, head,
 //    sequence), one wave per 32 queries (two blocks of 16, so that every K or
-//    V fragment read from LDS feeds two MFMAs); keys in tiles of 32 staged in LDS for
-//    all four waves (K row-major, V transposed), with an online softmax in base
-//    2: S^T[16 keys x 16 queries] on MFMA (K rows as A, the query tile as B, 6
+//    V fragment read from LDS feeds two MFMAs); keys in tiles of 32 staged in
+//    LDS for all four waves (K row-major, V transposed), with an online
+//    softmax in base 2 whose reference moves only when the running maximum
+//    gains more than 2^8 (the accumulators are rescaled only then).
+//    S^T[16 keys x 16 queries] on MFMA (K rows as A, the query tile as B, 6
 //    steps over the 192 dimensions), then O^T[128 x 16 queries] += V^T . P^T
 //    with the reduction index running over the keys each lane's score
 //    accumulators hold, so P^T needs no reshuffle.
@@ -34,6 +36,7 @@
 namespace mla {
 namespace {
 
+constexpr float kRefSlack = 8.f;   // log2 units the softmax reference may trail the running maximum
 constexpr int kQB = 2;             // 16-query blocks per attention wave
 constexpr int kQWave = 16 * kQB;   // query tokens per attention wave
 constexpr int kKeyTile = 32;   // keys per attention iteration
@@ -263,29 +266,49 @@ __global__ __launch_bounds__(64 * kAttnWaves, 2) void prefill_attn_kernel(
         }
       }
     }
+    bool rescale = false;
     float alpha[kQB];
     bf16x8 pf[kQB];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-      const float mx = fmaxf(fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3])),
-                             fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3])));
-      // finite: key 0 <= pos, and m_run is finite after the first tile
-      const float m_new = fmaxf(m_run[qb], rows4_max(mx));
-      alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+      const float mx = rows4_max(fmaxf(fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3])),
+                                       fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3]))));
+      // The reference m_run moves only when some query of the wave gains more
+      // than kRefSlack over it (always in the first tile, where m_run = -inf;
+      // mx is finite since key 0 <= pos).  Weights 2^(s - m_run) then stay
+      // below 2^kRefSlack, which bf16 weights and float32 sums carry without
+      // loss, and the accumulators are rescaled only on those tiles.
+      alpha[qb] = 1.f;
+      if (__any(mx > m_run[qb] + kRefSlack)) {  // the same for the whole wave
+        const float m_new = fmaxf(m_run[qb], mx);
+        alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        rescale = true;
+      }
       float p[2][4], psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[kb][i] = __builtin_amdgcn_exp2f(s[qb][kb][i] - m_new);
+          p[kb][i] = __builtin_amdgcn_exp2f(s[qb][kb][i] - m_run[qb]);
           psum += p[kb][i];
         }
       l_run[qb] = l_run[qb] * alpha[qb] + rows4_sum(psum);
-      m_run[qb] = m_new;
       // P^T as the B operand: reduction index 8g + jj = key 4g + jj (jj < 4) or 16 + 4g + jj - 4
       const uint32_t pk[4] = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                               pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
       pf[qb] = __builtin_bit_cast(bf16x8, pk);
+    }
+    if (rescale) {  // one branch per tile; alpha is 1 for a block whose reference stayed
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+        for (int db = 0; db < kDh / 16; ++db) {
+          o[qb][db][0] *= alpha[qb];
+          o[qb][db][1] *= alpha[qb];
+          o[qb][db][2] *= alpha[qb];
+          o[qb][db][3] *= alpha[qb];
+        }
     }
 #pragma unroll
     for (int db = 0; db < kDh / 16; ++db) {
@@ -296,13 +319,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, 2) void prefill_attn_kernel(
       const uint64_t vv[2] = {lds_tr4(v_lds, voff), lds_tr4(v_lds, voff + 16 * kVRowB)};
       const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
 #pragma unroll
-      for (int qb = 0; qb < kQB; ++qb) {
-        o[qb][db][0] *= alpha[qb];
-        o[qb][db][1] *= alpha[qb];
-        o[qb][db][2] *= alpha[qb];
-        o[qb][db][3] *= alpha[qb];
+      for (int qb = 0; qb < kQB; ++qb)
         o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[qb], o[qb][db], 0, 0, 0);
-      }
     }
   }
 
