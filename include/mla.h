@@ -41,7 +41,8 @@
  *   returns a negative status and enqueues nothing.  A failed launch returns
  *   MLA_ERR_HIP.  Device data is not checked: a block-table entry outside
  *   [0, num_pages) or a length outside [1, max_pages_per_seq * page_size] is
- *   undefined behaviour.  No C++ exception crosses this interface.
+ *   undefined behaviour (mla_check_paging looks for both, for debugging).  No
+ *   C++ exception crosses this interface.
  * Layouts (row-major, innermost last; "dtype" is mla_dims.dtype):
  *   q_nope      [batch][n_heads][d_head]                 dtype
  *   q_pe        [batch][n_heads][d_rope]                 dtype (not yet encoded)
@@ -318,6 +319,24 @@ mla_status mla_append_kv(const mla_dims* dims, int32_t d_model, int32_t batch, c
 
 /* Bytes of workspace mla_append_kv needs; -1 on bad arguments.  Host only. */
 int64_t mla_append_kv_workspace_bytes(const mla_dims* dims, int32_t d_model, int32_t batch);
+
+/* Debug check of the device data the decode and prefill entry points take on
+ * trust.  Page "DeepSeek V2 技术解析" 2.1.1 (paged KV memory): sequence b reads
+ * pages block_table[b][0 .. ceil(L_b / page_size) - 1], which must lie in
+ * [0, num_pages), with L_b = seq_lens[b] in [min_len, max_pages_per_seq * page_size]
+ * (min_len = 1 for mla_decode_splitkv and mla_decode_merged, q_len for
+ * mla_decode_splitkv_multi and mla_prefill_naive).
+ * Writes result[0] = the number of bad values (one per length out of range,
+ * whose entries are then not looked at, plus one per entry out of range among
+ * the pages a good length uses) and result[1] = the smallest b with a bad value,
+ * or -1.  result: device int32[2], owned by the caller, need not be cleared.
+ * One workgroup: cheap next to a decode step, but not free; meant for debugging.
+ * Entries past a sequence's pages are not looked at.
+ * Errors: MLA_ERR_INVALID_ARG for null pointers, batch/min_len/num_pages/
+ * max_pages_per_seq < 1 or misalignment. */
+mla_status mla_check_paging(const mla_dims* dims, int32_t batch, int32_t min_len,
+                            const int32_t* seq_lens, int32_t num_pages, const int32_t* block_table,
+                            int32_t max_pages_per_seq, int32_t* result, void* stream);
 
 /* Text of the last HIP error that made a libmla call on this thread return
  * MLA_ERR_HIP ("" if none).  Valid until the next libmla call on the thread. */

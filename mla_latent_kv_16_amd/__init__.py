@@ -8,7 +8,14 @@ been built -- there is no fallback.
 Entry points mirror include/mla.h:
     absorb_q, plan_splits, decode_splitkv, combine, decode_merged, out_proj, append_kv,
     decode_splitkv_multi, combine_multi, combine_out_proj, prefill_naive
-plus `decode_step`, which runs the four device steps in order.
+plus `decode_step`, which runs the four device steps in order, and
+`check_paging`, a device check of the lengths and block-table entries.
+
+With the environment variable MLA_DEBUG set (to anything but "" or "0"),
+decode_splitkv, decode_splitkv_multi, decode_merged and prefill_naive first run
+check_paging on their stream, wait for it and raise MlaError on a bad length or
+block-table entry (the check runs even inside record_calls() and is not
+recorded).
 """
 from __future__ import annotations
 
@@ -24,7 +31,7 @@ __all__ = ["MlaError", "Dims", "load", "lib_path", "absorb_q", "plan_splits", "d
            "decode_merged", "append_kv", "decode_splitkv_multi", "combine_multi", "combine_out_proj",
            "prefill_naive",
            "combine", "out_proj", "decode_step", "fast_path", "version", "record_calls", "replay_calls",
-           "BF16", "F32"]
+           "check_paging", "BF16", "F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 BF16, F32 = 0, 1
@@ -110,6 +117,7 @@ def load():
         "mla_append_kv": (i32, [pd, i32, i32, vp, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, i32,
                                  vp, ctypes.c_int64, vp]),
         "mla_append_kv_workspace_bytes": (ctypes.c_int64, [pd, i32, i32]),
+        "mla_check_paging": (i32, [pd, i32, i32, vp, i32, vp, i32, vp, vp]),
         "mla_status_string": (ctypes.c_char_p, [i32]),
         "mla_version": (i32, []),
         "mla_fast_path": (i32, [pd]),
@@ -245,6 +253,36 @@ def plan_splits(dims: Dims, seq_lens_host, num_slots: int) -> Tuple[np.ndarray, 
     return items[:n.value].copy(), offs
 
 
+def check_paging(dims: Dims, block_table, seq_lens, num_pages: int, min_len: int = 1,
+                 result=None, stream=None):
+    """Device check of seq_lens and the block-table entries they address:
+    result int32 [2] = (number of bad values, first bad sequence or -1).
+    Enqueued on the stream, not waited for."""
+    torch = _torch()
+    B = seq_lens.shape[0]
+    if result is None:
+        result = torch.empty(2, dtype=torch.int32, device=seq_lens.device)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must have shape ({B}, max_pages)")
+    _check(load().mla_check_paging(
+        ctypes.byref(dims.c()), B, int(min_len), _ptr(seq_lens, torch.int32, (B,), "seq_lens"),
+        int(num_pages), _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
+        _ptr(result, torch.int32, (2,), "result"), _stream(stream)), "mla_check_paging")
+    return result
+
+
+def _debug_paging(dims: Dims, block_table, seq_lens, num_pages: int, min_len: int, stream, where):
+    if os.environ.get("MLA_DEBUG", "0") in ("", "0"):
+        return
+    torch = _torch()
+    r = check_paging(dims, block_table, seq_lens, num_pages, min_len, stream=stream)
+    torch.cuda.synchronize(r.device)
+    bad, first = (int(v) for v in r.cpu())
+    if bad:
+        raise MlaError(-1, f"{where}: MLA_DEBUG found {bad} bad length or block-table "
+                           f"value(s), first in sequence {first}")
+
+
 def decode_splitkv(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items,
                    o_part=None, lse_part=None, stream=None):
     """Per work item: (o_part [W, H, d_c] float32, lse_part [W, H] float32)."""
@@ -258,6 +296,7 @@ def decode_splitkv(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items,
     if lse_part is None:
         lse_part = torch.empty((W, H), dtype=torch.float32, device=dev)
     num_pages = kv_cache.shape[0]
+    _debug_paging(dims, block_table, seq_lens, num_pages, 1, stream, "mla_decode_splitkv")
     _launch("mla_decode_splitkv",
         ctypes.byref(dims.c()), B, _ptr(q_abs, dt, (B, H, dims.row), "q_abs"),
         _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
@@ -303,6 +342,7 @@ def decode_splitkv_multi(dims: Dims, q_abs, kv_cache, block_table, seq_lens, ite
     if lse_part is None:
         lse_part = torch.empty((W, T, H), dtype=torch.float32, device=dev)
     num_pages = kv_cache.shape[0]
+    _debug_paging(dims, block_table, seq_lens, num_pages, T, stream, "mla_decode_splitkv_multi")
     _launch("mla_decode_splitkv_multi",
         ctypes.byref(dims.c()), B, T, _ptr(q_abs, dt, (B, T, H, dims.row), "q_abs"),
         _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
@@ -355,6 +395,7 @@ def decode_merged(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items, spl
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     num_pages = kv_cache.shape[0]
+    _debug_paging(dims, block_table, seq_lens, num_pages, 1, stream, "mla_decode_merged")
     _launch("mla_decode_merged",
         ctypes.byref(dims.c()), B, _ptr(q_abs, dt, (B, H, dims.row), "q_abs"),
         _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
@@ -457,6 +498,7 @@ def prefill_naive(dims: Dims, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, s
     if lse is None and want_lse:
         lse = torch.empty((B, T, H), dtype=torch.float32, device=dev)
     num_pages = kv_cache.shape[0]
+    _debug_paging(dims, block_table, seq_lens, num_pages, T, stream, "mla_prefill_naive")
     _check(L.mla_prefill_naive(
         ctypes.byref(dims.c()), B, T, _ptr(q_nope, dt, (B, T, H, dims.d_head), "q_nope"),
         _ptr(q_pe, dt, (B, T, H, dims.d_rope), "q_pe"),

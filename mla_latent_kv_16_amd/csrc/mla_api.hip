@@ -214,6 +214,20 @@ mla_status mla_combine_multi(const mla_dims* dims, int32_t batch, int32_t q_len,
   return combine_impl(dims, batch, q_len, split_offsets, o_part, lse_part, o_latent, lse, stream);
 }
 
+mla_status mla_check_paging(const mla_dims* dims, int32_t batch, int32_t min_len,
+                            const int32_t* seq_lens, int32_t num_pages, const int32_t* block_table,
+                            int32_t max_pages_per_seq, int32_t* result, void* stream) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  if (batch < 1 || min_len < 1 || num_pages < 1 || max_pages_per_seq < 1) return MLA_ERR_INVALID_ARG;
+  if (!seq_lens || !block_table || !result) return MLA_ERR_INVALID_ARG;
+  if (!al4(seq_lens) || !al4(block_table) || !al4(result)) return MLA_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+  return launched(check_paging(*dims, batch, min_len, seq_lens, block_table, max_pages_per_seq,
+                               num_pages, result, st));
+}
+
 int64_t mla_append_kv_workspace_bytes(const mla_dims* dims, int32_t d_model, int32_t batch) {
   if (check_dims(dims) != MLA_OK || d_model < 1 || batch < 1) return -1;
   return static_cast<int64_t>(append_slices(d_model)) * batch * (dims->d_latent + dims->d_rope) *

@@ -71,6 +71,12 @@ hipError_t append_kv(const mla_dims& d, int d_model, int batch, const void* h, c
                      void* kv_cache, const int32_t* block_table, int max_pages, float* ws,
                      hipStream_t stream);
 
+// Debug check of seq_lens and the block-table entries they address (check.hip):
+// result[0] = bad values, result[1] = first bad sequence or -1.
+hipError_t check_paging(const mla_dims& d, int batch, int min_len, const int32_t* seq_lens,
+                        const int32_t* block_table, int max_pages, int num_pages,
+                        int32_t* result, hipStream_t stream);
+
 // Host planner (plan.cpp).
 mla_status plan_splits(int page_size, int batch, const int32_t* seq_lens, int num_slots,
                        int max_items, int32_t* items, int32_t* split_offsets, int32_t* num_items,

@@ -93,6 +93,7 @@ int main(void) {
     CHECK(mla_append_kv(&v2, 5120, 2, p, p, p, i, 1, 1e-6f, p, 10, i, 4, NULL, 1 << 20, NULL) ==
           MLA_ERR_INVALID_ARG);
     CHECK(mla_append_kv_workspace_bytes(&v2, 5120, 64) == (int64_t)8 * 64 * 576 * 4);
+    CHECK(mla_check_paging(&v2, 2, 1, i, 10, NULL, 4, (int32_t*)p, NULL) == MLA_ERR_INVALID_ARG);
   }
 
   if (fails) return 1;

@@ -175,6 +175,25 @@ def test_append_kv_rejects_bad_arguments(lib):
     assert f(_d(), *args) == WORKSPACE
 
 
+def test_check_paging_rejects_bad_arguments(lib):
+    f = lib.mla_check_paging
+    # batch min_len seq_lens num_pages block_table max_pages result stream
+    good = [64, 1, A, 10, A, 4, A, None]
+    for i in (2, 4, 6):                            # each pointer argument set to NULL
+        args = list(good)
+        args[i] = None
+        assert f(_d(), *args) == INVALID, i
+    for i in (0, 1, 3, 5):                         # sizes < 1
+        args = list(good)
+        args[i] = 0
+        assert f(_d(), *args) == INVALID, i
+    for i in (2, 4, 6):                            # misaligned int32 arrays
+        args = list(good)
+        args[i] = A + 2
+        assert f(_d(), *args) == INVALID, i
+    assert f(None, *good) == INVALID
+
+
 def test_combine_and_out_proj_reject_bad_arguments(lib):
     assert lib.mla_combine(_d(), 0, A, A, A, A, A, None) == INVALID
     assert lib.mla_combine(_d(), 2, None, A, A, A, A, None) == INVALID

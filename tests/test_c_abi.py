@@ -26,3 +26,29 @@ def test_c_client(tmp_path):
     assert r.returncode == 0, r.stdout + r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
+
+
+ROCM_INCLUDE = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not available")
+@pytest.mark.skipif(not os.path.exists(os.path.join(ROCM_INCLUDE, "hip", "hip_runtime.h")),
+                    reason="HIP headers not available")
+def test_planner_under_sanitizers(tmp_path):
+    """The host planner built with g++ under ASan + UBSan, driven by
+    tests/c_abi/plan_host.cpp: argument errors, capacity errors with exactly
+    sized buffers, edge and random length mixes, the plan's invariants."""
+    exe = tmp_path / "plan_host"
+    csrc = os.path.join(PKG, "csrc")
+    # host code only: the planner source and the driver, no device code
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-D__HIP_PLATFORM_AMD__", "-I", ROCM_INCLUDE, "-I", os.path.join(ROOT, "include"),
+           "-I", csrc, os.path.join(ROOT, "tests", "c_abi", "plan_host.cpp"),
+           os.path.join(csrc, "plan.cpp"), "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    env = dict(os.environ, ASAN_OPTIONS="abort_on_error=0:halt_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
