@@ -36,8 +36,10 @@ inline int64_t part_pages(int64_t pages, int64_t n, int64_t k) {
   return pages / n + (k < pages % n ? 1 : 0);
 }
 
+// Stops as soon as the makespan passes `bound` (a size already known to be
+// worse needs no finishing).
 Layout simulate(const std::vector<int64_t>& pages, int64_t chunk, int num_slots,
-                int64_t overhead) {
+                int64_t overhead, int64_t bound) {
   Layout r{chunk, 0, 0};
   std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>> free_at;
   for (int i = 0; i < num_slots; ++i) free_at.push(0);
@@ -48,6 +50,7 @@ Layout simulate(const std::vector<int64_t>& pages, int64_t chunk, int num_slots,
       free_at.pop();
       const int64_t end = t + part_pages(p, n, k) * kUnit + overhead;
       r.makespan = std::max(r.makespan, end);
+      if (r.makespan > bound) return r;
       free_at.push(end);
       ++r.items;
     }
@@ -88,14 +91,24 @@ mla_status plan_splits(int page_size, int batch, const int32_t* seq_lens, int nu
   const int64_t partial_bytes = static_cast<int64_t>(n_heads) * 513 * 4 * 2;
   const int64_t overhead = kUnit + (partial_bytes * kUnit) / (64 * 1152);
 
+  // Candidate item sizes: about total / (k * num_slots) pages for k from 1 to 8
+  // in steps of 1/16 (k waves of items), plus the longest sequence (no split).
+  // The makespan changes by several percent between neighbouring sizes when
+  // lengths are mixed, so the grid is fine.  Equal sizes are tried once, the
+  // larger ones (fewer items, quicker to simulate) first, so that a good
+  // makespan early cuts the simulation of worse sizes short.
   Layout best{longest, 0, INT64_MAX};
   std::vector<int64_t> cands;
-  for (int k = 1; k <= 8; ++k) cands.push_back(std::max<int64_t>(1, (total + int64_t(k) * num_slots - 1) / (int64_t(k) * num_slots)));
+  for (int j = 16; j <= 128; ++j) {
+    const int64_t den = int64_t(j) * num_slots;
+    // sizes past the longest sequence all give one item per sequence
+    cands.push_back(std::min(longest, std::max<int64_t>(1, (total * 16 + den - 1) / den)));
+  }
   cands.push_back(longest);
-  std::sort(cands.begin(), cands.end());
+  std::sort(cands.begin(), cands.end(), std::greater<int64_t>());
   cands.erase(std::unique(cands.begin(), cands.end()), cands.end());
   for (int64_t c : cands) {
-    Layout l = simulate(pages, c, num_slots, overhead);
+    Layout l = simulate(pages, c, num_slots, overhead, best.makespan);
     if (l.makespan < best.makespan || (l.makespan == best.makespan && l.items < best.items)) best = l;
   }
   if (best.items > max_items) {
