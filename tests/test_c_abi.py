@@ -48,7 +48,8 @@ def test_planner_under_sanitizers(tmp_path):
            os.path.join(csrc, "plan.cpp"), "-o", str(exe)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
-    env = dict(os.environ, ASAN_OPTIONS="abort_on_error=0:halt_on_error=1",
+    # a library preloaded by the environment would otherwise make ASan refuse to start
+    env = dict(os.environ, ASAN_OPTIONS="abort_on_error=0:halt_on_error=1:verify_asan_link_order=0",
                UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr
