@@ -21,6 +21,8 @@
 //    and the scatter into the cache slot.
 #include <math.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "mla_internal.h"
 
@@ -28,6 +30,7 @@ namespace mla {
 namespace {
 
 constexpr int kKSlice = 640;  // d_model values per K-slice (20 MFMA steps)
+constexpr int kSteps = kKSlice / 32;
 
 __global__ __launch_bounds__(64) void append_project_mfma(
     int batch, int d_model, int D, const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_dkv,
@@ -41,12 +44,25 @@ __global__ __launch_bounds__(64) void append_project_mfma(
   const bool bvalid = b < batch;
   const uint16_t* hrow = h + static_cast<int64_t>(bvalid ? b : 0) * d_model;
   const int kend = min(d_model, ks0 + kKSlice);
+  // Every load of the slice is issued before the first MFMA, so the wave waits
+  // for memory once instead of once per step.  Steps past d_model (the last
+  // slice may be short; d_model % 32 == 0) load the slice's first step again,
+  // a valid address, and are dropped below.
+  bf16x8 av[kSteps], wv[kSteps];
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int kk = ks0 + 32 * i;
+    const int k = (kk < kend ? kk : ks0) + 8 * g;
+    av[i] = *reinterpret_cast<const bf16x8*>(hrow + k);
+    wv[i] = *reinterpret_cast<const bf16x8*>(wrow + k);
+  }
   float4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int kk = ks0; kk < kend; kk += 32) {  // uniform trip count (d_model % 32 == 0)
-    const int k = kk + 8 * g;
-    const bf16x8 a = bvalid ? *reinterpret_cast<const bf16x8*>(hrow + k) : bf16x8{};
-    const bf16x8 wv = *reinterpret_cast<const bf16x8*>(wrow + k);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wv, acc, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    if (ks0 + 32 * i < kend) {  // uniform
+      const bf16x8 a = bvalid ? av[i] : bf16x8{};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wv[i], acc, 0, 0, 0);
+    }
   }
   // lane holds D[b = 16bb + 4g + i][col = 16cb + q]
   float* out = ws + (static_cast<int64_t>(blockIdx.z) * batch) * D;
@@ -76,18 +92,27 @@ __global__ __launch_bounds__(256) void append_project_generic(
   ws[(static_cast<int64_t>(s) * batch + b) * D + col] = acc;
 }
 
-__global__ __launch_bounds__(256) void append_finish(
+__global__ __launch_bounds__(1024) void append_finish(
     int batch, int dc, int dr, int n_slices, bool bf, bool rms_norm, float eps, double rope_base,
     const int32_t* __restrict__ positions, const float* __restrict__ ws, void* __restrict__ cache,
     int page_size, const int32_t* __restrict__ block_table, int max_pages) {
-  extern __shared__ float row[];  // [dc + dr], then 4 floats of reduction space
+  extern __shared__ float row[];  // [dc + dr], then one float per wave for the reduction
   const int b = blockIdx.x;
   const int D = dc + dr;
   float* red = row + D;
   float ss = 0.f;
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    // the slices in order, eight loads in flight at a time
     float v = 0.f;
-    for (int s = 0; s < n_slices; ++s) v += ws[(static_cast<int64_t>(s) * batch + b) * D + c];
+    int s = 0;
+    for (; s + 8 <= n_slices; s += 8) {
+      float t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[j] = ws[(static_cast<int64_t>(s + j) * batch + b) * D + c];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += t[j];
+    }
+    for (; s < n_slices; ++s) v += ws[(static_cast<int64_t>(s) * batch + b) * D + c];
     row[c] = v;
     if (c < dc) ss = fmaf(v, v, ss);
   }
@@ -138,7 +163,11 @@ hipError_t append_kv(const mla_dims& d, int d_model, int batch, const void* h, c
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(append_finish, dim3(batch), dim3(256), (D + 4) * sizeof(float), stream, batch,
+  // one thread per output column where D allows (up to 1024), so each thread's
+  // slice loads are all in flight at once
+  const int threads = std::min(1024, (D + 63) / 64 * 64);
+  hipLaunchKernelGGL(append_finish, dim3(batch), dim3(threads), (D + threads / 64) * sizeof(float),
+                     stream, batch,
                      d.d_latent, d.d_rope, S, bf, rms_norm, eps, d.rope_base, positions, ws, kv_cache,
                      d.page_size, block_table, max_pages);
   return hipGetLastError();
