@@ -57,20 +57,16 @@
 
 #include <type_traits>
 
-#include "device_common.h"
-#include "mla_internal.h"
+#include "decode_common.h"
 
 namespace mla {
 namespace {
 
-constexpr int kRowBytes = kDq * 2;             // 1152
-constexpr int kSliceTok = 32;
-constexpr int kSlotBytes = kSliceTok * kRowBytes;  // 36,864
+using namespace dec;
+
 constexpr int kStages = 4;
 constexpr int kDmaWaves = 4;
 constexpr int kLoadsPerWave = kSlotBytes / 1024 / kDmaWaves;  // 9 instructions of 1 KiB
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kMaxJumpDefault = 20.0f;  // log2 units; see the softmax note above
 
 // Pipelining depths (steps of LDS reads issued ahead of their MFMAs).
@@ -83,67 +79,6 @@ constexpr float kMaxJumpDefault = 20.0f;  // log2 units; see the softmax note ab
 #ifndef MLA_S_PRIO
 #define MLA_S_PRIO 3
 #endif
-
-static_assert(kSlotBytes % (1024 * kDmaWaves) == 0, "slot must split evenly over the waves");
-
-#define MLA_VMCNT(n) (((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
-
-// Row swizzle: logical 16-byte chunk `ch` of LDS row `t` sits at chunk position
-// ch ^ swz(t), a permutation inside aligned groups of 8 chunks (a row has 72).
-// LDS has 64 four-byte banks; a 1152-byte row moves the bank position by half
-// of the 256-byte period, so row parity picks the half.  How gfx950 services a
-// wave (measured with the SQ_LDS_BANK_CONFLICT counter): ds_read_b128 takes 16
-// lanes per cycle, namely the lanes of one half-wave whose lane-index bits 2..4
-// have equal parity; ds_read_b64_tr_b16 takes one half-wave per cycle.
-// With swz(t) = 2 ((t >> 1) & 3):
-//  * QK^T reads, lane 16g + q reading row q, chunk 4k + g: in one cycle
-//    (q0, g0, q1 ^ g1, q2) takes all 16 values, so the 16 lanes hit 16
-//    distinct bank groups;
-//  * PV reads, row 4g + q/4, chunk 2c + q1, half q0: over a half-wave the
-//    8-byte bank pair (q2, q1, q3 ^ c0, g0 ^ c1, q0) takes all 32 values.
-__device__ __forceinline__ int swz(int t) { return ((t >> 1) & 3) << 1; }
-
-// Maximum / sum over the four lanes q, q+16, q+32, q+48 (the 16-lane rows of
-// a wave) with the gfx950 row-swap permutes: v_permlane16_swap exchanges rows
-// 0<->1 and 2<->3 between its two operands, v_permlane32_swap the two halves.
-__device__ __forceinline__ float rows_max(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// 16 bytes per lane from `base + voff` into LDS at m0 + 16 * lane.  (The
-// instruction's immediate offset is left at 0: it would move the LDS
-// destination as well.)
-#ifndef MLA_DMA_POLICY
-#define MLA_DMA_POLICY ""
-#endif
-__device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" MLA_DMA_POLICY ::"v"(voff), "s"(base), "{m0}"(lds_addr)
-               : "memory");
-}
-
-// The same with the non-temporal bit.  At 16 heads every row is read by one
-// workgroup and streams through once; the hint measured 35.7 -> 32.7 us on the
-// V2-Lite workload.  (At 128 heads, where the two workgroups of an item read
-// each row, it made no difference.)
-__device__ __forceinline__ void dma16_nt(const char* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
-}
-
-// 4 bytes per lane from `base + voff` into LDS at m0 + 4 * lane: used only to
-// pull rows into the L2 ahead of their DMA (the LDS bytes are never read).  No
-// register receives the data, so nothing waits for it until the epilogue.
-__device__ __forceinline__ void touch4(const char* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr) : "memory");
-}
 // How many slices ahead of the one being scored the V waves without DMA pull
 // rows into the L2 (0: off).  The four-slot LDS ring keeps only two slices in
 // flight; these touches keep HBM reads of a third in flight as well.
@@ -151,15 +86,7 @@ __device__ __forceinline__ void touch4(const char* base, uint32_t voff, uint32_t
 #define MLA_PREFETCH_D 3
 #endif
 
-__device__ __forceinline__ bf16x8 lds_read128(const char* lds, uint32_t off) {
-  return *reinterpret_cast<const bf16x8*>(lds + off);
-}
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const char* lds, uint32_t off) {
-  short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) short4_t*)((__attribute__((address_space(3))) const char*)lds + off));
-  return __builtin_bit_cast(bf16x4, v);
-}
+static_assert(kSlotBytes % (1024 * kDmaWaves) == 0, "slot must split evenly over the waves");
 
 // ---------------------------------------------------------------------------
 // H = 128, two workgroups per work item: workgroup half hh takes heads
@@ -216,25 +143,10 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
   const int g = lane >> 4;   // lane group (k block of the MFMA operands)
   const int q = lane & 15;   // row/column within a 16-block
 
-  // block -> (item, query token, half): an item has per = 2 q_len workgroups;
-  // blocks 8 per m + 8 r + j (j < 8, r < per) take part r of item 8m + j, so
-  // all parts of an item run on one XCD (blocks go to XCDs round-robin) and
-  // are dispatched together; a last incomplete group of items is laid out the
-  // same way over the blocks that remain.  Part r = query token r / 2, half r % 2.
+  // block -> (item, part): an item has 2 q_len workgroups, all on one XCD and
+  // dispatched together (block_to_item); part r = query token r / 2, half r % 2.
   int it, part;
-  {
-    const int per = 2 * q_len;
-    const int blk = blockIdx.x;
-    const int full = num_items & ~7;
-    if (blk < per * full) {
-      it = (blk / (8 * per)) * 8 + (blk & 7);
-      part = (blk >> 3) % per;
-    } else {
-      const int j = blk - per * full, rest = num_items - full;
-      it = full + j % rest;
-      part = j / rest;
-    }
-  }
+  block_to_item(blockIdx.x, num_items, 2 * q_len, it, part);
   const int hh = part & 1, tq = part >> 1;
   const int b = items[4 * it];
   const int p0 = items[4 * it + 2];
@@ -271,8 +183,6 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
   // Slot layout: row t, logical chunk c at tile (t / 8, c / 8): (9 (t / 8) +
   // c / 8) KiB + 128 (t % 8) + 16 ((c % 8) ^ swz(t)); rows t and t + 16 are
   // kRowGroup2 bytes apart.
-  constexpr uint32_t kTileRowGroup = 9 * 1024;
-  constexpr uint32_t kRowGroup2 = 2 * kTileRowGroup;
 
   // Every wave runs the same sequence of workgroup barriers: a full pass has
   // n_slices + 4 of them, the exact-maximum pass n_slices + 2, the epilogue 1.
@@ -642,18 +552,7 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
 
   // block -> (item, query token), laid out as in the 128-head kernel
   int it, tq;
-  {
-    const int blk = blockIdx.x;
-    const int full = num_items & ~7;
-    if (blk < q_len * full) {
-      it = (blk / (8 * q_len)) * 8 + (blk & 7);
-      tq = (blk >> 3) % q_len;
-    } else {
-      const int j = blk - q_len * full, rest = num_items - full;
-      it = full + j % rest;
-      tq = j / rest;
-    }
-  }
+  block_to_item(blockIdx.x, num_items, q_len, it, tq);
   const int b = items[4 * it];
   const int p0 = items[4 * it + 2];
   const int p1 = items[4 * it + 3];
@@ -669,8 +568,6 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     if (threadIdx.x < H) lse_part[prow0 + threadIdx.x] = -INFINITY;
     return;
   }
-  constexpr uint32_t kTileRowGroup = 9 * 1024;
-  constexpr uint32_t kRowGroup2 = 2 * kTileRowGroup;
   auto slot_of = [&](int n) -> const char* { return lds + (n % kStages) * kSlotBytes; };
   // merged mode, as in the 128-head kernel (one ticket per sequence)
   const bool merged = tickets != nullptr;
