@@ -34,7 +34,13 @@ Readings where the pages are silent (all formulas there were images):
   * the query sits at position L-1 and attends to tokens 0..L-1.
 
 Every function is pinned in tests/test_oracle.py against closed forms,
-identities the pages state, or library routines; none is "parity unpinned".
+identities the pages state, fixed bit patterns, library routines, or inputs
+built so that the right answer is known by construction (selection
+matrices), and each pin is shown to fail on a planted mistake; none is
+"parity unpinned".  The two whole-workload drivers (decode_workload,
+multi_decode_workload) only gather rows and loop over sequences around the
+pinned per-sequence functions; they are checked against each other and
+against the generator's token order.
 """
 from __future__ import annotations
 
@@ -259,6 +265,66 @@ def multi_decode_seq(c: np.ndarray, k_rope: np.ndarray, q_nope: np.ndarray, q_pe
     return {k: np.stack(v) for k, v in res.items()}
 
 
+def causal_prefill_seq(c: np.ndarray, k_rope: np.ndarray, q_nope: np.ndarray, q_pe: np.ndarray,
+                       w_uk: np.ndarray, w_uv: np.ndarray, scale: float, rope_base: float,
+                       heads: Optional[Iterable[int]] = None) -> Dict[str, np.ndarray]:
+    """multi_decode_seq for many query tokens: the naive path with each head's
+    keys and values materialised once for the whole sequence.
+
+    The T newest tokens of a sequence of L cached rows attend causally: token t
+    at position p_t = L - T + t sees rows 0 .. p_t ([V2-解析] 2.2.1.2: a query
+    sees only the tokens up to its own).  k^C_{j,i} = W^UK_i c_j and
+    v^C_{j,i} = W^UV_i c_j ([V2-解析] 2.2.1.1) do not depend on the query, so
+    they are formed once; rows after p_t get score -inf.  q_nope [T, n_h, d_h],
+    q_pe [T, n_h, d_h^R] (not yet encoded).  Returns o [T, n, d_h],
+    o_latent [T, n, d_c], lse [T, n] for the selected heads.
+    """
+    c = np.asarray(c, F64)
+    k_rope = np.asarray(k_rope, F64)
+    L, d_c = c.shape
+    T, n_h, d_h = q_nope.shape
+    heads = list(range(n_h)) if heads is None else list(heads)
+    pos = L - T + np.arange(T)                                   # p_t
+    visible = np.arange(L)[None, :] <= pos[:, None]             # [T, L]
+    out = {k: [] for k in ("o", "o_latent", "lse")}
+    for i in heads:
+        kC = c @ _head_rows(w_uk, i, d_h).astype(F64).T          # [L, d_h]
+        vC = c @ _head_rows(w_uv, i, d_h).astype(F64).T
+        K = np.concatenate([kC, k_rope], axis=1)                 # [L, d_h + d_h^R]
+        q = np.concatenate([np.asarray(q_nope[:, i], F64),
+                            rope(np.asarray(q_pe[:, i], F64), pos, rope_base)], axis=1)   # [T, .]
+        s = np.where(visible, (q @ K.T) * scale, -np.inf)         # [T, L]
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        z = e.sum(axis=1, keepdims=True)
+        a = e / z
+        out["o"].append(a @ vC)
+        out["o_latent"].append(a @ c)
+        out["lse"].append((m + np.log(z))[:, 0])
+    return {"o": np.stack(out["o"], axis=1), "o_latent": np.stack(out["o_latent"], axis=1),
+            "lse": np.stack(out["lse"], axis=1)}
+
+
+def causal_prefill_workload(wl, q_nope: np.ndarray, q_pe: np.ndarray,
+                            seqs: Optional[Iterable[int]] = None, heads=None) -> Dict[str, np.ndarray]:
+    """causal_prefill_seq over the selected sequences of a workload (inputs as
+    for multi_decode_workload)."""
+    cfg = wl.cfg
+    bf = cfg.dtype == "bf16"
+    seqs = range(cfg.batch) if seqs is None else list(seqs)
+    w_uk = to_f64(wl.w_uk, bf)
+    w_uv = to_f64(wl.w_uv, bf)
+    scale = softmax_scale(cfg.d_head, cfg.d_rope)
+    res = {k: [] for k in ("o", "o_latent", "lse")}
+    for b in seqs:
+        rows = to_f64(gather_rows(wl.cache, wl.block_table[b], int(wl.seq_lens[b]), cfg.page_size), bf)
+        r = causal_prefill_seq(rows[:, :cfg.d_latent], rows[:, cfg.d_latent:], to_f64(q_nope[b], bf),
+                               to_f64(q_pe[b], bf), w_uk, w_uv, scale, cfg.rope_base, heads=heads)
+        for k in res:
+            res[k].append(r[k])
+    return {k: np.stack(v) for k, v in res.items()}
+
+
 def multi_decode_workload(wl, q_nope: np.ndarray, q_pe: np.ndarray,
                           seqs: Optional[Iterable[int]] = None, heads=None) -> Dict[str, np.ndarray]:
     """multi_decode_seq over the selected sequences of a workload; q_nope
@@ -300,8 +366,31 @@ def cache_rows_from_hidden(h: np.ndarray, w_dkv: np.ndarray, w_kr: np.ndarray,
 
 
 def query_from_hidden(h_t: np.ndarray, w_q: np.ndarray, w_qr: np.ndarray, n_heads: int):
-    """q^C_i and the (not yet encoded) q^R_i of one token without query compression."""
+    """q^C_i and the (not yet encoded) q^R_i of one token without query compression.
+
+    W^Q [n_h d_h, d_model] and W^QR [n_h d_h^R, d_model] map column vectors;
+    head i owns rows i*d_h .. i*d_h + d_h - 1 (and i*d_h^R .. of W^QR), the
+    same convention as W^UK ([V2-解析] 2.2.1.1, per-head up-projection).
+    """
     h_t = np.asarray(h_t, F64)
     qn = (np.asarray(w_q, F64) @ h_t).reshape(n_heads, -1)
     qp = (np.asarray(w_qr, F64) @ h_t).reshape(n_heads, -1)
+    return qn, qp
+
+
+def query_from_latent(h_t: np.ndarray, w_dq: np.ndarray, w_uq: np.ndarray, w_qr: np.ndarray,
+                      n_heads: int):
+    """q^C_i and the (not yet encoded) q^R_i of one token with query compression.
+
+    The query is compressed like the keys and values, down and then up
+    ([V2-解析] 2.2.1.2): c^Q = W^DQ h_t, q^C = W^UQ c^Q ([V2-解析] 2.2.2, the
+    absorbed score written with W^UQ c^Q).  The decoupled per-head q^R is read
+    from the same compressed latent, q^R = W^QR c^Q (the pages' formula for
+    it is lost; this is the reading that keeps the whole query on the
+    compressed path).  W^DQ [d_cq, d_model], W^UQ [n_h d_h, d_cq],
+    W^QR [n_h d_h^R, d_cq]; no normalisation of c^Q (the pages name none).
+    """
+    c_q = np.asarray(w_dq, F64) @ np.asarray(h_t, F64)
+    qn = (np.asarray(w_uq, F64) @ c_q).reshape(n_heads, -1)
+    qp = (np.asarray(w_qr, F64) @ c_q).reshape(n_heads, -1)
     return qn, qp

@@ -267,6 +267,39 @@ def hidden_recipe(cfg: MLAConfig, length: int) -> dict:
     return out
 
 
+def chain_recipe(cfg: MLAConfig, lens) -> dict:
+    """Everything one decode step derives from hidden states, float32 draws.
+
+    h_b [L_b, d_model] ~ N(0, 1) for every sequence b (its tokens 0 .. L_b - 1;
+    the query is token L_b - 1), and every projection ~ N(0, 1/fan_in), each
+    mapping column vectors: W^DKV [d_c, d_model], W^KR [d_h^R, d_model],
+    W^UK and W^UV [n_h d_h, d_c]; with a query latent of width d_cq
+    (cfg.q_latent): W^DQ [d_cq, d_model], W^UQ [n_h d_h, d_cq],
+    W^QR [n_h d_h^R, d_cq]; without one: W^Q [n_h d_h, d_model],
+    W^QR [n_h d_h^R, d_model].  Streams: key (6,) for the weights, (7, b) for
+    the hidden states of sequence b.
+    """
+    r = _rng(cfg, 6)
+    dm, H = cfg.d_model, cfg.n_heads
+
+    def w(rows, fan_in):
+        return (r.standard_normal((rows, fan_in), dtype=np.float32) /
+                np.float32(np.sqrt(fan_in)))
+
+    out = {"w_dkv": w(cfg.d_latent, dm), "w_kr": w(cfg.d_rope, dm),
+           "w_uk": w(H * cfg.d_head, cfg.d_latent), "w_uv": w(H * cfg.d_head, cfg.d_latent)}
+    if cfg.q_latent:
+        out["w_dq"] = w(cfg.q_latent, dm)
+        out["w_uq"] = w(H * cfg.d_head, cfg.q_latent)
+        out["w_qr"] = w(H * cfg.d_rope, cfg.q_latent)
+    else:
+        out["w_q"] = w(H * cfg.d_head, dm)
+        out["w_qr"] = w(H * cfg.d_rope, dm)
+    out["h"] = [_rng(cfg, 7, b).standard_normal((int(n), dm), dtype=np.float32)
+                for b, n in enumerate(lens)]
+    return out
+
+
 def append_recipe(cfg: MLAConfig, batch: int) -> dict:
     """Inputs of the cache write of one new token per sequence, float64:
     h [batch, d_model] ~ N(0, 1), W^DKV [d_c, d_model] and W^KR [d_h^R, d_model]

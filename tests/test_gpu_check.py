@@ -130,7 +130,7 @@ def test_debug_switch_raises_before_the_launch(mla, monkeypatch):
     q2 = q_abs.unsqueeze(1).expand(-1, 2, -1, -1).contiguous()
     with pytest.raises(mla.MlaError, match="first in sequence 1"):
         mla.decode_splitkv_multi(dims, q2, cache, bad_bt, dev["seq_lens"], it_d)
-    tickets = torch.zeros(len(lens), dtype=torch.int32, device="cuda")
+    tickets = torch.zeros(2 * len(lens), dtype=torch.int32, device="cuda")  # 2 per sequence, as the ABI needs
     with pytest.raises(mla.MlaError, match="first in sequence 1"):
         mla.decode_merged(dims, q_abs, cache, bad_bt, dev["seq_lens"], it_d, of_d, tickets)
     q_nope = dev["q_nope"].unsqueeze(1).contiguous()

@@ -57,6 +57,59 @@ def test_prefill_against_oracle(gpu_lib, name, cfg, lens, T, heads):
     assert_lse(lse[:, :, h], ref["lse"])
 
 
+# The sizes the bench times: a workgroup takes 128 query tokens (four waves of
+# 32), so these fill every wave, several workgroups and a ragged last one.
+# The oracle forms each head's keys and values once (causal_prefill_workload).
+LARGE = [
+    # name, config, lengths, q_len, sampled heads
+    ("h128_T128_whole_and_long", small(V2, "pfL1", 2, permute_pages=True), [8200, 128], 128,
+     [0, 77, 127]),
+    ("h128_T129_ragged", small(V2, "pfL2", 1, permute_pages=True), [8300], 129, [3, 64]),
+    ("h128_T256", small(V2, "pfL3", 1, permute_pages=True), [8192], 256, [10, 100]),
+    ("h16_T512", small(LITE, "pfL4", 1, permute_pages=True), [4096], 512, None),
+    ("h128_T2048", small(V2, "pfL5", 1, permute_pages=True), [8192], 2048, [0, 127]),
+]
+
+
+@pytest.mark.parametrize("name,cfg,lens,T,heads", LARGE, ids=[c[0] for c in LARGE])
+def test_prefill_benchmarked_sizes(gpu_lib, name, cfg, lens, T, heads):
+    from oracle import causal_prefill_workload
+    wl = generate(cfg, lens=np.array(lens, np.int32))
+    say(f"[prefill {name}] lens {lens} q_len {T}")
+    dev = upload(wl)
+    qn, qp, out, lse = run_prefill(wl, dev, T)
+    h = list(range(cfg.n_heads)) if heads is None else heads
+    ref = causal_prefill_workload(wl, qn, qp, heads=h)
+    assert_close(out[:, :, h], ref["o"], "out")
+    assert_lse(lse[:, :, h], ref["lse"])
+
+
+def test_prefill_reference_moves(gpu_lib):
+    """Key tiles after the first 1024 rows carry latents scaled by 8, so the
+    queries' score maxima grow by far more than 2^8 after the first tiles and
+    the kernel's per-block softmax reference must move (and rescale)."""
+    from oracle import causal_prefill_workload
+    from synth import bf16_bits_to_f32, f32_to_bf16_bits
+    cfg = small(V2, "pfjump", 1, permute_pages=True)
+    L, T = 2100, 300
+    wl = generate(cfg, lens=np.array([L], np.int32))
+    for j in range(1024, L):
+        p, s = wl.block_table[0, j // 64], j % 64
+        row = bf16_bits_to_f32(wl.cache[p, s])
+        row[:512] *= 8.0
+        wl.cache[p, s] = f32_to_bf16_bits(row)
+    say("[prefill reference moves]")
+    dev = upload(wl)
+    qn, qp, out, lse = run_prefill(wl, dev, T)
+    h = [0, 31, 64, 127]
+    ref = causal_prefill_workload(wl, qn, qp, heads=h)
+    s_jump = float(np.max(ref["lse"]) - np.min(ref["lse"]))
+    say(f"  lse spread {s_jump:.1f}")
+    assert_close(out[:, :, h], ref["o"], "out")
+    # scores 8x the usual carry 8x the bf16 rounding error of the query
+    assert_lse(lse[:, :, h], ref["lse"], tol=2e-3 * float(np.abs(ref["lse"]).max()))
+
+
 def test_prefill_matches_absorbed_multi_token(gpu_lib):
     """The two paths on one input: materialised K/V and the absorbed decode."""
     import torch

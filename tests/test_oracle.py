@@ -539,3 +539,92 @@ def test_planted_mistake_is_caught(monkeypatch, target, replacement, check):
     monkeypatch.setattr(O, target, replacement)
     with pytest.raises(AssertionError):
         check()
+
+
+# ---------------------------------------------------------------------------
+# causal prefill with K/V materialised once: the per-token path, many tokens
+# ---------------------------------------------------------------------------
+def check_prefill_equals_multi():
+    """causal_prefill_workload gives what the pinned per-token path gives
+    (each token a single-query naive decode over its own prefix)."""
+    from synth import query_multi
+    for base, lens, T, heads in ((TINY, (37, 9), 9, None),
+                                 (CONFIGS["v2lite_b32_l4096"], (70, 33), 33, [0, 5, 15])):
+        cfg = small(base, "pfo", len(lens))
+        wl = generate(cfg, lens=np.array(lens, np.int32))
+        qs = [query_multi(cfg, b, T) for b in range(cfg.batch)]
+        qn, qp = np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs])
+        a = O.causal_prefill_workload(wl, qn, qp, heads=heads)
+        b = O.multi_decode_workload(wl, qn, qp, heads=heads)
+        for k in ("o", "o_latent", "lse"):
+            assert a[k].shape == b[k].shape, k
+            assert rel(a[k], b[k]) < 1e-12, k
+
+
+def check_prefill_causal():
+    """Token 0 never sees the rows after its own position; the last token sees all."""
+    from synth import query_multi
+    T = 4
+    cfg = small(TINY, "pfc", 1)
+    wl = generate(cfg, lens=np.array([23], np.int32))
+    qn, qp = (x[None] for x in query_multi(cfg, 0, T))
+    a = O.causal_prefill_workload(wl, qn, qp)
+    L = 23
+    for j in range(L - T + 1, L):
+        wl.cache[wl.block_table[0, j // 64], j % 64] *= np.float32(3.0)
+    b = O.causal_prefill_workload(wl, qn, qp)
+    assert np.array_equal(b["o"][0, 0], a["o"][0, 0]) and np.array_equal(b["lse"][0, 0], a["lse"][0, 0])
+    assert not np.allclose(b["o"][0, T - 1], a["o"][0, T - 1])
+
+
+def test_prefill_equals_multi():
+    check_prefill_equals_multi()
+
+
+def test_prefill_causal():
+    check_prefill_causal()
+
+
+def _prefill_excludes_self(c, k_rope, q_nope, q_pe, w_uk, w_uv, scale, rope_base, heads=None):
+    # token t sees rows 0 .. p_t - 1 only (with a guard row so the first token is defined)
+    L, T = c.shape[0], q_nope.shape[0]
+    res = {k: [] for k in ("o", "o_latent", "lse")}
+    for t in range(T):
+        p = L - T + t
+        r = O.naive_decode_seq(c[:max(p, 1)], k_rope[:max(p, 1)], q_nope[t], q_pe[t], p, w_uk, w_uv,
+                               scale, rope_base, heads=heads)
+        for k in res:
+            res[k].append(r[k])
+    return {k: np.stack(v) for k, v in res.items()}
+
+
+def _prefill_unmasked(c, k_rope, q_nope, q_pe, w_uk, w_uv, scale, rope_base, heads=None):
+    L, T = c.shape[0], q_nope.shape[0]
+    res = {k: [] for k in ("o", "o_latent", "lse")}
+    for t in range(T):
+        r = O.naive_decode_seq(c, k_rope, q_nope[t], q_pe[t], L - T + t, w_uk, w_uv, scale, rope_base,
+                               heads=heads)
+        for k in res:
+            res[k].append(r[k])
+    return {k: np.stack(v) for k, v in res.items()}
+
+
+def _prefill_position_off_by_one(c, k_rope, q_nope, q_pe, w_uk, w_uv, scale, rope_base, heads=None):
+    L, T = c.shape[0], q_nope.shape[0]
+    res = {k: [] for k in ("o", "o_latent", "lse")}
+    for t in range(T):
+        p = L - T + t
+        r = O.naive_decode_seq(c[:p + 1], k_rope[:p + 1], q_nope[t], q_pe[t], p + 1, w_uk, w_uv, scale,
+                               rope_base, heads=heads)
+        for k in res:
+            res[k].append(r[k])
+    return {k: np.stack(v) for k, v in res.items()}
+
+
+@pytest.mark.parametrize("replacement", [_prefill_excludes_self, _prefill_unmasked,
+                                         _prefill_position_off_by_one])
+def test_planted_prefill_mistake_is_caught(monkeypatch, replacement):
+    monkeypatch.setattr(O, "causal_prefill_seq", replacement)
+    with pytest.raises(AssertionError):
+        check_prefill_equals_multi()
+        check_prefill_causal()
