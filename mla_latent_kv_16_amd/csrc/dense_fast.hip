@@ -395,14 +395,28 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
 
 }  // namespace
 
+int64_t absorb_fast_groups(int64_t batch) { return (batch + 63) / 64; }
+
+int64_t out_proj_fast_groups(int64_t rows) { return (rows + 31) / 32; }
+
+int combine_out_proj_rows_per_group(int n_heads, int64_t rows) {
+  // Query rows per workgroup: the largest of 32, 16, 8 that still gives
+  // 256 workgroups (one per CU), else 8.  A workgroup pulls every item's
+  // partial of its rows through one CU, so few large workgroups are slow: at
+  // 16 heads x 32 rows, 16 workgroups of 32 rows took 26 us.
+  for (int cand : {32, 16})
+    if (n_heads * ((rows + cand - 1) / cand) >= 256) return cand;
+  return 8;
+}
+
 hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const void* q_pe,
                        const int32_t* positions, const void* w_uk, void* q_abs,
                        hipStream_t stream) {
-  const int groups = (batch + 63) / 64;
+  const int64_t groups = absorb_fast_groups(batch);
   if (groups > 65535 || d.n_heads % 8 != 0) return hipErrorInvalidValue;
   RopeTheta theta;
   for (int k = 0; k < kDr / 2; ++k) theta.t[k] = pow(d.rope_base, -2.0 * k / kDr);
-  hipLaunchKernelGGL(absorb_kernel, dim3(d.n_heads * 4, groups), dim3(256), 0, stream, batch,
+  hipLaunchKernelGGL(absorb_kernel, dim3(d.n_heads * 4, static_cast<uint32_t>(groups)), dim3(256), 0, stream, batch,
                      d.n_heads, theta, static_cast<const uint16_t*>(q_nope),
                      static_cast<const uint16_t*>(q_pe), positions,
                      static_cast<const char*>(w_uk), static_cast<uint16_t*>(q_abs));
@@ -412,9 +426,9 @@ hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const v
 hipError_t out_proj_fast(const mla_dims& d, int batch, const float* o_latent, const void* w_uv,
                          float* out, hipStream_t stream) {
   constexpr int kOutRows = 32;
-  const int groups = (batch + kOutRows - 1) / kOutRows;
+  const int64_t groups = out_proj_fast_groups(batch);
   if (groups > 65535 || d.n_heads % 8 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((out_proj_kernel<false, kOutRows>), dim3(d.n_heads, groups), dim3(kOutThreads), 0, stream, batch,
+  hipLaunchKernelGGL((out_proj_kernel<false, kOutRows>), dim3(d.n_heads, static_cast<uint32_t>(groups)), dim3(kOutThreads), 0, stream, batch,
                      d.n_heads, 1, nullptr, nullptr, nullptr, const_cast<float*>(o_latent), nullptr,
                      static_cast<const uint16_t*>(w_uv), out);
   return hipGetLastError();
@@ -425,17 +439,7 @@ hipError_t combine_out_proj_fast(const mla_dims& d, int batch, int q_len, const 
                                  float* out, float* o_latent, float* lse, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(batch) * q_len;
   if (d.n_heads % 8 != 0) return hipErrorInvalidValue;
-  // Query rows per workgroup: the largest of 32, 16, 8 that still gives
-  // 256 workgroups (one per CU), else 8.  A workgroup pulls every item's
-  // partial of its rows through one CU, so few large workgroups are slow: at
-  // 16 heads x 32 rows, 16 workgroups of 32 rows took 26 us.
-  int R = 8;
-  for (int cand : {32, 16}) {
-    if (d.n_heads * ((rows + cand - 1) / cand) >= 256) {
-      R = cand;
-      break;
-    }
-  }
+  const int R = combine_out_proj_rows_per_group(d.n_heads, rows);
   const int64_t groups = (rows + R - 1) / R;
   if (groups > 65535) return hipErrorInvalidValue;
   const dim3 grid(d.n_heads, static_cast<uint32_t>(groups));

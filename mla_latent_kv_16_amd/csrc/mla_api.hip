@@ -77,8 +77,10 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, const void* q_nope,
   if (static_cast<int64_t>(batch) * dims->n_heads > (int64_t{1} << 31)) return MLA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
-  if (is_fast_shape(*dims))
+  if (is_fast_shape(*dims)) {
+    if (absorb_fast_groups(batch) > 65535) return MLA_ERR_UNSUPPORTED;
     return launched(absorb_fast(*dims, batch, q_nope, q_pe, positions, w_uk, q_abs, st));
+  }
   if (batch > 65535) return MLA_ERR_UNSUPPORTED;
   return launched(absorb_generic(*dims, batch, q_nope, q_pe, positions, w_uk, q_abs, st));
 }
@@ -189,6 +191,10 @@ mla_status mla_decode_merged(const mla_dims* dims, int32_t batch, const void* q_
       !al4(block_table) || !al4(seq_lens) || !al4(items) || !al4(split_offsets) || !al4(tickets) ||
       (lse && !al4(lse)))
     return MLA_ERR_INVALID_ARG;
+  // partial rows and workgroup counts stay within 32-bit grid limits
+  if (static_cast<int64_t>(num_items) * 2 > INT32_MAX ||
+      static_cast<int64_t>(batch) * dims->n_heads > (int64_t{1} << 31))
+    return MLA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
   if (is_fast_shape(*dims))
@@ -265,8 +271,10 @@ mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const float* o_late
   if (!al16(o_latent) || !al16(w_uv) || !al16(out)) return MLA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
-  if (is_fast_shape(*dims))
+  if (is_fast_shape(*dims)) {
+    if (out_proj_fast_groups(batch) > 65535) return MLA_ERR_UNSUPPORTED;
     return launched(out_proj_fast(*dims, batch, o_latent, w_uv, out, st));
+  }
   if (batch > 65535) return MLA_ERR_UNSUPPORTED;
   return launched(out_proj_generic(*dims, batch, o_latent, w_uv, out, st));
 }
@@ -318,7 +326,8 @@ mla_status mla_combine_out_proj(const mla_dims* dims, int32_t batch, int32_t q_l
   if (rows * dims->n_heads > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (is_fast_shape(*dims)) {
-    if ((rows + 63) / 64 > 65535) return MLA_ERR_UNSUPPORTED;
+    const int R = combine_out_proj_rows_per_group(dims->n_heads, rows);
+    if ((rows + R - 1) / R > 65535) return MLA_ERR_UNSUPPORTED;
     (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
     return launched(combine_out_proj_fast(*dims, batch, q_len, split_offsets, o_part, lse_part, w_uv,
                                           out, o_latent, lse, st));

@@ -31,6 +31,12 @@ hipError_t combine_generic(const mla_dims& d, int batch, int q_len, const int32_
 hipError_t out_proj_generic(const mla_dims& d, int batch, const float* o_latent, const void* w_uv,
                             float* out, hipStream_t stream);
 
+// Grid sizes of the fast dense kernels (grid y is at most 65535): workgroups
+// along the rows for absorb and out_proj, and the rows per workgroup the fused
+// merge + out_proj picks.
+int64_t absorb_fast_groups(int64_t batch);
+int64_t out_proj_fast_groups(int64_t rows);
+int combine_out_proj_rows_per_group(int n_heads, int64_t rows);
 hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const void* q_pe,
                        const int32_t* positions, const void* w_uk, void* q_abs,
                        hipStream_t stream);

@@ -279,3 +279,23 @@ def test_record_calls_does_not_nest():
     # the outer block ended cleanly: a new recording starts empty
     with mla.record_calls() as again:
         assert again == []
+
+
+def test_grid_limits_are_unsupported_not_hip_errors(lib):
+    """Sizes whose fast-path grid would pass 65535 workgroups along y come back
+    as MLA_ERR_UNSUPPORTED from the host checks, before any launch."""
+    # mla_absorb_q: 64 query rows per workgroup
+    assert lib.mla_absorb_q(_d(), 65535 * 64 + 1, A, A, A, A, A, None) == UNSUPPORTED
+    # mla_out_proj: 32 rows per workgroup
+    assert lib.mla_out_proj(_d(), 65535 * 32 + 1, A, A, A, None) == UNSUPPORTED
+    # mla_combine_out_proj: at 128 heads 32 rows per workgroup once there are
+    # enough rows; rows = batch * q_len
+    good = [A, A, A, A, A, None, None, None]
+    assert lib.mla_combine_out_proj(_d(), 65535 * 32 + 1, 1, *good) == UNSUPPORTED
+    assert lib.mla_combine_out_proj(_d(), (65535 * 32 + 2) // 2, 2, *good) == UNSUPPORTED
+    # at 16 heads too
+    lite = mla.Dims(16, 128, 512, 64)
+    assert lib.mla_combine_out_proj(_d(lite), 65535 * 32 + 1, 1, *good) == UNSUPPORTED
+    # mla_decode_merged: two workgroups per item must fit a 32-bit grid
+    args = [A, A, 10, A, 4, A, A, 2 ** 30, A, A, A, A, A, None, None]
+    assert lib.mla_decode_merged(_d(), 2, *args) == UNSUPPORTED
