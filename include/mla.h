@@ -17,6 +17,7 @@
  *   mla_prefill_naive   q_len query tokens per sequence through the materialised
  *                       per-head K/V path (for long chunks, where it costs less)
  *   mla_append_kv       write the decoded token's [c^KV | RoPE(k^R)] row into the cache
+ *   mla_append_kv_noalloc  the same without a workspace argument (static scratch)
  *   mla_out_proj        o_i = W^UV_i o~_i                                    (per head i)
  *   mla_combine_out_proj  mla_combine and mla_out_proj in one launch
  *
@@ -34,7 +35,9 @@
  * Memory: every pointer argument, unless its name ends in _host, is a device
  *   pointer on the current HIP device.  The caller allocates and owns all
  *   buffers; the library allocates nothing, frees nothing and keeps no pointer
- *   after a call returns.  Calls keep no state between them.
+ *   after a call returns.  Calls keep no state between them.  The one
+ *   exception is mla_append_kv_noalloc, whose scratch is a static device
+ *   buffer of the library (see there).
  * Streams: `stream` is a hipStream_t (NULL = the default stream).  Kernels are
  *   enqueued on it and the call returns without synchronising.
  * Errors: arguments are checked on the host before any HIP call; a failed check
@@ -319,6 +322,31 @@ mla_status mla_append_kv(const mla_dims* dims, int32_t d_model, int32_t batch, c
 
 /* Bytes of workspace mla_append_kv needs; -1 on bad arguments.  Host only. */
 int64_t mla_append_kv_workspace_bytes(const mla_dims* dims, int32_t d_model, int32_t batch);
+
+/* mla_append_kv without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (minus the workspace), same
+ * kernels and the same result bits as mla_append_kv.  The K-slice partial sums
+ * go to a static device buffer of the library (mla_append_kv_noalloc_max_bytes()
+ * = 8 MiB per device, held until the process ends); the call allocates
+ * nothing.  Its device address is looked up once per device, on the first call
+ * made with that device current.  Every element of the buffer that a call
+ * reads is written earlier in the same call, so nothing needs clearing between
+ * calls.  All calls on one device share the buffer: calls that can overlap in
+ * time on one device (different streams, or different host threads without
+ * ordering) race and must not be made.
+ * Errors: as for mla_append_kv; MLA_ERR_WORKSPACE when
+ * mla_append_kv_workspace_bytes(dims, d_model, batch) exceeds the buffer
+ * (e.g. more than 455 tokens at d_model 5120 with d_c + d_h^R = 576);
+ * MLA_ERR_HIP if the buffer's address cannot be found on the current device. */
+mla_status mla_append_kv_noalloc(const mla_dims* dims, int32_t d_model, int32_t batch, const void* h,
+                                 const void* w_dkv, const void* w_kr, const int32_t* positions,
+                                 int32_t rms_norm, float eps, void* kv_cache, int32_t num_pages,
+                                 const int32_t* block_table, int32_t max_pages_per_seq,
+                                 void* stream);
+
+/* Size in bytes of mla_append_kv_noalloc's static buffer (per device). */
+int64_t mla_append_kv_noalloc_max_bytes(void);
 
 /* Debug check of the device data the decode and prefill entry points take on
  * trust.  Page "DeepSeek V2 技术解析" 2.1.1 (paged KV memory): sequence b reads

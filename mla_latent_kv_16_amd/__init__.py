@@ -7,6 +7,7 @@ been built -- there is no fallback.
 
 Entry points mirror include/mla.h:
     absorb_q, plan_splits, decode_splitkv, combine, decode_merged, out_proj, append_kv,
+    append_kv_noalloc,
     decode_splitkv_multi, combine_multi, combine_out_proj, prefill_naive
 plus `decode_step`, which runs the four device steps in order, and
 `check_paging`, a device check of the lengths and block-table entries.
@@ -28,7 +29,7 @@ from typing import Optional, Tuple
 import numpy as np
 
 __all__ = ["MlaError", "Dims", "load", "lib_path", "absorb_q", "plan_splits", "decode_splitkv",
-           "decode_merged", "append_kv", "decode_splitkv_multi", "combine_multi", "combine_out_proj",
+           "decode_merged", "append_kv", "append_kv_noalloc", "decode_splitkv_multi", "combine_multi", "combine_out_proj",
            "prefill_naive",
            "combine", "out_proj", "decode_step", "fast_path", "version", "record_calls", "replay_calls",
            "check_paging", "BF16", "F32"]
@@ -117,6 +118,9 @@ def load():
         "mla_append_kv": (i32, [pd, i32, i32, vp, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp, i32,
                                  vp, ctypes.c_int64, vp]),
         "mla_append_kv_workspace_bytes": (ctypes.c_int64, [pd, i32, i32]),
+        "mla_append_kv_noalloc": (i32, [pd, i32, i32, vp, vp, vp, vp, i32, ctypes.c_float, vp, i32, vp,
+                                         i32, vp]),
+        "mla_append_kv_noalloc_max_bytes": (ctypes.c_int64, []),
         "mla_check_paging": (i32, [pd, i32, i32, vp, i32, vp, i32, vp, vp]),
         "mla_status_string": (ctypes.c_char_p, [i32]),
         "mla_version": (i32, []),
@@ -431,6 +435,30 @@ def append_kv(dims: Dims, h, w_dkv, w_kr, positions, kv_cache, block_table, rms_
         _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
         _ptr(workspace, None, None, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)), "mla_append_kv")
+    return kv_cache
+
+
+def append_kv_noalloc(dims: Dims, h, w_dkv, w_kr, positions, kv_cache, block_table,
+                      rms_norm: bool = True, eps: float = 1e-6, stream=None):
+    """append_kv with the partial sums in the library's static device buffer
+    (no workspace; nothing allocated).  Calls that overlap on one device race."""
+    torch = _torch()
+    dt = _store_dtype(dims)
+    B, d_model = h.shape
+    L = load()
+    need = L.mla_append_kv_workspace_bytes(ctypes.byref(dims.c()), d_model, B)
+    cap = L.mla_append_kv_noalloc_max_bytes()
+    if need > cap:
+        raise MlaError(-3, f"mla_append_kv_noalloc: {B} tokens at d_model {d_model} need {need} "
+                           f"bytes of scratch, the static buffer holds {cap}")
+    num_pages = kv_cache.shape[0]
+    _check(L.mla_append_kv_noalloc(
+        ctypes.byref(dims.c()), d_model, B, _ptr(h, dt, (B, d_model), "h"),
+        _ptr(w_dkv, dt, (dims.d_latent, d_model), "w_dkv"), _ptr(w_kr, dt, (dims.d_rope, d_model), "w_kr"),
+        _ptr(positions, torch.int32, (B,), "positions"), int(bool(rms_norm)), float(eps),
+        _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
+        _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
+        _stream(stream)), "mla_append_kv_noalloc")
     return kv_cache
 
 

@@ -22,6 +22,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "device_common.h"
 #include "mla_internal.h"
@@ -141,7 +142,34 @@ __global__ __launch_bounds__(1024) void append_finish(
   }
 }
 
+// Scratch of mla_append_kv_noalloc: the K-slice partial sums live in this
+// static array instead of a caller's workspace.  Every device the library
+// runs on holds its own copy until the process ends.  In host code `scratch`
+// is only a stand-in for the symbol: its device address on the current device
+// comes from hipGetSymbolAddress (scratch_on_current_device).
+static __device__ __align__(256) float scratch[kAppendScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+hipError_t scratch_on_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<float*>(g_scratch_ptr[dev]);
+  return hipSuccess;
+}
 
 int append_slices(int d_model) { return (d_model + kKSlice - 1) / kKSlice; }
 

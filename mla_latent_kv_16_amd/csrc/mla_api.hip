@@ -263,6 +263,32 @@ mla_status mla_append_kv(const mla_dims* dims, int32_t d_model, int32_t batch, c
                             static_cast<float*>(workspace), st));
 }
 
+mla_status mla_append_kv_noalloc(const mla_dims* dims, int32_t d_model, int32_t batch, const void* h,
+                                 const void* w_dkv, const void* w_kr, const int32_t* positions,
+                                 int32_t rms_norm, float eps, void* kv_cache, int32_t num_pages,
+                                 const int32_t* block_table, int32_t max_pages_per_seq,
+                                 void* stream) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  if (d_model < 1 || batch < 1 || num_pages < 1 || max_pages_per_seq < 1) return MLA_ERR_INVALID_ARG;
+  if (!h || !w_dkv || !w_kr || !positions || !kv_cache || !block_table) return MLA_ERR_INVALID_ARG;
+  if (rms_norm && !(eps > 0.f && isfinite(eps))) return MLA_ERR_INVALID_ARG;
+  if (!al16(h) || !al16(w_dkv) || !al16(w_kr) || !al16(kv_cache) || !al4(positions) ||
+      !al4(block_table))
+    return MLA_ERR_INVALID_ARG;
+  if (d_model > (1 << 20) || batch > 65535) return MLA_ERR_UNSUPPORTED;
+  if (mla_append_kv_workspace_bytes(dims, d_model, batch) > kAppendScratchBytes) return MLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+  float* ws = nullptr;
+  mla_status r = launched(scratch_on_current_device(&ws));
+  if (r != MLA_OK) return r;
+  return launched(append_kv(*dims, d_model, batch, h, w_dkv, w_kr, positions, rms_norm != 0, eps,
+                            kv_cache, block_table, max_pages_per_seq, ws, st));
+}
+
+int64_t mla_append_kv_noalloc_max_bytes(void) { return kAppendScratchBytes; }
+
 mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const float* o_latent,
                         const void* w_uv, float* out, void* stream) {
   mla_status s = check_dims(dims);

@@ -72,6 +72,10 @@ hipError_t prefill_naive(const mla_dims& d, int batch, int q_len, const void* q_
 // Cache write of one token per sequence (append.hip); `ws` holds
 // append_slices(d_model) x batch x (d_latent + d_rope) floats.
 int append_slices(int d_model);
+// The static scratch of mla_append_kv_noalloc: its size, and its device
+// address on the current device (looked up once per device).
+constexpr int64_t kAppendScratchBytes = int64_t{8} << 20;
+hipError_t scratch_on_current_device(float** out);
 hipError_t append_kv(const mla_dims& d, int d_model, int batch, const void* h, const void* w_dkv,
                      const void* w_kr, const int32_t* positions, bool rms_norm, float eps,
                      void* kv_cache, const int32_t* block_table, int max_pages, float* ws,

@@ -281,6 +281,33 @@ def test_record_calls_does_not_nest():
         assert again == []
 
 
+def test_append_kv_noalloc_rejects_bad_arguments(lib):
+    f = lib.mla_append_kv_noalloc
+    cap = lib.mla_append_kv_noalloc_max_bytes()
+    assert cap == 8 << 20
+    fits = cap // (8 * 576 * 4)                    # tokens at d_model 5120
+    # d_model batch h w_dkv w_kr positions rms eps cache num_pages bt max_pages stream
+    good = [5120, fits, A, A, A, A, 1, 1e-6, A, 10, A, 4, None]
+    for i in (2, 3, 4, 5, 8, 10):                  # each pointer argument set to NULL
+        args = list(good)
+        args[i] = None
+        assert f(_d(), *args) == INVALID, i
+    for i, bad in ((0, 0), (1, 0), (9, 0), (11, 0)):   # sizes < 1
+        args = list(good)
+        args[i] = bad
+        assert f(_d(), *args) == INVALID, i
+    for i, bad in ((2, MIS), (8, MIS), (5, A + 2)):     # misaligned
+        args = list(good)
+        args[i] = bad
+        assert f(_d(), *args) == INVALID, i
+    args = list(good)
+    args[1] = fits + 1                             # more than the static buffer holds
+    assert f(_d(), *args) == WORKSPACE
+    args = list(good)
+    args[1] = 70000                                # beyond the grid limit
+    assert f(_d(), *args) == UNSUPPORTED
+
+
 def test_grid_limits_are_unsupported_not_hip_errors(lib):
     """Sizes whose fast-path grid would pass 65535 workgroups along y come back
     as MLA_ERR_UNSUPPORTED from the host checks, before any launch."""
