@@ -113,9 +113,19 @@ class HipTimingEvent:
             self._lib.hipEventDestroy(self.ev)
 
 
-def algorithmic(cfg, lens, q_len: int = 1):
-    """Algorithmic work of one step and of one decode launch (q_len query
-    tokens per sequence; token t of T sees L - T + t + 1 rows)."""
+def algorithmic(cfg, lens, q_len: int = 1, n_items: int = 0):
+    """Algorithmic work of one step and of its kernels (q_len query tokens per
+    sequence; token t of T sees L - T + t + 1 rows).
+
+    Decode bytes: every cached row once, q_abs read, the latent output written
+    once in bf16 (B T H d_c values), 4 bytes per page of block table.  The
+    split partials are implementation overhead and are not counted.  A second
+    figure counts the latent output at float32 with its lse (what a merged
+    result written once would take at float32) for comparison.
+    Step bytes: the step's own inputs and outputs (cache rows, block table,
+    q^C and q^R, W^UK and W^UV, the float32 output o); the intermediates
+    (q_abs, partials) are not counted.
+    """
     L = lens.astype(np.int64)
     B, H, T = cfg.batch, cfg.n_heads, q_len
     D = cfg.d_latent + cfg.d_rope
@@ -124,15 +134,26 @@ def algorithmic(cfg, lens, q_len: int = 1):
     decode_flop = seen * H * 2 * (D + cfg.d_latent)
     dense_flop = 2 * B * T * H * cfg.d_head * cfg.d_latent * 2   # absorb + out_proj
     cache_bytes = int(L.sum()) * D * 2
-    decode_bytes = (cache_bytes + B * T * H * D * 2 + B * T * H * (cfg.d_latent + 1) * 4
-                    + 4 * pages)
+    q_abs_bytes = B * T * H * D * 2
+    decode_bytes = cache_bytes + q_abs_bytes + B * T * H * cfg.d_latent * 2 + 4 * pages
+    decode_bytes_f32 = cache_bytes + q_abs_bytes + B * T * H * (cfg.d_latent + 1) * 4 + 4 * pages
+    w_bytes = H * cfg.d_head * cfg.d_latent * 2                  # one of W^UK, W^UV
+    q_in = B * T * H * (cfg.d_head + cfg.d_rope) * 2
+    out_bytes = B * T * H * cfg.d_head * 4
+    absorb_bytes = w_bytes + q_in + q_abs_bytes
+    merge_bytes = n_items * T * H * (cfg.d_latent + 1) * 4 + w_bytes + out_bytes
+    step_bytes = cache_bytes + 4 * pages + q_in + 2 * w_bytes + out_bytes
     return dict(decode_flop=decode_flop, step_flop=decode_flop + dense_flop,
-                cache_bytes=cache_bytes, decode_bytes=decode_bytes, pages=pages)
+                cache_bytes=cache_bytes, decode_bytes=decode_bytes, decode_bytes_f32=decode_bytes_f32,
+                absorb_bytes=absorb_bytes, merge_bytes=merge_bytes, step_bytes=step_bytes, pages=pages)
 
 
 def decode_source_hash() -> str:
-    p = os.path.join(ROOT, "mla_latent_kv_16_amd", "csrc", "decode_fast.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """sha256 (16 hex digits) of the decode kernel's sources."""
+    h = hashlib.sha256()
+    for f in ("decode_fast.hip", "decode_common.h"):
+        h.update(open(os.path.join(ROOT, "mla_latent_kv_16_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
@@ -153,11 +174,12 @@ def cpu_baseline(wl, budget_s: float = 20.0):
     """The fp64 oracle, untuned, on a bounded sample of the same workload."""
     from oracle import decode_workload
     cfg = wl.cfg
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+        threads = affinity
     order = list(range(cfg.batch))
     done, flop, t_total = [], 0, 0.0
     for b in order:
@@ -170,6 +192,7 @@ def cpu_baseline(wl, budget_s: float = 20.0):
             break
     toks = int(sum(int(wl.seq_lens[b]) for b in done))
     return {"value": flop / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "affinity_cores": int(affinity), "blas_threads": int(threads),
             "kind": "oracle",
             "sample": f"{len(done)} of {cfg.batch} sequences ({toks} cached tokens, all "
                       f"{cfg.n_heads} heads), naive fp64 path, {t_total:.1f} s wall",
@@ -262,6 +285,9 @@ def main():
                     help="query tokens per sequence (multi-token decode)")
     ap.add_argument("--slots", type=int, default=0,
                     help="workgroup slots the split plan aims at (default: the CU count)")
+    ap.add_argument("--in-order", action="store_true",
+                    help="plan for in-order dispatch and run the items in plan order "
+                         "(default: longest-first plan and dispatch, mla_plan_splits_ordered)")
     ap.add_argument("--fenced-events", action="store_true",
                     help="time with torch.cuda.Event (each record also writes back and invalidates caches)")
     ap.add_argument("--prefill", type=int, default=0, metavar="T",
@@ -327,8 +353,15 @@ def main():
                     rope_base=cfg.rope_base, dtype=mla.BF16 if bf else mla.F32)
     props = torch.cuda.get_device_properties(0)
     slots = args.slots or int(props.multi_processor_count)
-    # each item is decoded once per query token: plan for the CUs over T
-    items_h, offs_h = mla.plan_splits(dims, wl.seq_lens, max(1, slots // T))
+    # each item is decoded once per query token: plan for the CUs over T.  The
+    # single-token split decode runs the items longest first unless --in-order.
+    ordered = T == 1 and not args.merged and not args.in_order
+    order = None
+    if ordered:
+        items_h, offs_h, order_h = mla.plan_splits(dims, wl.seq_lens, max(1, slots // T), ordered=True)
+        order = torch.from_numpy(order_h).cuda()
+    else:
+        items_h, offs_h = mla.plan_splits(dims, wl.seq_lens, max(1, slots // T))
     items, offs = torch.from_numpy(items_h).cuda(), torch.from_numpy(offs_h).cuda()
     log(f"[bench] {props.name} {getattr(props, 'gcnArchName', '')}, {props.multi_processor_count} CUs, "
         f"plan for {slots} slots; {len(items_h)} work items, q_len {T}, {n_layers} layer(s)")
@@ -381,7 +414,8 @@ def main():
             names = ["absorb_q", "decode_splitkv", "combine", "out_proj"]
             fns = [absorb,
                    lambda: mla.decode_splitkv(dims, bufs["q_abs"], L["cache"], block_table, seq_lens,
-                                              items, bufs["o_part"], bufs["lse_part"], cur()),
+                                              items, bufs["o_part"], bufs["lse_part"], cur(),
+                                              order=order),
                    lambda: mla.combine(dims, offs, bufs["o_part"], bufs["lse_part"], B,
                                        bufs["o_latent"], bufs["lse"], cur()),
                    lambda: mla.out_proj(dims, bufs["o_latent"], L["w_uv"], bufs["out"], cur())]
@@ -389,7 +423,8 @@ def main():
             names = ["absorb_q", "decode_splitkv", "combine_out_proj"]
             fns = [absorb,
                    lambda: mla.decode_splitkv(dims, bufs["q_abs"], L["cache"], block_table, seq_lens,
-                                              items, bufs["o_part"], bufs["lse_part"], cur()),
+                                              items, bufs["o_part"], bufs["lse_part"], cur(),
+                                              order=order),
                    lambda: mla.combine_out_proj(dims, offs, bufs["o_part"], bufs["lse_part"],
                                                 L["w_uv"], B, bufs["out"], stream=cur())]
         return names, fns
@@ -537,9 +572,15 @@ def main():
         f"wall {wall * 1e3 / args.steps:.3f} ms/step")
     assert torch.isfinite(bufs["out"]).all().item(), "non-finite output"
 
-    work = algorithmic(cfg, wl.seq_lens, T)
+    work = algorithmic(cfg, wl.seq_lens, T, n_items=len(items_h))
     dec_s = dec_ms * 1e-3
     achieved = work["decode_bytes"] / dec_s / 1e9
+    # HBM fraction of each kernel's own bytes (event-bracketed times, so each
+    # includes the few microseconds an event between kernels adds)
+    kbytes = {"absorb_q": work["absorb_bytes"], names[1]: work["decode_bytes"],
+              "combine_out_proj": work["merge_bytes"]}
+    kernel_frac = {n: round(kbytes[n] / (v * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+                   for n, v in zip(names, k_ms) if n in kbytes}
     traffic = measured_traffic(cfg.name) if T == 1 and not args.merged else None
     result = {
         "metric": METRIC,
@@ -559,6 +600,7 @@ def main():
                    "total_tokens": int(wl.seq_lens.sum()), "n_heads": H, "d_head": cfg.d_head,
                    "d_latent": cfg.d_latent, "d_rope": cfg.d_rope, "page_size": cfg.page_size,
                    "work_items": int(len(items_h)), "q_len": T, "decode_entry": names[1],
+                   "dispatch": "longest-first" if ordered else "in-order",
                    "timing": ("per-step events, 512 MiB read flush before each step" if args.flush
                               else f"back to back, cycling over {n_layers} layers' inputs")
                              + (f"; {args.settle_ms:g} ms of the flush kernel before the warm-up"
@@ -573,7 +615,14 @@ def main():
         "roofline": {"kernel": names[1], "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": work["decode_bytes"]},
+                     "algorithmic_bytes_per_launch": work["decode_bytes"],
+                     "bytes_definition": "cache rows once + q_abs + latent output (bf16) + block table",
+                     "frac_with_f32_latent_output": round(
+                         work["decode_bytes_f32"] / dec_s / 1e9 / HBM_PEAK_GBPS, 4)},
+        "kernel_hbm_frac": kernel_frac,
+        "step_hbm_frac": round(work["step_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "step_mfma_frac": round(work["step_flop"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "step_algorithmic_bytes": work["step_bytes"],
     }
     # The cache write of the next token of every sequence (mla_append_kv), timed
     # on its own (per-launch events): it precedes the step in a model and is not

@@ -8,8 +8,10 @@
  *
  *   mla_absorb_q        q~_i = (W^UK_i)^T q^C_i, and RoPE_p(q^R_i)           (per head i)
  *   mla_plan_splits     cut every sequence's pages into work items (host)
+ *   mla_plan_splits_ordered  the same, sized for longest-first dispatch, and the order
  *   mla_decode_splitkv  per work item: scores against [c^KV | k^R], online
  *                       softmax, latent-space weighted sum, partial LSE
+ *   mla_decode_splitkv_ordered  the same, items started in a given order
  *   mla_combine         log-sum-exp merge of the work items of a sequence
  *   mla_decode_merged   the two above in one launch
  *   mla_decode_splitkv_multi, mla_combine_multi
@@ -145,6 +147,25 @@ mla_status mla_plan_splits(const mla_dims* dims, int32_t batch, const int32_t* s
                            int32_t num_slots, int32_t max_items, int32_t* items_host,
                            int32_t* split_offsets_host, int32_t* num_items);
 
+/* mla_plan_splits for longest-first dispatch (host only, no HIP call,
+ * deterministic).  Items and split offsets as mla_plan_splits writes them (the
+ * same cover of every sequence, grouped by sequence in token order), but the
+ * item size is chosen for dispatching the items longest first, and
+ * order_host [max_items] receives that dispatch order: order_host[s] is the
+ * item the s-th workgroup slot takes (a permutation of 0 .. *num_items-1,
+ * items sorted by decreasing page count, equal sizes in item order).  The
+ * simulation behind the size places dispatch slot s on XCD s % 8, as the
+ * hardware places workgroups, and starts each XCD's items in order on its
+ * num_slots / 8 slots.  With mixed lengths the longest items then start
+ * first and the short ones fill the gaps at the end, which takes fewer,
+ * larger items than in-order dispatch (fewer partials to merge).  Pass the
+ * order to mla_decode_splitkv_ordered.
+ * Errors: as for mla_plan_splits, plus MLA_ERR_INVALID_ARG for a null order_host. */
+mla_status mla_plan_splits_ordered(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host,
+                                   int32_t num_slots, int32_t max_items, int32_t* items_host,
+                                   int32_t* split_offsets_host, int32_t* order_host,
+                                   int32_t* num_items);
+
 /* Upper bound on the number of items mla_plan_splits can produce for this batch:
  * sum over b of ceil(L_b / page_size).  Host only.  Returns -1 on bad arguments. */
 int64_t mla_plan_max_items(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host);
@@ -166,6 +187,22 @@ mla_status mla_decode_splitkv(const mla_dims* dims, int32_t batch, const void* q
                               int32_t max_pages_per_seq, const int32_t* seq_lens,
                               const int32_t* items, int32_t num_items, float* o_part,
                               float* lse_part, void* stream);
+
+/* mla_decode_splitkv with a dispatch order: workgroup slot s decodes item
+ * order[s] (device int32 [num_items], a permutation of 0 .. num_items-1, e.g.
+ * from mla_plan_splits_ordered).  Partials are written at their item's index,
+ * so o_part and lse_part are bit-identical to mla_decode_splitkv's on the same
+ * items; only the time at which each item runs changes.  The order is taken on
+ * trust (a value outside [0, num_items) is undefined behaviour); on shapes off
+ * the gfx950 fast path it is ignored.
+ * Errors: as for mla_decode_splitkv, plus MLA_ERR_INVALID_ARG for a null or
+ * misaligned order. */
+mla_status mla_decode_splitkv_ordered(const mla_dims* dims, int32_t batch, const void* q_abs,
+                                      const void* kv_cache, int32_t num_pages,
+                                      const int32_t* block_table, int32_t max_pages_per_seq,
+                                      const int32_t* seq_lens, const int32_t* items,
+                                      int32_t num_items, const int32_t* order, float* o_part,
+                                      float* lse_part, void* stream);
 
 /* Split-KV decode with q_len query tokens per sequence (speculative or chunked
  * decode: the newest q_len tokens of each sequence, already in the cache, are

@@ -103,6 +103,9 @@ def load():
         "mla_absorb_q": (i32, [pd, i32, vp, vp, vp, vp, vp, vp]),
         "mla_plan_splits": (i32, [pd, i32, pi32, i32, i32, pi32, pi32, pi32]),
         "mla_plan_max_items": (ctypes.c_int64, [pd, i32, pi32]),
+        "mla_plan_splits_ordered": (i32, [pd, i32, pi32, i32, i32, pi32, pi32, pi32, pi32]),
+        "mla_decode_splitkv_ordered": (i32, [pd, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp,
+                                              vp]),
         "mla_decode_splitkv": (i32, [pd, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp]),
         "mla_combine": (i32, [pd, i32, vp, vp, vp, vp, vp, vp]),
         "mla_decode_splitkv_multi": (i32, [pd, i32, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp,
@@ -238,8 +241,10 @@ def absorb_q(dims: Dims, q_nope, q_pe, positions, w_uk, q_abs=None, stream=None)
     return q_abs
 
 
-def plan_splits(dims: Dims, seq_lens_host, num_slots: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Host planner: (items [W, 4] int32, split_offsets [B + 1] int32)."""
+def plan_splits(dims: Dims, seq_lens_host, num_slots: int, ordered: bool = False):
+    """Host planner: (items [W, 4] int32, split_offsets [B + 1] int32), and with
+    `ordered` also the longest-first dispatch order [W] int32
+    (mla_plan_splits_ordered) as a third element."""
     L = load()
     lens = np.ascontiguousarray(np.asarray(seq_lens_host, dtype=np.int32))
     B = int(lens.shape[0])
@@ -251,6 +256,13 @@ def plan_splits(dims: Dims, seq_lens_host, num_slots: int) -> Tuple[np.ndarray, 
     items = np.zeros((max(int(cap), 1), 4), dtype=np.int32)
     offs = np.zeros(B + 1, dtype=np.int32)
     n = ctypes.c_int32(0)
+    if ordered:
+        order = np.zeros(items.shape[0], dtype=np.int32)
+        _check(L.mla_plan_splits_ordered(ctypes.byref(d), B, lens.ctypes.data_as(pi32), int(num_slots),
+                                         items.shape[0], items.ctypes.data_as(pi32),
+                                         offs.ctypes.data_as(pi32), order.ctypes.data_as(pi32),
+                                         ctypes.byref(n)), "mla_plan_splits_ordered")
+        return items[:n.value].copy(), offs, order[:n.value].copy()
     _check(L.mla_plan_splits(ctypes.byref(d), B, lens.ctypes.data_as(pi32), int(num_slots),
                              items.shape[0], items.ctypes.data_as(pi32),
                              offs.ctypes.data_as(pi32), ctypes.byref(n)), "mla_plan_splits")
@@ -288,8 +300,10 @@ def _debug_paging(dims: Dims, block_table, seq_lens, num_pages: int, min_len: in
 
 
 def decode_splitkv(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items,
-                   o_part=None, lse_part=None, stream=None):
-    """Per work item: (o_part [W, H, d_c] float32, lse_part [W, H] float32)."""
+                   o_part=None, lse_part=None, stream=None, order=None):
+    """Per work item: (o_part [W, H, d_c] float32, lse_part [W, H] float32).
+    With `order` (device int32 [W], e.g. plan_splits(..., ordered=True)'s third
+    output) workgroup slot s takes item order[s] (mla_decode_splitkv_ordered)."""
     torch = _torch()
     dt = _store_dtype(dims)
     B, H = q_abs.shape[0], dims.n_heads
@@ -301,13 +315,16 @@ def decode_splitkv(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items,
         lse_part = torch.empty((W, H), dtype=torch.float32, device=dev)
     num_pages = kv_cache.shape[0]
     _debug_paging(dims, block_table, seq_lens, num_pages, 1, stream, "mla_decode_splitkv")
-    _launch("mla_decode_splitkv",
-        ctypes.byref(dims.c()), B, _ptr(q_abs, dt, (B, H, dims.row), "q_abs"),
-        _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
-        _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
-        _ptr(seq_lens, torch.int32, (B,), "seq_lens"), _ptr(items, torch.int32, (W, 4), "items"), W,
-        _ptr(o_part, torch.float32, (W, H, dims.d_latent), "o_part"),
-        _ptr(lse_part, torch.float32, (W, H), "lse_part"), _stream(stream))
+    head = [ctypes.byref(dims.c()), B, _ptr(q_abs, dt, (B, H, dims.row), "q_abs"),
+            _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
+            _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
+            _ptr(seq_lens, torch.int32, (B,), "seq_lens"), _ptr(items, torch.int32, (W, 4), "items"), W]
+    tail = [_ptr(o_part, torch.float32, (W, H, dims.d_latent), "o_part"),
+            _ptr(lse_part, torch.float32, (W, H), "lse_part"), _stream(stream)]
+    if order is None:
+        _launch("mla_decode_splitkv", *head, *tail)
+    else:
+        _launch("mla_decode_splitkv_ordered", *head, _ptr(order, torch.int32, (W,), "order"), *tail)
     return o_part, lse_part
 
 
@@ -542,17 +559,19 @@ def prefill_naive(dims: Dims, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, s
 
 
 def decode_step(dims: Dims, q_nope, q_pe, positions, w_uk, w_uv, kv_cache, block_table, seq_lens,
-                items, split_offsets, bufs: Optional[dict] = None, stream=None) -> dict:
+                items, split_offsets, bufs: Optional[dict] = None, stream=None, order=None) -> dict:
     """absorb_q -> decode_splitkv -> combine -> out_proj on one stream.
 
-    `items`/`split_offsets` are device copies of plan_splits' output.  `bufs` may
-    hold preallocated q_abs, o_part, lse_part, o_latent, lse, out tensors.
+    `items`/`split_offsets` (and `order`, for plan_splits(..., ordered=True))
+    are device copies of plan_splits' output.  `bufs` may hold preallocated
+    q_abs, o_part, lse_part, o_latent, lse, out tensors.
     """
     b = {} if bufs is None else bufs
     B = q_nope.shape[0]
     b["q_abs"] = absorb_q(dims, q_nope, q_pe, positions, w_uk, b.get("q_abs"), stream)
     b["o_part"], b["lse_part"] = decode_splitkv(dims, b["q_abs"], kv_cache, block_table, seq_lens,
-                                                items, b.get("o_part"), b.get("lse_part"), stream)
+                                                items, b.get("o_part"), b.get("lse_part"), stream,
+                                                order=order)
     b["o_latent"], b["lse"] = combine(dims, split_offsets, b["o_part"], b["lse_part"], B,
                                       b.get("o_latent"), b.get("lse"), stream)
     b["out"] = out_proj(dims, b["o_latent"], w_uv, b.get("out"), stream)

@@ -124,7 +124,8 @@ static_assert(kStages * kSlotBytes + 2 * kPBytesWG + 256 + kSWaves * 4 + 4 * kHe
 __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ items, int num_items, int q_len, float scale, float max_jump,
+    const int32_t* __restrict__ items, int num_items, const int32_t* __restrict__ order, int q_len,
+    float scale, float max_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
   constexpr int H = 128;
@@ -147,6 +148,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
   // dispatched together (block_to_item); part r = query token r / 2, half r % 2.
   int it, part;
   block_to_item(blockIdx.x, num_items, 2 * q_len, it, part);
+  if (order) it = order[it];  // dispatch slot -> item
   const int hh = part & 1, tq = part >> 1;
   const int b = items[4 * it];
   const int p0 = items[4 * it + 2];
@@ -535,7 +537,8 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
 __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ items, int num_items, int q_len, float scale, float max_jump,
+    const int32_t* __restrict__ items, int num_items, const int32_t* __restrict__ order, int q_len,
+    float scale, float max_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
   constexpr int H = 16;
@@ -553,6 +556,7 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
   // block -> (item, query token), laid out as in the 128-head kernel
   int it, tq;
   block_to_item(blockIdx.x, num_items, q_len, it, tq);
+  if (order) it = order[it];  // dispatch slot -> item
   const int b = items[4 * it];
   const int p0 = items[4 * it + 2];
   const int p1 = items[4 * it + 3];
@@ -829,7 +833,8 @@ float max_jump() {
 
 hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const void* kv_cache,
                        const int32_t* block_table, int max_pages, const int32_t* seq_lens,
-                       const int32_t* items, int num_items, float* o_part, float* lse_part,
+                       const int32_t* items, int num_items, const int32_t* order, float* o_part,
+                       float* lse_part,
                        const int32_t* split_offsets, int32_t* tickets, float* o_latent,
                        float* lse_out, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(num_items) * q_len * (d.n_heads == 128 ? 2 : 1);
@@ -837,13 +842,13 @@ hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const vo
   if (d.n_heads == 128) {
     hipLaunchKernelGGL(decode_h128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(1024), 0, stream,
                        static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
-                       block_table, max_pages, seq_lens, items, num_items, q_len, d.softmax_scale,
+                       block_table, max_pages, seq_lens, items, num_items, order, q_len, d.softmax_scale,
                        max_jump(), o_part, lse_part, split_offsets, tickets, o_latent, lse_out);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(decode_h16_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
-                     block_table, max_pages, seq_lens, items, num_items, q_len, d.softmax_scale,
+                     block_table, max_pages, seq_lens, items, num_items, order, q_len, d.softmax_scale,
                      max_jump(), o_part, lse_part, split_offsets, tickets, o_latent, lse_out);
   return hipGetLastError();
 }

@@ -103,13 +103,26 @@ mla_status mla_plan_splits(const mla_dims* dims, int32_t batch, const int32_t* s
                      split_offsets_host, num_items, dims->n_heads);
 }
 
+mla_status mla_plan_splits_ordered(const mla_dims* dims, int32_t batch, const int32_t* seq_lens_host,
+                                   int32_t num_slots, int32_t max_items, int32_t* items_host,
+                                   int32_t* split_offsets_host, int32_t* order_host,
+                                   int32_t* num_items) {
+  mla_status s = check_dims(dims);
+  if (s != MLA_OK) return s;
+  if (!order_host) return MLA_ERR_INVALID_ARG;
+  const int per_item = (is_fast_shape(*dims) && dims->n_heads == 128) ? 2 : 1;
+  const int slots = num_slots >= per_item ? num_slots / per_item : num_slots;
+  return plan_splits(dims->page_size, batch, seq_lens_host, slots, max_items, items_host,
+                     split_offsets_host, num_items, dims->n_heads, order_host);
+}
+
 namespace {
 
 mla_status decode_splitkv_impl(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_abs,
                                const void* kv_cache, int32_t num_pages, const int32_t* block_table,
                                int32_t max_pages_per_seq, const int32_t* seq_lens,
-                               const int32_t* items, int32_t num_items, float* o_part,
-                               float* lse_part, void* stream) {
+                               const int32_t* items, int32_t num_items, const int32_t* order,
+                               float* o_part, float* lse_part, void* stream) {
   mla_status s = check_dims(dims);
   if (s != MLA_OK) return s;
   if (batch < 1 || q_len < 1 || num_pages < 1 || max_pages_per_seq < 1 || num_items < 1)
@@ -117,7 +130,7 @@ mla_status decode_splitkv_impl(const mla_dims* dims, int32_t batch, int32_t q_le
   if (!q_abs || !kv_cache || !block_table || !seq_lens || !items || !o_part || !lse_part)
     return MLA_ERR_INVALID_ARG;
   if (!al16(q_abs) || !al16(kv_cache) || !al16(o_part) || !al4(lse_part) || !al4(block_table) ||
-      !al4(seq_lens) || !al4(items))
+      !al4(seq_lens) || !al4(items) || (order && !al4(order)))
     return MLA_ERR_INVALID_ARG;
   // partial rows and workgroup counts stay within 32-bit grid limits
   if (static_cast<int64_t>(num_items) * q_len * 2 > INT32_MAX ||
@@ -127,8 +140,8 @@ mla_status decode_splitkv_impl(const mla_dims* dims, int32_t batch, int32_t q_le
   (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
   if (is_fast_shape(*dims))
     return launched(decode_fast(*dims, q_len, q_abs, kv_cache, block_table, max_pages_per_seq,
-                                seq_lens, items, num_items, o_part, lse_part, nullptr, nullptr,
-                                nullptr, nullptr, st));
+                                seq_lens, items, num_items, order, o_part, lse_part, nullptr,
+                                nullptr, nullptr, nullptr, st));
   return launched(decode_generic(*dims, q_len, q_abs, kv_cache, block_table, max_pages_per_seq,
                                  seq_lens, items, num_items, o_part, lse_part, st));
 }
@@ -162,7 +175,20 @@ mla_status mla_decode_splitkv(const mla_dims* dims, int32_t batch, const void* q
                               const int32_t* items, int32_t num_items, float* o_part,
                               float* lse_part, void* stream) {
   return decode_splitkv_impl(dims, batch, 1, q_abs, kv_cache, num_pages, block_table,
-                             max_pages_per_seq, seq_lens, items, num_items, o_part, lse_part, stream);
+                             max_pages_per_seq, seq_lens, items, num_items, nullptr, o_part, lse_part,
+                             stream);
+}
+
+mla_status mla_decode_splitkv_ordered(const mla_dims* dims, int32_t batch, const void* q_abs,
+                                      const void* kv_cache, int32_t num_pages,
+                                      const int32_t* block_table, int32_t max_pages_per_seq,
+                                      const int32_t* seq_lens, const int32_t* items,
+                                      int32_t num_items, const int32_t* order, float* o_part,
+                                      float* lse_part, void* stream) {
+  if (!order) return MLA_ERR_INVALID_ARG;
+  return decode_splitkv_impl(dims, batch, 1, q_abs, kv_cache, num_pages, block_table,
+                             max_pages_per_seq, seq_lens, items, num_items, order, o_part, lse_part,
+                             stream);
 }
 
 mla_status mla_decode_splitkv_multi(const mla_dims* dims, int32_t batch, int32_t q_len,
@@ -172,7 +198,8 @@ mla_status mla_decode_splitkv_multi(const mla_dims* dims, int32_t batch, int32_t
                                     int32_t num_items, float* o_part, float* lse_part,
                                     void* stream) {
   return decode_splitkv_impl(dims, batch, q_len, q_abs, kv_cache, num_pages, block_table,
-                             max_pages_per_seq, seq_lens, items, num_items, o_part, lse_part, stream);
+                             max_pages_per_seq, seq_lens, items, num_items, nullptr, o_part, lse_part,
+                             stream);
 }
 
 mla_status mla_decode_merged(const mla_dims* dims, int32_t batch, const void* q_abs,
@@ -199,7 +226,7 @@ mla_status mla_decode_merged(const mla_dims* dims, int32_t batch, const void* q_
   (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
   if (is_fast_shape(*dims))
     return launched(decode_fast(*dims, 1, q_abs, kv_cache, block_table, max_pages_per_seq,
-                                seq_lens, items, num_items, o_part, lse_part, split_offsets,
+                                seq_lens, items, num_items, nullptr, o_part, lse_part, split_offsets,
                                 tickets, o_latent, lse, st));
   mla_status r = launched(decode_generic(*dims, 1, q_abs, kv_cache, block_table, max_pages_per_seq,
                                          seq_lens, items, num_items, o_part, lse_part, st));

@@ -44,9 +44,11 @@ hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const v
 // sequence's partials into o_latent / lse_out (split_offsets as for combine;
 // q_len 1 only).  q_len query tokens per sequence: q_abs rows b * q_len + t,
 // partial rows item * q_len + t.
+// order: null, or the item each dispatch slot takes (a permutation of the items).
 hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const void* kv_cache,
                        const int32_t* block_table, int max_pages, const int32_t* seq_lens,
-                       const int32_t* items, int num_items, float* o_part, float* lse_part,
+                       const int32_t* items, int num_items, const int32_t* order, float* o_part,
+                       float* lse_part,
                        const int32_t* split_offsets, int32_t* tickets, float* o_latent,
                        float* lse_out, hipStream_t stream);
 hipError_t combine_fast(const mla_dims& d, int batch, int q_len, const int32_t* split_offsets,
@@ -88,9 +90,11 @@ hipError_t check_paging(const mla_dims& d, int batch, int min_len, const int32_t
                         int32_t* result, hipStream_t stream);
 
 // Host planner (plan.cpp).
+// order: null, or [max_items] to receive the longest-first dispatch order (the
+// item size is then chosen for that order).
 mla_status plan_splits(int page_size, int batch, const int32_t* seq_lens, int num_slots,
                        int max_items, int32_t* items, int32_t* split_offsets, int32_t* num_items,
-                       int n_heads);
+                       int n_heads, int32_t* order = nullptr);
 int64_t plan_max_items(int page_size, int batch, const int32_t* seq_lens);
 
 }  // namespace mla

@@ -5,8 +5,10 @@
 // writes one partial (o, lse) that the combine step merges.  More items fill
 // more of the machine but each one adds a fixed cost (pipeline start-up and the
 // partial's write + re-read), so the item size is picked by simulating the
-// in-order dispatch of the items onto `num_slots` workgroup slots and keeping
-// the size with the shortest simulated makespan.
+// dispatch of the items onto `num_slots` workgroup slots and keeping the size
+// with the shortest simulated makespan.  Items are dispatched in their own
+// order (sequence by sequence), or, when the caller asks for a dispatch
+// order, longest first, which the simulation then follows.
 #include <algorithm>
 #include <cstdint>
 #include <functional>
@@ -58,6 +60,45 @@ Layout simulate(const std::vector<int64_t>& pages, int64_t chunk, int num_slots,
   return r;
 }
 
+// Longest-first dispatch (the items sorted by decreasing size) onto
+// `num_slots` slots as the hardware places them: slot s of the dispatch order
+// runs on XCD s % kXcds, and each XCD starts its items in order on its
+// num_slots / kXcds slots as they free up.
+constexpr int kXcds = 8;
+
+// Item sizes (pages) of every sequence cut at `chunk`, longest first; ties keep
+// the item order (sequence, then token order).
+std::vector<int64_t> lpt_sizes(const std::vector<int64_t>& pages, int64_t chunk) {
+  std::vector<int64_t> sz;
+  for (int64_t p : pages) {
+    const int64_t n = parts_of(p, chunk);
+    for (int64_t k = 0; k < n; ++k) sz.push_back(part_pages(p, n, k));
+  }
+  std::stable_sort(sz.begin(), sz.end(), std::greater<int64_t>());
+  return sz;
+}
+
+Layout simulate_lpt(const std::vector<int64_t>& pages, int64_t chunk, int num_slots,
+                    int64_t overhead, int64_t bound) {
+  Layout r{chunk, 0, 0};
+  const std::vector<int64_t> sz = lpt_sizes(pages, chunk);
+  const int per_xcd = std::max(1, num_slots / kXcds);
+  std::vector<std::priority_queue<int64_t, std::vector<int64_t>, std::greater<int64_t>>> free_at(kXcds);
+  for (auto& q : free_at)
+    for (int i = 0; i < per_xcd; ++i) q.push(0);
+  for (size_t s = 0; s < sz.size(); ++s) {
+    auto& q = free_at[s % kXcds];
+    const int64_t t = q.top();
+    q.pop();
+    const int64_t end = t + sz[s] * kUnit + overhead;
+    r.makespan = std::max(r.makespan, end);
+    if (r.makespan > bound) return r;
+    q.push(end);
+    ++r.items;
+  }
+  return r;
+}
+
 }  // namespace
 
 int64_t plan_max_items(int page_size, int batch, const int32_t* seq_lens) {
@@ -72,7 +113,7 @@ int64_t plan_max_items(int page_size, int batch, const int32_t* seq_lens) {
 
 mla_status plan_splits(int page_size, int batch, const int32_t* seq_lens, int num_slots,
                        int max_items, int32_t* items, int32_t* split_offsets, int32_t* num_items,
-                       int n_heads) {
+                       int n_heads, int32_t* order) {
   if (!seq_lens || !items || !split_offsets || !num_items) return MLA_ERR_INVALID_ARG;
   if (page_size < 1 || batch < 1 || num_slots < 1 || max_items < 0 || n_heads < 1)
     return MLA_ERR_INVALID_ARG;
@@ -108,7 +149,8 @@ mla_status plan_splits(int page_size, int batch, const int32_t* seq_lens, int nu
   std::sort(cands.begin(), cands.end(), std::greater<int64_t>());
   cands.erase(std::unique(cands.begin(), cands.end()), cands.end());
   for (int64_t c : cands) {
-    Layout l = simulate(pages, c, num_slots, overhead, best.makespan);
+    Layout l = order ? simulate_lpt(pages, c, num_slots, overhead, best.makespan)
+                     : simulate(pages, c, num_slots, overhead, best.makespan);
     if (l.makespan < best.makespan || (l.makespan == best.makespan && l.items < best.items)) best = l;
   }
   if (best.items > max_items) {
@@ -132,6 +174,13 @@ mla_status plan_splits(int page_size, int batch, const int32_t* seq_lens, int nu
   }
   split_offsets[batch] = w;
   *num_items = w;
+  if (order) {
+    // longest first; among equal sizes, item order
+    for (int32_t i = 0; i < w; ++i) order[i] = i;
+    std::stable_sort(order, order + w, [&](int32_t a, int32_t b) {
+      return items[4 * a + 3] - items[4 * a + 2] > items[4 * b + 3] - items[4 * b + 2];
+    });
+  }
   return MLA_OK;
 }
 

@@ -37,15 +37,18 @@ uint64_t next(uint64_t& s) {
 
 // Plans `lens` twice: first with no room (the planner reports the count it
 // needs), then with exactly that room; checks the result.
-void plan_and_check(int page, const std::vector<int32_t>& lens, int slots, int heads) {
+void plan_and_check(int page, const std::vector<int32_t>& lens, int slots, int heads,
+                    bool ordered = false) {
   const int batch = static_cast<int>(lens.size());
   // the lengths live in an exactly sized heap block, so a read past batch is caught
   std::unique_ptr<int32_t[]> L(new int32_t[batch]);
   for (int b = 0; b < batch; ++b) L[b] = lens[b];
   std::unique_ptr<int32_t[]> offs(new int32_t[batch + 1]);
   std::unique_ptr<int32_t[]> none(new int32_t[0]);
+  std::unique_ptr<int32_t[]> no_order(new int32_t[0]);
   int32_t need = -1;
-  mla_status st = mla::plan_splits(page, batch, L.get(), slots, 0, none.get(), offs.get(), &need, heads);
+  mla_status st = mla::plan_splits(page, batch, L.get(), slots, 0, none.get(), offs.get(), &need, heads,
+                                   ordered ? no_order.get() : nullptr);
   EXPECT(st == MLA_ERR_WORKSPACE);
   EXPECT(need >= batch);
   const int64_t bound = mla::plan_max_items(page, batch, L.get());
@@ -53,8 +56,10 @@ void plan_and_check(int page, const std::vector<int32_t>& lens, int slots, int h
   if (st != MLA_ERR_WORKSPACE || need < batch || bound < need) return;
 
   std::unique_ptr<int32_t[]> items(new int32_t[4 * static_cast<size_t>(need)]);
+  std::unique_ptr<int32_t[]> order(new int32_t[static_cast<size_t>(need)]);
   int32_t got = -1;
-  st = mla::plan_splits(page, batch, L.get(), slots, need, items.get(), offs.get(), &got, heads);
+  st = mla::plan_splits(page, batch, L.get(), slots, need, items.get(), offs.get(), &got, heads,
+                        ordered ? order.get() : nullptr);
   EXPECT(st == MLA_OK);
   EXPECT(got == need);
   if (st != MLA_OK || got != need) return;
@@ -80,6 +85,22 @@ void plan_and_check(int page, const std::vector<int32_t>& lens, int slots, int h
     }
     EXPECT(p == pages);
     EXPECT(mx - mn <= 1);
+  }
+  if (ordered) {
+    // a permutation of the items, longest first, equal sizes in item order
+    std::vector<char> seen(static_cast<size_t>(got), 0);
+    for (int32_t s = 0; s < got; ++s) {
+      const int32_t i = order[s];
+      EXPECT(i >= 0 && i < got);
+      if (i < 0 || i >= got) return;
+      EXPECT(!seen[i]);
+      seen[i] = 1;
+      if (s > 0) {
+        const int32_t j = order[s - 1];
+        const int32_t si = items[4 * i + 3] - items[4 * i + 2], sj = items[4 * j + 3] - items[4 * j + 2];
+        EXPECT(sj > si || (sj == si && j < i));
+      }
+    }
   }
 }
 
@@ -119,7 +140,8 @@ int main() {
       std::vector<int32_t>(64, 8192), std::vector<int32_t>(8, 131072), {INT32_MAX / 4}};
   for (const auto& lens : fixed)
     for (int heads : {16, 128})
-      for (int slots : {1, 3, 256, 1024}) plan_and_check(64, lens, slots, heads);
+      for (int slots : {1, 3, 256, 1024})
+        for (bool ordered : {false, true}) plan_and_check(64, lens, slots, heads, ordered);
   // random mixes: batch 1..300, lengths 1..70000, page sizes 1..256
   uint64_t s = 20240611;
   for (int t = 0; t < 300; ++t) {
@@ -128,7 +150,7 @@ int main() {
     std::vector<int32_t> lens(batch);
     for (auto& l : lens) l = 1 + static_cast<int32_t>(next(s) % 70000);
     const int slots = 1 + static_cast<int>(next(s) % 2048);
-    plan_and_check(page, lens, slots, (t & 1) ? 128 : 16);
+    plan_and_check(page, lens, slots, (t & 1) ? 128 : 16, (t & 2) != 0);
   }
   if (g_failures) {
     std::printf("%d failures\n", g_failures);

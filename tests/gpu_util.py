@@ -47,17 +47,24 @@ def num_slots() -> int:
     return int(torch.cuda.get_device_properties(0).multi_processor_count)
 
 
-def run(wl, dev=None, slots=None, items=None, offs=None) -> dict:
-    """Run the four device steps; return numpy copies of every output."""
+def run(wl, dev=None, slots=None, items=None, offs=None, ordered=False) -> dict:
+    """Run the four device steps; return numpy copies of every output.
+    `ordered`: the longest-first plan and dispatch (as the bench runs them)."""
     import torch
     dims = dims_of(wl.cfg)
     dev = upload(wl) if dev is None else dev
+    order = None
     if items is None:
-        items, offs = mla.plan_splits(dims, wl.seq_lens, slots or num_slots())
+        if ordered:
+            items, offs, order = mla.plan_splits(dims, wl.seq_lens, slots or num_slots(), ordered=True)
+        else:
+            items, offs = mla.plan_splits(dims, wl.seq_lens, slots or num_slots())
     it_d = torch.from_numpy(items).cuda()
     of_d = torch.from_numpy(offs).cuda()
+    or_d = None if order is None else torch.from_numpy(order).cuda()
     b = mla.decode_step(dims, dev["q_nope"], dev["q_pe"], dev["positions"], dev["w_uk"],
-                        dev["w_uv"], dev["cache"], dev["block_table"], dev["seq_lens"], it_d, of_d)
+                        dev["w_uv"], dev["cache"], dev["block_table"], dev["seq_lens"], it_d, of_d,
+                        order=or_d)
     torch.cuda.synchronize()
     out = {}
     for k in ("q_abs", "o_latent", "lse", "out", "o_part", "lse_part"):

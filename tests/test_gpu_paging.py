@@ -63,3 +63,30 @@ def test_plan_changes_only_rounding(mla):
     # shrink with the number of tokens.
     assert_close(many["o_latent"], one["o_latent"], "o_latent many vs one", 3e-3, 1e-2)
     assert_lse(many["lse"], one["lse"], "lse many vs one", 1e-3)
+
+
+@pytest.mark.parametrize("heads", [128, 16])
+def test_ordered_dispatch_bit_identical(mla, heads):
+    """Dispatching the items longest first (or in any other order) changes
+    only when each item runs: partials and outputs are bit-identical to the
+    in-order decode on the same items."""
+    import torch
+    from gpu_util import dims_of, num_slots, upload
+    cfg = small(V2, "ord", 5, n_heads=heads, permute_pages=True)
+    lens = np.array([1, 700, 9000, 65, 20000], np.int32)
+    wl = generate(cfg, lens=lens)
+    dims = dims_of(cfg)
+    dev = upload(wl)
+    items, offs, order = mla.plan_splits(dims, lens, num_slots(), ordered=True)
+    say(f"[ordered dispatch H={heads}] {len(items)} items")
+    q_abs = mla.absorb_q(dims, dev["q_nope"], dev["q_pe"], dev["positions"], dev["w_uk"])
+    it_d = torch.from_numpy(items).cuda()
+    outs = []
+    for o in (None, order, order[::-1].copy()):
+        o_d = None if o is None else torch.from_numpy(o).cuda()
+        op, lp = mla.decode_splitkv(dims, q_abs, dev["cache"], dev["block_table"], dev["seq_lens"], it_d,
+                                    order=o_d)
+        torch.cuda.synchronize()
+        outs.append((op.cpu().numpy(), lp.cpu().numpy()))
+    for op, lp in outs[1:]:
+        assert np.array_equal(op, outs[0][0]) and np.array_equal(lp, outs[0][1])

@@ -124,7 +124,7 @@ def test_full_size_sampled(mla, name, seqs, heads):
         seqs = [int(order[0]), int(order[-1]), int(order[len(order) // 2])]
     say(f"[full {name}] running; checking sequences {seqs}")
     dev = upload(wl)
-    out = run(wl, dev=dev)
+    out = run(wl, dev=dev, ordered=True)   # the bench's plan and dispatch
     assert np.all(np.isfinite(out["out"])) and np.all(np.isfinite(out["lse"]))
     compare_with_oracle(wl, out, seqs, heads=heads)
     # the step the bench times merges and projects in one launch: on the same

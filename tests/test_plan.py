@@ -78,3 +78,35 @@ def test_plan_random(seed):
     for dims in (V2, LITE):
         items, offs = mla.plan_splits(dims, L, int(r.integers(1, 600)))
         check_plan(L, items, offs)
+
+
+@pytest.mark.parametrize("dims", [V2, LITE], ids=["h128", "h16"])
+@pytest.mark.parametrize("lens", [[1], [65], [1, 64, 65, 32768], [4096] * 32, [8192] * 64,
+                                  list(np.random.default_rng(3).integers(1, 20000, 77))])
+def test_plan_ordered(dims, lens):
+    """Longest-first plans: a valid cover, and an order that is a permutation
+    of the items with non-increasing sizes (equal sizes in item order)."""
+    items, offs, order = mla.plan_splits(dims, lens, 256, ordered=True)
+    check_plan(lens, items, offs)
+    assert sorted(order.tolist()) == list(range(len(items)))
+    sz = (items[:, 3] - items[:, 2])[order]
+    assert np.all(np.diff(sz) <= 0)
+    for a, b in zip(order[:-1], order[1:]):
+        if sz[list(order).index(a)] == sz[list(order).index(b)]:
+            assert a < b
+
+
+def test_plan_ordered_uniform_is_the_plain_plan():
+    # equal lengths: longest first is the item order, and the sizes are the same
+    for dims, lens in ((V2, [8192] * 64), (V2, [131072] * 8), (LITE, [4096] * 32)):
+        a_items, a_offs = mla.plan_splits(dims, lens, 256)
+        b_items, b_offs, order = mla.plan_splits(dims, lens, 256, ordered=True)
+        assert np.array_equal(a_items, b_items) and np.array_equal(a_offs, b_offs)
+        assert np.array_equal(order, np.arange(len(b_items)))
+
+
+def test_plan_ordered_varlen_takes_fewer_items():
+    L = seq_lens(CONFIGS["v2_varlen_b128"])
+    items, _ = mla.plan_splits(V2, L, 256)
+    o_items, _, _ = mla.plan_splits(V2, L, 256, ordered=True)
+    assert len(o_items) < len(items)
