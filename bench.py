@@ -299,6 +299,10 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=100.0,
                     help="before the warm-up steps, keep the GPU (and this process) busy this long "
                          "with the flush kernel: out of idle, the first steps run up to 10%% slower")
+    ap.add_argument("--score-jump", type=float, default=0.0, metavar="F",
+                    help="multiply the latent of every cached row after each sequence's first 32 "
+                         "tokens by F (a jump of the score maxima after the first slice, which "
+                         "moves the decode's softmax reference)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -343,6 +347,17 @@ def main():
         positions = dev(pos.reshape(-1).astype(np.int32), False)
     layer0 = {"q_nope": q_nope, "q_pe": q_pe, "w_uk": dev(wl.w_uk, bf), "w_uv": dev(wl.w_uv, bf),
               "cache": dev(wl.cache, bf)}
+    if args.score_jump:
+        # every used slot except the first 32 tokens of each sequence
+        scale = np.zeros(wl.cache.shape[:2], bool)
+        for b in range(B):
+            n = int(wl.seq_lens[b])
+            toks = np.arange(32, n)
+            scale[wl.block_table[b, toks // cfg.page_size], toks % cfg.page_size] = True
+        m = torch.from_numpy(scale).cuda()
+        lat = layer0["cache"][:, :, :cfg.d_latent]
+        lat[m] = (lat[m].float() * args.score_jump).to(lat.dtype)
+        log(f"[bench] latents after the first 32 tokens scaled by {args.score_jump:g}")
     # further layers: the same values in other memory (what matters for the
     # timing is that their rows, weights and queries are not where layer 0's are)
     args.flush = not args.back_to_back
@@ -549,6 +564,8 @@ def main():
 
     # The decode kernel alone, K launches back to back (cycling over the layers).
     dec = [(lambda c=calls[1]: mla.replay_calls(c)) for calls in recorded]
+    if H == 128 and bf:
+        mla.exact_pass_count(reset=True)
     if args.flush:
         d_ev = [new_events(2) for _ in range(args.steps)]
         for k in range(args.steps):
@@ -566,6 +583,12 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         dec_ms = e0.elapsed_time(e1) / args.steps
+    # work-item halves the decode redid against exact maxima, over the decode
+    # launches of the last pass
+    exact_passes = None
+    if H == 128 and bf:
+        exact_passes = mla.exact_pass_count(reset=True)
+        torch.cuda.synchronize()
     log("[bench] per-kernel mean ms (event between kernels): " +
         ", ".join(f"{n} {v:.4f}" for n, v in zip(names, k_ms)))
     log(f"[bench] step ms: {ms:.4f} ({spread}); decode launch ms: {dec_ms:.4f}; "
@@ -620,6 +643,9 @@ def main():
                      "frac_with_f32_latent_output": round(
                          work["decode_bytes_f32"] / dec_s / 1e9 / HBM_PEAK_GBPS, 4)},
         "kernel_hbm_frac": kernel_frac,
+        "score_jump": args.score_jump or None,
+        "exact_pass_workgroups_per_launch": (None if exact_passes is None
+                                             else round(exact_passes / args.steps, 3)),
         "step_hbm_frac": round(work["step_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "step_mfma_frac": round(work["step_flop"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "step_algorithmic_bytes": work["step_bytes"],

@@ -76,10 +76,15 @@
  *   are float64 except in the gfx950 fast absorb, which reduces the float64
  *   angle to [-pi, pi] in float64 and takes them in float32 (within about one
  *   float32 ulp of the float64 values).
- *   The fast decode kernel weighs tokens against each work item's first-slice
- *   score maximum; if a later maximum exceeds it by more than 2^20 it recomputes
- *   the item against exact maxima.  The environment variable
- *   MLA_DECODE_MAX_JUMP (log2 units, in (0, 30]) lowers that threshold.
+ *   The fast decode kernels weigh tokens against a per-head reference that
+ *   starts at the work item's first-slice score maximum and moves up to a later
+ *   slice's maximum when that passes it by more than 2^8 (the accumulators are
+ *   rescaled then); MLA_DECODE_MAX_JUMP (log2 units, in (0, 30]) sets that
+ *   threshold.  At 128 heads the two halves of a slice's tokens agree on a move
+ *   one slice later, so a single slice can push weights past the reference; if
+ *   one passes 2^64 the item is recomputed against exact maxima (read the count
+ *   with mla_decode_exact_pass_count; MLA_DECODE_SAFE_JUMP, in (0, 100], lowers
+ *   that bound).  The result is the same softmax either way.
  *
  * Supported shapes: the gfx950 fast path needs dtype MLA_BF16, d_latent 512,
  * d_rope 64, d_head 128, page_size 64 and n_heads 16 or 128; any other shape
@@ -402,6 +407,17 @@ int64_t mla_append_kv_noalloc_max_bytes(void);
 mla_status mla_check_paging(const mla_dims* dims, int32_t batch, int32_t min_len,
                             const int32_t* seq_lens, int32_t num_pages, const int32_t* block_table,
                             int32_t max_pages_per_seq, int32_t* result, void* stream);
+
+/* Number of workgroups of the 128-head fast decode (each takes one half of a
+ * work item's heads for one query token) that recomputed their item against
+ * exact score maxima (a single 32-token slice pushed a weight past 2^64 of its
+ * reference) on the current device since the count was last reset; with
+ * reset != 0 the
+ * count goes back to zero after it is read.  For monitoring and tests: the
+ * call copies a device counter synchronously.  Pages as for mla_decode_splitkv
+ * (the softmax of one head over the item's tokens).
+ * Errors: MLA_ERR_INVALID_ARG for a null count_host; MLA_ERR_HIP if the copy fails. */
+mla_status mla_decode_exact_pass_count(int32_t reset, uint64_t* count_host);
 
 /* Text of the last HIP error that made a libmla call on this thread return
  * MLA_ERR_HIP ("" if none).  Valid until the next libmla call on the thread. */

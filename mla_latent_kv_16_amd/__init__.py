@@ -32,7 +32,7 @@ __all__ = ["MlaError", "Dims", "load", "lib_path", "absorb_q", "plan_splits", "d
            "decode_merged", "append_kv", "append_kv_noalloc", "decode_splitkv_multi", "combine_multi", "combine_out_proj",
            "prefill_naive",
            "combine", "out_proj", "decode_step", "fast_path", "version", "record_calls", "replay_calls",
-           "check_paging", "BF16", "F32"]
+           "check_paging", "exact_pass_count", "BF16", "F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 BF16, F32 = 0, 1
@@ -125,6 +125,7 @@ def load():
                                          i32, vp]),
         "mla_append_kv_noalloc_max_bytes": (ctypes.c_int64, []),
         "mla_check_paging": (i32, [pd, i32, i32, vp, i32, vp, i32, vp, vp]),
+        "mla_decode_exact_pass_count": (i32, [i32, ctypes.POINTER(ctypes.c_uint64)]),
         "mla_status_string": (ctypes.c_char_p, [i32]),
         "mla_version": (i32, []),
         "mla_fast_path": (i32, [pd]),
@@ -180,6 +181,15 @@ def _check(status: int, where: str):
         if status == -4 and _lib is not None:
             detail = " [" + (_lib.mla_last_hip_error() or b"").decode(errors="replace") + "]"
         raise MlaError(status, where + detail)
+
+
+def exact_pass_count(reset: bool = False) -> int:
+    """Work items the 128-head decode redid against exact maxima on the current
+    device since the last reset (synchronous)."""
+    n = ctypes.c_uint64(0)
+    _check(load().mla_decode_exact_pass_count(int(bool(reset)), ctypes.byref(n)),
+           "mla_decode_exact_pass_count")
+    return int(n.value)
 
 
 def version() -> int:

@@ -5,6 +5,7 @@
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -31,15 +32,40 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
+# (SGPR spills go to VGPR lanes; they reach memory only through ScratchSize)
+_REMARK = re.compile(r"remark: +(Function Name|ScratchSize \[bytes/lane\]|VGPRs Spill): +(\S+)")
+
+
+def _check_resources(src: str, text: str) -> None:
+    """Every kernel must keep its data in registers and LDS: a kernel that
+    uses scratch (private memory), by a spill or a stack array the compiler
+    could not promote, runs many times slower, so the build refuses it."""
+    kernel, bad = None, []
+    for m in _REMARK.finditer(text):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            kernel = val
+        elif val != "0":
+            bad.append(f"{kernel}: {key} {val}")
+    if bad:
+        raise RuntimeError(f"{src}: kernels use scratch memory:\n  " + "\n  ".join(bad))
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = ["hipcc", *HIPCC_FLAGS, *lang, "-c", src, "-o", obj]
+    is_hip = src.endswith(".hip")
+    lang = ["-x", "hip"] if is_hip else []
+    remarks = ["-Rpass-analysis=kernel-resource-usage"] if is_hip else []
+    cmd = ["hipcc", *HIPCC_FLAGS, *lang, *remarks, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
-                    if "packed-fp32-ops" not in line)  # the host pass does not know the feature
+    text = r.stdout + r.stderr
+    out = "\n".join(line for line in text.splitlines()
+                    if "packed-fp32-ops" not in line       # the host pass does not know the feature
+                    and "kernel-resource-usage" not in line and not line.startswith(" "))
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{out}")
+    if is_hip:
+        _check_resources(src, text)
     if out.strip():
         print(out, file=sys.stderr)
     return obj

@@ -44,14 +44,23 @@
 //  slice.  H = 16 (decode_h16_kernel): one workgroup of four waves per item,
 //  each scoring all 16 heads itself.
 //
-// Softmax in base 2 against a fixed reference per head: the maximum of the
-// item's first slice.  Weights 2^(x - m_ref) may exceed 1 by up to 2^20, which
-// float32 accumulators and bf16 weights carry without loss of relative
-// precision, so the accumulators are never rescaled in registers.  If a
-// later slice exceeds the reference by more than that, the workgroup agrees on
-// it through an LDS vote after the pass, takes the exact per-head maxima in a
-// scores-only pass and redoes the item against them; the result is the same
-// softmax either way.
+// Softmax in base 2 against a reference per head that starts at the maximum
+// of the item's first slice and moves up to a later slice's maximum when that
+// passes it by more than move_t (8 log2 units by default).  A move rescales
+// the row sum and the accumulators of that head; between moves the
+// accumulators are never touched.  Weights 2^(x - m_ref) above 1 are carried
+// without loss of relative precision by the float32 accumulators and the bf16
+// weights.
+//  * H = 16: every wave computes the whole slice's scores, so it moves the
+//    reference before it forms that slice's weights (weights <= 2^move_t).
+//  * H = 128: the two token halves of a slice are scored by two S waves; they
+//    publish their half maxima, and both take the same move one slice later
+//    (the V waves rescale their accumulators before they add that slice).  A
+//    slice can thus push its weights past the reference by its own jump; if
+//    that ever passes 2^safe_jump (64 by default) the workgroup agrees on it
+//    through an LDS vote after the pass, takes the exact per-head maxima in a
+//    scores-only pass and redoes the item against them.
+// The result is the same softmax either way.
 #include <math.h>
 #include <stdlib.h>
 
@@ -67,7 +76,18 @@ using namespace dec;
 constexpr int kStages = 4;
 constexpr int kDmaWaves = 4;
 constexpr int kLoadsPerWave = kSlotBytes / 1024 / kDmaWaves;  // 9 instructions of 1 KiB
-constexpr float kMaxJumpDefault = 20.0f;  // log2 units; see the softmax note above
+// Work items the 128-head kernel redid against exact maxima since the count
+// was last reset (per device; read and reset by exact_pass_count).
+__device__ unsigned long long g_exact_passes = 0;
+
+constexpr float kMoveDefault = 8.0f;       // log2 units: the reference moves past this
+// The 128-head kernel decides reference moves once per window of this many
+// slices (from the previous window's maxima).
+#ifndef MLA_MOVE_WINDOW
+#define MLA_MOVE_WINDOW 8
+#endif
+constexpr int kMoveWindow = MLA_MOVE_WINDOW;
+constexpr float kSafeJumpDefault = 64.0f;  // log2 units: an item is redone past this
 
 // Pipelining depths (steps of LDS reads issued ahead of their MFMAs).
 #ifndef MLA_QK_AHEAD
@@ -118,14 +138,16 @@ constexpr int kHeadsWG = 64;
 constexpr int kHeadBlocksWG = kHeadsWG / 16;        // 4
 constexpr int kPBytesWG = kHeadBlocksWG * 64 * 16;  // 4 KiB of weights per slice
 constexpr int kSWaves = 8;
-static_assert(kStages * kSlotBytes + 2 * kPBytesWG + 256 + kSWaves * 4 + 4 * kHeadsWG * 4 + 4 <= 163840,
+static_assert(kStages * kSlotBytes + 2 * kPBytesWG + 256 + kSWaves * 4 + 4 * kHeadsWG * 4 +
+                      2 * kHeadsWG * 4 + 2 * 4 * 4 + 2 * kHeadsWG * 4 + 4 <=
+                  163840,
               "LDS budget");
 
 __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ items, int num_items, const int32_t* __restrict__ order, int q_len,
-    float scale, float max_jump,
+    float scale, float move_t, float safe_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
   constexpr int H = 128;
@@ -133,7 +155,9 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
   __shared__ __attribute__((aligned(16))) char junk[256];
   __shared__ int ticket_lds;
   __shared__ int votes[kSWaves];          // after a pass: jump flags of the S waves
-  __shared__ float mref_x[2][kHeadsWG];   // per token half: a head's maximum
+  __shared__ float mx_half[2][2][kHeadsWG];  // per window parity and token half: a head's maximum
+  __shared__ float rsc[2][kHeadsWG];      // per window parity: a head's rescale factor
+  __shared__ __attribute__((aligned(16))) int moved[2][kHeadBlocksWG];  // per window parity: slice of the last move
   __shared__ float lsum2[2][kHeadsWG];    // per token half: a head's row sum
   char* const pbuf = lds + kStages * kSlotBytes;
   const uint32_t lds_base =
@@ -181,6 +205,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
 
   auto slot_of = [&](int n) -> const char* { return lds + (n % kStages) * kSlotBytes; };
   auto pbuf_of = [&](int n) -> char* { return pbuf + (n & 1) * kPBytesWG; };
+  if (threadIdx.x < 2 * kHeadBlocksWG) (&moved[0][0])[threadIdx.x] = -2;
 
   // Slot layout: row t, logical chunk c at tile (t / 8, c / 8): (9 (t / 8) +
   // c / 8) KiB + 128 (t % 8) + 16 ((c % 8) ^ swz(t)); rows t and t + 16 are
@@ -245,38 +270,82 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
           __builtin_bit_cast(bf16x4, pk);
     };
 
-    // Full pass.  With `first`, m_ref is the per-head maximum of the first
-    // slice (both token halves, exchanged through LDS) and the lane keeps a
-    // running maximum of its later scores; the pass is discarded (returns
-    // false) if some head's maximum exceeds m_ref by more than max_jump.
-    // Slices 1 .. n-2 are whole, so only the first and the last are masked.
+    // Reference moves, once per window of kMoveWindow slices.  At the end of
+    // window v the S waves publish their half's per-head maximum over the
+    // window (mx_half[v & 1]); when window v + 1 starts (slice k =
+    // kMoveWindow (v + 1)), both S waves of a head block read the two values,
+    // and heads whose window maximum passed m_ref + move_t move their
+    // reference there, before slice k's weights are formed.  The two waves
+    // see the same values and so take the same decision.  The row sum is
+    // rescaled at once; the V waves rescale the accumulators of that head
+    // block before they add slice k (the factor and the slice index of the
+    // move go through LDS).
+    auto move_ref = [&](int k, float mprev) {
+      const bool up = mprev > m_ref + move_t;
+      if (__any(up)) {
+        const float m_new = up ? mprev : m_ref;
+        const float r = __builtin_amdgcn_exp2f(m_ref - m_new);
+        l_run *= r;
+        m_ref = m_new;
+        const int v = k / kMoveWindow;
+        if (th == 0) {
+          if (g == 0) rsc[v & 1][hidx] = r;
+          if (lane == 0) moved[v & 1][hb] = k;
+        }
+      }
+    };
+
+    // Full pass.  With `first`, m_ref starts at the per-head maximum of the
+    // first slice (both token halves, exchanged through LDS) and moves up
+    // during the pass (move_ref); a weight can thus exceed 1 by the jump of
+    // the scores within one window.  The pass is discarded (returns false) if
+    // that ever passes 2^safe_jump.  Without `first`, m_ref holds the exact
+    // maxima and does not move.
     auto full_pass = [&](bool first) -> bool {
-      float m_lane = -INFINITY;
+      float e_lane = -INFINITY;  // largest weight exponent s - m_ref published
+      float m_win = -INFINITY;   // this lane's maximum over the current window
       float s[4];
       __syncthreads();
       scores(slot_of(0), nvalid(0), s);
       if (first) {
         const float m = rows_max(lane_max(s));
-        if (g == 0) mref_x[th][hidx] = m;
+        if (g == 0) mx_half[0][th][hidx] = m;
       }
       __syncthreads();
-      if (first) m_ref = fmaxf(mref_x[0][hidx], mref_x[1][hidx]);
+      if (first) m_ref = fmaxf(mx_half[0][0][hidx], mx_half[0][1][hidx]);
       publish(0, s);
-      for (int k = 1; k < n_slices - 1; ++k) {
+      // slice k (k >= 1) holds nv valid tokens
+      auto step = [&](int k, int nv) {
         __syncthreads();
-        scores(slot_of(k), kSliceTok, s);
-        if (first) m_lane = fmaxf(m_lane, lane_max(s));
+        const bool check = first && k % kMoveWindow == 0;
+        float mp0 = -INFINITY, mp1 = -INFINITY;
+        if (check) {  // the previous window's maxima, read before the MFMAs
+          const int v = k / kMoveWindow - 1;
+          mp0 = mx_half[v & 1][0][hidx];
+          mp1 = mx_half[v & 1][1][hidx];
+        }
+        scores(slot_of(k), nv, s);
+        if (first) {
+          if (check) move_ref(k, fmaxf(mp0, mp1));
+          m_win = fmaxf(m_win, lane_max(s));
+          if (k % kMoveWindow == kMoveWindow - 1) {  // window k / kMoveWindow ends
+            // m_ref is constant within a window: its weights' largest exponent
+            e_lane = fmaxf(e_lane, m_win - m_ref);
+            const float mh = rows_max(m_win);  // every lane takes part in the row permutes
+            if (g == 0) mx_half[(k / kMoveWindow) & 1][th][hidx] = mh;
+            m_win = -INFINITY;
+          }
+        }
         publish(k, s);
-      }
-      if (n_slices > 1) {
-        __syncthreads();
-        scores(slot_of(n_slices - 1), nvalid(n_slices - 1), s);
-        if (first) m_lane = fmaxf(m_lane, lane_max(s));
-        publish(n_slices - 1, s);
-      }
+      };
+      // slices 1 .. n-2 are whole (the constant count lets the compiler drop
+      // the mask); only the first and the last can be short
+      for (int k = 1; k < n_slices - 1; ++k) step(k, kSliceTok);
+      if (n_slices > 1) step(n_slices - 1, nvalid(n_slices - 1));
+      e_lane = fmaxf(e_lane, m_win - m_ref);  // a last, partial window
       __syncthreads();
-      // vote: did a head of any S wave jump?
-      const bool mine = __any(first && rows_max(m_lane) > m_ref + max_jump);
+      // vote: did a weight of any S wave pass 2^safe_jump?
+      const bool mine = __any(first && e_lane > safe_jump);
       if (lane == 0) votes[w] = mine ? 1 : 0;
       __syncthreads();
       int any = 0;
@@ -287,8 +356,10 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     };
 
     if (!full_pass(true)) {
-      // A head's maximum jumped by more than max_jump: exact maxima first,
-      // then the item again against them (every weight <= 1).
+      // A weight passed 2^safe_jump (one slice jumped that far past the
+      // reference): exact maxima first, then the item again against them
+      // (every weight <= 1, no moves).
+      if (threadIdx.x == 0) atomicAdd(&g_exact_passes, 1ull);
       float m_lane = -INFINITY;
       for (int k = 0; k < n_slices; ++k) {
         __syncthreads();
@@ -298,9 +369,9 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       }
       __syncthreads();
       const float m = rows_max(m_lane);
-      if (g == 0) mref_x[th][hidx] = m;
+      if (g == 0) mx_half[0][th][hidx] = m;
       __syncthreads();
-      m_ref = fmaxf(mref_x[0][hidx], mref_x[1][hidx]);
+      m_ref = fmaxf(mx_half[0][0][hidx], mx_half[0][1][hidx]);
       l_run = 0.f;
       full_pass(false);
     }
@@ -393,8 +464,17 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
 #pragma unroll
         for (int hb = 0; hb < kHeadBlocksWG; ++hb) oacc[c][hb] = float4_t{0.f, 0.f, 0.f, 0.f};
     };
-    // O^T[64 columns x 64 heads] += C^T . P^T for one slice
-    auto accumulate = [&](const char* slot, const char* pb) {
+    // O^T[64 columns x 64 heads] += C^T . P^T for slice k; with `moves`, first
+    // the rescale of the head blocks whose reference moved at slice k
+    auto accumulate = [&](int k, bool moves) {
+      const char* slot = slot_of(k);
+      const char* pb = pbuf_of(k);
+      // the slice indices of the last moves first (at window starts), then
+      // every operand read of the slice; the scheduling barrier keeps that
+      // order, so the move test waits only for its own read
+      moves = moves && k > 0 && k % kMoveWindow == 0;  // moves happen at window starts only
+      int4 mv = {-1, -1, -1, -1};
+      if (moves) mv = *reinterpret_cast<const int4*>(&moved[(k / kMoveWindow) & 1][0]);
       bf16x8 pf[kHeadBlocksWG];
 #pragma unroll
       for (int hb = 0; hb < kHeadBlocksWG; ++hb)
@@ -405,6 +485,27 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
         f0[c] = lds_read_tr(slot, pv_off(4 * u + c));
         f1[c] = lds_read_tr(slot, pv_off(4 * u + c) + kRowGroup2);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (moves) {
+        const int hit = (__builtin_amdgcn_readfirstlane(mv.x) == k ? 1 : 0) |
+                        (__builtin_amdgcn_readfirstlane(mv.y) == k ? 2 : 0) |
+                        (__builtin_amdgcn_readfirstlane(mv.z) == k ? 4 : 0) |
+                        (__builtin_amdgcn_readfirstlane(mv.w) == k ? 8 : 0);
+        if (hit) {
+          // whole-vector products, written out per head block: indexed element
+          // updates in a loop kept the compiler from holding oacc in registers
+          static_assert(kHeadBlocksWG == 4, "one line per head block below");
+          const int v = (k / kMoveWindow) & 1;
+          const float r0 = (hit & 1) ? rsc[v][q] : 1.f;
+          const float r1 = (hit & 2) ? rsc[v][16 + q] : 1.f;
+          const float r2 = (hit & 4) ? rsc[v][32 + q] : 1.f;
+          const float r3 = (hit & 8) ? rsc[v][48 + q] : 1.f;
+          oacc[0][0] *= r0; oacc[1][0] *= r0; oacc[2][0] *= r0; oacc[3][0] *= r0;
+          oacc[0][1] *= r1; oacc[1][1] *= r1; oacc[2][1] *= r1; oacc[3][1] *= r1;
+          oacc[0][2] *= r2; oacc[1][2] *= r2; oacc[2][2] *= r2; oacc[3][2] *= r2;
+          oacc[0][3] *= r3; oacc[1][3] *= r3; oacc[2][3] *= r3; oacc[3][3] *= r3;
+        }
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const bf16x8 a = __builtin_shufflevector(f0[c], f1[c], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -413,7 +514,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
           oacc[c][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[hb], oacc[c][hb], 0, 0, 0);
       }
     };
-    auto full_pass = [&]() -> bool {
+    auto full_pass = [&](bool first) -> bool {
       if (dma) {
         issue(0);
         if (n_slices > 1) issue(1);
@@ -428,7 +529,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
         __syncthreads();
         if (dma && k + 2 < n_slices) issue(k + 2);
         prefetch(k + MLA_PREFETCH_D);
-        accumulate(slot_of(k - 1), pbuf_of(k - 1));
+        accumulate(k - 1, first);
       }
       // vote (written by the S waves)
       __syncthreads();
@@ -440,7 +541,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     };
 
     zero_acc();
-    if (!full_pass()) {
+    if (!full_pass(true)) {
       // exact-maximum pass of the S waves: stream the slices again
       if (dma) {
         issue(0);
@@ -454,7 +555,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       __syncthreads();
       __syncthreads();  // the S waves' maximum exchange
       zero_acc();
-      full_pass();
+      full_pass(false);
     }
     // epilogue: normalise by the row sums of the S waves and write the partial
     // (or, for a sequence with one item in merged mode, o~ itself)
@@ -538,12 +639,11 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ items, int num_items, const int32_t* __restrict__ order, int q_len,
-    float scale, float max_jump,
+    float scale, float move_t, float safe_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
   constexpr int H = 16;
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes];
-  __shared__ int votes[4];
   __shared__ int ticket_lds;
   const uint32_t lds_base =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
@@ -688,33 +788,44 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
           __builtin_shufflevector(f0[c], f1[c], 0, 1, 2, 3, 4, 5, 6, 7), pf, oacc[c], 0, 0, 0);
   };
 
-  // Full pass (see the softmax note at the top); every wave computes the same
-  // scores, the vote only keeps the waves' control flow provably identical.
-  auto full_pass = [&](bool first, bool started) -> bool {
+  // The pass.  Every wave computes the same scores (the same operands in the
+  // same order), so every wave takes the same softmax decisions: the
+  // reference starts at the first slice's per-head maximum and moves up to a
+  // slice's maximum, before that slice's weights are formed, when the maximum
+  // passes it by more than move_t.  A move rescales the wave's own
+  // accumulators and row sum; weights never exceed 2^move_t.
+  auto full_pass = [&]() {
 #pragma unroll
     for (int c = 0; c < 8; ++c) oacc[c] = float4_t{0.f, 0.f, 0.f, 0.f};
     l_run = 0.f;
-    float m_lane = -INFINITY;
-    if (!started) start();
     for (int n = 0; n < n_slices; ++n) {
       enter(n);
       float s[2][4];
       scores(slot_of(n), nvalid(n), s);
-      if (first) {
-        if (n == 0)
-          m_ref = rows_max(lane_max(s));
-        else
-          m_lane = fmaxf(m_lane, lane_max(s));
+      const float mx = rows_max(lane_max(s));
+      if (n == 0) {
+        m_ref = mx;
+      } else {
+        const bool up = mx > m_ref + move_t;
+        if (__any(up)) {
+          const float m_new = up ? mx : m_ref;
+          const float r = __builtin_amdgcn_exp2f(m_ref - m_new);
+          l_run *= r;
+          // whole-vector products, written out: indexed element updates inside
+          // the branch kept the compiler from holding oacc in registers
+          oacc[0] *= r;
+          oacc[1] *= r;
+          oacc[2] *= r;
+          oacc[3] *= r;
+          oacc[4] *= r;
+          oacc[5] *= r;
+          oacc[6] *= r;
+          oacc[7] *= r;
+          m_ref = m_new;
+        }
       }
       accumulate(slot_of(n), s);
     }
-    const bool mine = __any(first && rows_max(m_lane) > m_ref + max_jump);
-    __syncthreads();
-    if (lane == 0) votes[w] = mine ? 1 : 0;
-    __syncthreads();
-    const bool any = (votes[0] | votes[1] | votes[2] | votes[3]) != 0;
-    __syncthreads();
-    return !any;
   };
 
   // The 16 Q rows of this item (18 KiB, contiguous in q_abs) go to ring slot 3
@@ -740,19 +851,7 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qlds + 64 * ks);
   }
 
-  if (!full_pass(true, true)) {
-    float m_lane = -INFINITY;
-    start();
-    for (int n = 0; n < n_slices; ++n) {
-      enter(n);
-      float s[2][4];
-      scores(slot_of(n), nvalid(n), s);
-      m_lane = fmaxf(m_lane, lane_max(s));
-    }
-    __syncthreads();
-    m_ref = rows_max(m_lane);
-    full_pass(false, false);
-  }
+  full_pass();
 
   const float l = rows_sum(l_run);
   if (w == 0 && g == 0) {
@@ -819,17 +918,41 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
   }
 }
 
-// Threshold (log2 units) beyond which a head's score maximum triggers the
-// exact-maximum pass.  MLA_DECODE_MAX_JUMP overrides it (a value in (0, 30]),
-// which lets tests drive that pass with ordinary inputs.
-float max_jump() {
+// Reference-move threshold (log2 units).  MLA_DECODE_MAX_JUMP overrides it (a
+// value in (0, 30]); tests use a small value to move the reference on
+// ordinary inputs.
+float move_threshold() {
   const char* e = getenv("MLA_DECODE_MAX_JUMP");
-  if (!e) return kMaxJumpDefault;
+  if (!e) return kMoveDefault;
   const float v = strtof(e, nullptr);
-  return (v > 0.f && v <= 30.f) ? v : kMaxJumpDefault;
+  return (v > 0.f && v <= 30.f) ? v : kMoveDefault;
+}
+
+// Largest weight exponent (log2 units past the reference) the 128-head kernel
+// keeps before it redoes an item against exact maxima.  MLA_DECODE_SAFE_JUMP
+// overrides it (a value in (0, 100]); tests use a small value to drive that
+// pass with ordinary inputs.
+float safe_jump() {
+  const char* e = getenv("MLA_DECODE_SAFE_JUMP");
+  if (!e) return kSafeJumpDefault;
+  const float v = strtof(e, nullptr);
+  return (v > 0.f && v <= 100.f) ? v : kSafeJumpDefault;
 }
 
 }  // namespace
+
+hipError_t exact_pass_count(uint64_t* count, bool reset) {
+  unsigned long long v = 0;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_exact_passes), sizeof(v));
+  if (e != hipSuccess) return e;
+  if (reset) {
+    const unsigned long long zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_exact_passes), &zero, sizeof(zero));
+    if (e != hipSuccess) return e;
+  }
+  *count = v;
+  return hipSuccess;
+}
 
 hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const void* kv_cache,
                        const int32_t* block_table, int max_pages, const int32_t* seq_lens,
@@ -843,13 +966,15 @@ hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const vo
     hipLaunchKernelGGL(decode_h128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(1024), 0, stream,
                        static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
                        block_table, max_pages, seq_lens, items, num_items, order, q_len, d.softmax_scale,
-                       max_jump(), o_part, lse_part, split_offsets, tickets, o_latent, lse_out);
+                       move_threshold(), safe_jump(), o_part, lse_part, split_offsets, tickets, o_latent,
+                       lse_out);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(decode_h16_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
                      block_table, max_pages, seq_lens, items, num_items, order, q_len, d.softmax_scale,
-                     max_jump(), o_part, lse_part, split_offsets, tickets, o_latent, lse_out);
+                     move_threshold(), safe_jump(), o_part, lse_part, split_offsets, tickets, o_latent,
+                       lse_out);
   return hipGetLastError();
 }
 

@@ -247,6 +247,12 @@ mla_status mla_combine_multi(const mla_dims* dims, int32_t batch, int32_t q_len,
   return combine_impl(dims, batch, q_len, split_offsets, o_part, lse_part, o_latent, lse, stream);
 }
 
+mla_status mla_decode_exact_pass_count(int32_t reset, uint64_t* count_host) {
+  if (!count_host) return MLA_ERR_INVALID_ARG;
+  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
+  return launched(exact_pass_count(count_host, reset != 0));
+}
+
 mla_status mla_check_paging(const mla_dims* dims, int32_t batch, int32_t min_len,
                             const int32_t* seq_lens, int32_t num_pages, const int32_t* block_table,
                             int32_t max_pages_per_seq, int32_t* result, void* stream) {

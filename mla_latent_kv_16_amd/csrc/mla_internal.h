@@ -44,6 +44,9 @@ hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const v
 // sequence's partials into o_latent / lse_out (split_offsets as for combine;
 // q_len 1 only).  q_len query tokens per sequence: q_abs rows b * q_len + t,
 // partial rows item * q_len + t.
+// Items the 128-head fast decode redid against exact maxima on the current
+// device since the last reset (synchronous copies of a device counter).
+hipError_t exact_pass_count(uint64_t* count, bool reset);
 // order: null, or the item each dispatch slot takes (a permutation of the items).
 hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const void* kv_cache,
                        const int32_t* block_table, int max_pages, const int32_t* seq_lens,

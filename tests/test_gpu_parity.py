@@ -69,24 +69,34 @@ def test_generic_heads64(mla):
     compare_with_oracle(wl, out, range(2))
 
 
-def test_score_jump_takes_exact_path(mla):
-    # The first 32-token slice has small scores; later latents are scaled up so
-    # a head's maximum jumps far beyond the first slice's (the decode kernel
-    # then redoes the item against exact maxima).  Scores are ~8x larger than
-    # usual, and so is the absolute error that bf16 rounding of q_abs puts on
-    # them: lse is held to 2e-3 of its magnitude instead of 1e-2 absolute.
-    cfg = small(V2, "v2_jump", 2, permute_pages=True)
-    lens = np.array([700, 200], np.int32)
-    wl = generate(cfg, lens=lens)
+def _scale_latents(wl, first, factor):
+    """Multiply the latent part of every cached row from token `first` on."""
     from synth import bf16_bits_to_f32, f32_to_bf16_bits
-    for b in range(2):
-        for j in range(32, int(lens[b])):
+    for b in range(wl.cfg.batch):
+        for j in range(first, int(wl.seq_lens[b])):
             p, s = wl.block_table[b, j // 64], j % 64
             row = bf16_bits_to_f32(wl.cache[p, s])
-            row[:512] *= 8.0
+            row[:512] *= factor
             wl.cache[p, s] = f32_to_bf16_bits(row)
-    say("[score jump]")
+
+
+@pytest.mark.parametrize("heads", [128, 16])
+def test_score_jump_moves_reference(mla, heads):
+    # The first 32-token slice has small scores; later latents are scaled up so
+    # a head's maximum jumps far beyond the first slice's (several moves of
+    # the softmax reference, each rescaling the accumulators).  The jump of
+    # any one slice stays far below 2^64, so no item is redone.  Scores are
+    # ~8x larger than usual, and so is the absolute error that bf16 rounding
+    # of q_abs puts on them: lse is held to 2e-3 of its magnitude instead of
+    # 1e-2 absolute.
+    cfg = small(V2, "v2_jump", 2, n_heads=heads, permute_pages=True)
+    lens = np.array([700, 200], np.int32)
+    wl = generate(cfg, lens=lens)
+    _scale_latents(wl, 32, 8.0)
+    say(f"[score jump H={heads}]")
+    mla.exact_pass_count(reset=True)
     out = run(wl)
+    assert mla.exact_pass_count() == 0
     from oracle import decode_workload
     ref = decode_workload(wl)
     assert_close(out["o_latent"], ref["o_latent"], "o_latent")
@@ -94,15 +104,33 @@ def test_score_jump_takes_exact_path(mla):
     assert_lse(out["lse"], ref["lse"], tol=2e-3 * float(np.abs(ref["lse"]).max()))
 
 
-def test_exact_max_pass_forced(mla, monkeypatch):
-    # A 0.25 (log2) threshold sends nearly every work item through the
-    # exact-maximum pass on ordinary inputs.
-    cfg = small(V2, "v2_forced", len(RAGGED), permute_pages=True)
+@pytest.mark.parametrize("heads", [128, 16])
+def test_reference_moves_forced(mla, monkeypatch, heads):
+    # A 0.25 (log2) threshold moves the reference on ordinary inputs in most
+    # work items (every time a slice's maximum passes it by that much).
+    cfg = small(V2, "v2_moves", len(RAGGED), n_heads=heads, permute_pages=True)
     wl = generate(cfg, lens=np.array(RAGGED, np.int32))
     base = run(wl)
     monkeypatch.setenv("MLA_DECODE_MAX_JUMP", "0.25")
-    say("[forced exact-max pass]")
+    say(f"[forced reference moves H={heads}]")
     forced = run(wl, items=base["items"], offs=base["offs"])
+    compare_with_oracle(wl, forced, range(len(RAGGED)))
+    assert_close(forced["o_latent"], base["o_latent"], "forced vs default", 3e-3, 1e-2)
+
+
+def test_exact_pass_forced(mla, monkeypatch):
+    # A 0.25 (log2) bound on the weights sends nearly every work item of the
+    # 128-head kernel through the exact-maximum pass on ordinary inputs.
+    cfg = small(V2, "v2_exact", len(RAGGED), permute_pages=True)
+    wl = generate(cfg, lens=np.array(RAGGED, np.int32))
+    base = run(wl)
+    monkeypatch.setenv("MLA_DECODE_SAFE_JUMP", "0.25")
+    say("[forced exact-max pass]")
+    mla.exact_pass_count(reset=True)
+    forced = run(wl, items=base["items"], offs=base["offs"])
+    n = mla.exact_pass_count(reset=True)
+    say(f"  items redone: {n} of {2 * len(base['items'])} workgroups")
+    assert n > 0
     compare_with_oracle(wl, forced, range(len(RAGGED)))
     assert_close(forced["o_latent"], base["o_latent"], "forced vs default", 3e-3, 1e-2)
 
