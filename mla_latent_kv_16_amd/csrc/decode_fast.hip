@@ -53,13 +53,14 @@
 // weights.
 //  * H = 16: every wave computes the whole slice's scores, so it moves the
 //    reference before it forms that slice's weights (weights <= 2^move_t).
-//  * H = 128: the two token halves of a slice are scored by two S waves; they
-//    publish their half maxima, and both take the same move one slice later
-//    (the V waves rescale their accumulators before they add that slice).  A
-//    slice can thus push its weights past the reference by its own jump; if
-//    that ever passes 2^safe_jump (64 by default) the workgroup agrees on it
-//    through an LDS vote after the pass, takes the exact per-head maxima in a
-//    scores-only pass and redoes the item against them.
+//  * H = 128: the two token halves of a slice are scored by two S waves.  They
+//    publish their maxima over each window of kMoveWindow slices, and both
+//    take the same move when the next window starts (the V waves rescale
+//    their accumulators before they add that window's first slice).  Inside a
+//    window the weights can thus pass the reference by the window's own jump;
+//    if that ever passes 2^safe_jump (64 by default) the workgroup agrees on
+//    it through an LDS vote after the pass, takes the exact per-head maxima in
+//    a scores-only pass and redoes the item against them.
 // The result is the same softmax either way.
 #include <math.h>
 #include <stdlib.h>

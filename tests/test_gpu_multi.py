@@ -103,6 +103,7 @@ CASES = [
      [1, 62, 65, 127]),
     ("h128_T3_few_items", small(V2, "q128c", 3, permute_pages=True), [700, 5000, 12], 3, 256,
      [0, 127]),
+    ("h128_T8", small(V2, "q128d", 3, permute_pages=True), [8, 1000, 8200], 8, 2048, [2, 70, 127]),
     ("h16_T2", small(LITE, "q16a", 5, permute_pages=True), [2, 64, 65, 4097, 700], 2, 2048, None),
     ("h16_T5", small(LITE, "q16b", 4, permute_pages=True), [5, 69, 3333, 8000], 5, 2048, None),
     ("tiny_f32_T3", CONFIGS["tiny_f32"], None, 3, 64, None),
