@@ -228,8 +228,10 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
   // A operand: W^UV row 16w + q, values 32ks + 8g .. +8
   const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * kDh + 16 * w + q) * kDc + 8 * g;
   bf16x8 a[16];
+  auto load_w = [&]() {
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(wrow + 32 * ks);
+    for (int ks = 0; ks < 16; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(wrow + 32 * ks);
+  };
 
   // thread t stages float4 column 4 (t % 128) of rows t / 128 + 4 i, i < kOutF4
   const int c4 = 4 * (threadIdx.x & 127);
@@ -237,96 +239,109 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
   float4_t v[kOutF4];
   if constexpr (kMerge) {
     // Row rl = rl0 + 4i has items s0[i] .. s0[i] + ns[i] - 1 (the same for
-    // every lane of a wave).  Items go kPair at a time (fewer rows per
-    // thread, more items) with the loads of all the thread's rows in flight
-    // together: the partials and lse of the first kPair are loaded before
-    // anything waits; a first pass takes M over the lse of the rest, a
-    // second forms Z and the weighted sum.  Each row's arithmetic is
-    // the combine's, in item order, so every thread of a row computes the same
-    // M and Z and o~ matches mla_combine bit for bit.
+    // every lane of a wave).  The loads go out in three rounds, each in
+    // flight as a whole: (1) the split offsets of the workgroup's sequences,
+    // one per lane (per-row scalar loads were issued one round trip apart),
+    // then W^UV; (2) the lse of up to kChunk items of every row, one per
+    // lane, and the partials of the first kPair items of every row (16 float4
+    // per thread); (3) the partials of later items, kPair at a time.  M is a
+    // max over the lanes of a row; the weights exp(lse - M), Z and the
+    // weighted sum are taken in item order, each row's arithmetic exactly the
+    // combine's, so o~ matches mla_combine bit for bit.
     // Loads are unconditional (a row past the end, or an item past a row's
     // last, reads the row's last item and the value is then replaced), so no
-    // branch separates them and all of them are in flight together; the
-    // planner gives every sequence at least one item.
-    constexpr int kPair = 16 / kOutF4;  // items per load round: 2, 4 or 8
+    // branch separates them; the planner gives every sequence at least one
+    // item.
+    constexpr int kPair = 16 / kOutF4;   // items per load round of partials: 2, 4 or 8
+    constexpr int kChunk = 64 / kOutF4;  // items per lse load: 8, 16 or 32
+    // (a row's sequence: one query token per sequence is the common case, and
+    // it needs no division)
+    const bool one = q_len == 1;
+    const int b_first = one ? r0 : r0 / q_len;
+    const int nseq = (one ? r0 + nr - 1 : (r0 + nr - 1) / q_len) - b_first + 1;  // <= kOutRows < 64
+    const int off_v = offs[b_first + min(lane, nseq)];     // offs[b_first + lane]
+    load_w();
     int s0[kOutF4], ns[kOutF4], nv[kOutF4], tq[kOutF4];
     int nsmax = 0;
 #pragma unroll
     for (int i = 0; i < kOutF4; ++i) {
       const int rl = rl0 + 4 * i;
       const int r = r0 + min(rl, nr - 1);
-      const int b = r / q_len;
-      tq[i] = r % q_len;
-      s0[i] = offs[b];
-      nv[i] = offs[b + 1] - s0[i];
+      const int b = one ? r : r / q_len;
+      tq[i] = r - b * q_len;
+      s0[i] = __builtin_amdgcn_readlane(off_v, b - b_first);
+      nv[i] = __builtin_amdgcn_readlane(off_v, b - b_first + 1) - s0[i];
       ns[i] = rl < nr ? nv[i] : 0;
       nsmax = max(nsmax, ns[i]);
     }
+    // lane l holds the lse of item kc + l / kOutF4 of row l % kOutF4
+    const int li = lane % kOutF4, lk = lane / kOutF4;
+    int s0_l = s0[0], nv_l = nv[0], ns_l = ns[0], tq_l = tq[0];
+#pragma unroll
+    for (int i = 1; i < kOutF4; ++i) {
+      const bool mine = li == i;
+      s0_l = mine ? s0[i] : s0_l;
+      nv_l = mine ? nv[i] : nv_l;
+      ns_l = mine ? ns[i] : ns_l;
+      tq_l = mine ? tq[i] : tq_l;
+    }
+    auto lse_raw = [&](int kc) -> float {  // the load; lse_sel masks it
+      const int kk = max(0, min(kc + lk, nv_l - 1));
+      return lse_part[(static_cast<int64_t>(s0_l + kk) * q_len + tq_l) * H + h];
+    };
+    auto lse_sel = [&](int kc, float l) { return kc + lk < ns_l ? l : -INFINITY; };
+    auto lse_at = [&](int kc) { return lse_sel(kc, lse_raw(kc)); };
+    auto row_max = [&](float x) {
+#pragma unroll
+      for (int m = kOutF4; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m));
+      return x;
+    };
     auto prow = [&](int i, int k) -> int64_t {  // row of item min(k, last) of row i
       const int kk = max(0, min(k, nv[i] - 1));
       return (static_cast<int64_t>(s0[i] + kk) * q_len + tq[i]) * H + h;
     };
     float4_t x[kPair][kOutF4];
-    float lv[kPair][kOutF4];
     auto load_pair = [&](int k) {
 #pragma unroll
       for (int u = 0; u < kPair; ++u)
 #pragma unroll
         for (int i = 0; i < kOutF4; ++i) {
-          const bool ok = k + u < ns[i];
           const float4_t xv = *reinterpret_cast<const float4_t*>(o_part + prow(i, k + u) * kDc + c4);
-          const float l = lse_part[prow(i, k + u)];
-          x[u][i] = ok ? xv : float4_t{0.f, 0.f, 0.f, 0.f};
-          lv[u][i] = ok ? l : -INFINITY;
+          x[u][i] = k + u < ns[i] ? xv : float4_t{0.f, 0.f, 0.f, 0.f};
         }
     };
+    float lv = lse_raw(0);
+    __builtin_amdgcn_sched_barrier(0);  // the lse load goes out before the partials
     load_pair(0);
+    lv = lse_sel(0, lv);
+    float mv = row_max(lv);  // M of the lane's row, on every lane of that row
+    for (int kc = kChunk; kc < nsmax; kc += kChunk) mv = fmaxf(mv, row_max(lse_at(kc)));
+    float wv = expf(lv - mv);  // weight of the lane's (row, item)
     float M[kOutF4], Z[kOutF4];
 #pragma unroll
     for (int i = 0; i < kOutF4; ++i) {
-      M[i] = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < kPair; ++u)
-        if (u < ns[i]) M[i] = fmaxf(M[i], lv[u][i]);
+      M[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mv), i));
+      Z[i] = 0.f;
+      v[i] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
-    for (int k = kPair; k < nsmax; k += kPair) {  // M over the remaining items (lse only)
-      float lm[kPair][kOutF4];
-#pragma unroll
-      for (int u = 0; u < kPair; ++u)
-#pragma unroll
-        for (int i = 0; i < kOutF4; ++i) {
-          const float l = lse_part[prow(i, k + u)];
-          lm[u][i] = k + u < ns[i] ? l : -INFINITY;
-        }
-#pragma unroll
-      for (int i = 0; i < kOutF4; ++i)
-#pragma unroll
-        for (int u = 0; u < kPair; ++u)
-          if (k + u < ns[i]) M[i] = fmaxf(M[i], lm[u][i]);
-    }
-    auto accumulate = [&](int k, const float4_t (&xs)[kPair][kOutF4], const float (&ls)[kPair][kOutF4]) {
+    for (int k = 0; k < nsmax; k += kPair) {
+      if (k > 0) {
+        if (k % kChunk == 0) wv = expf(lse_at(k) - mv);
+        load_pair(k);
+      }
 #pragma unroll
       for (int i = 0; i < kOutF4; ++i)
 #pragma unroll
         for (int u = 0; u < kPair; ++u) {
           if (k + u >= ns[i]) continue;
-          const float wgt = expf(ls[u][i] - M[i]);
+          const float wgt = __int_as_float(
+              __builtin_amdgcn_readlane(__float_as_int(wv), (k + u) % kChunk * kOutF4 + i));
           Z[i] += wgt;
-          v[i][0] = fmaf(wgt, xs[u][i][0], v[i][0]);
-          v[i][1] = fmaf(wgt, xs[u][i][1], v[i][1]);
-          v[i][2] = fmaf(wgt, xs[u][i][2], v[i][2]);
-          v[i][3] = fmaf(wgt, xs[u][i][3], v[i][3]);
+          v[i][0] = fmaf(wgt, x[u][i][0], v[i][0]);
+          v[i][1] = fmaf(wgt, x[u][i][1], v[i][1]);
+          v[i][2] = fmaf(wgt, x[u][i][2], v[i][2]);
+          v[i][3] = fmaf(wgt, x[u][i][3], v[i][3]);
         }
-    };
-#pragma unroll
-    for (int i = 0; i < kOutF4; ++i) {
-      Z[i] = 0.f;
-      v[i] = float4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    accumulate(0, x, lv);
-    for (int k = kPair; k < nsmax; k += kPair) {  // weighted sum of the remaining items
-      load_pair(k);
-      accumulate(k, x, lv);
     }
 #pragma unroll
     for (int i = 0; i < kOutF4; ++i) {
@@ -345,6 +360,7 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
       }
     }
   } else {
+    load_w();
 #pragma unroll
     for (int i = 0; i < kOutF4; ++i) {
       const int rl = rl0 + 4 * i;

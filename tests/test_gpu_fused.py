@@ -50,6 +50,8 @@ def partials(wl, dev, slots, T):
     ("h16", small(LITE, "f16", 5, permute_pages=True), [1, 100, 4096, 4097, 700], 2048, 1),
     ("h16_T2_many_rows", small(LITE, "f16b", 40, lens=(2, 2000), permute_pages=True), None, 512, 2),
     ("h16_ragged_rows", small(LITE, "f16c", 21, lens=(1, 3000), permute_pages=True), None, 512, 1),
+    # 8-row groups and up to ~140 one-page items per row: several lse chunks
+    ("h16_many_items", small(LITE, "f16d", 3, permute_pages=True), [5000, 9000, 100], 2048, 1),
     ("tiny_f32", CONFIGS["tiny_f32"], None, 64, 1),
     ("tiny_f32_T4", CONFIGS["tiny_f32"], None, 64, 4),
 ])
