@@ -18,10 +18,13 @@
 //    wave at a time: D^T[128 x 16 rows] = W_i[128 x 512] . c^T[512 x 16 rows]
 //    with v_mfma_f32_16x16x32_bf16, the latent rows read straight from the
 //    paged cache, float32 accumulation rounded to bf16.
-//  * attention: one workgroup of four waves per (128 query tokens, head,
-//    sequence), one wave per 32 queries (two blocks of 16, so that every K or
-//    V fragment read from LDS feeds two MFMAs); keys in tiles of 32 staged in
-//    LDS for all four waves (K row-major, V transposed), with an online
+//  * attention: one workgroup of eight waves per (256 query tokens, head,
+//    sequence), numbered so that all query blocks of one (sequence, head)
+//    run on one XCD at about the same time (they stream the same keys and
+//    values, which that XCD's L2 then serves); one wave per 32 queries (two
+//    blocks of 16, so that every K or V fragment read from LDS feeds two
+//    MFMAs); keys in tiles of 32 staged in LDS for all eight waves (two
+//    buffers, K row-major, V transposed), with an online
 //    softmax in base 2 whose reference moves only when the running maximum
 //    gains more than 2^8 (the accumulators are rescaled only then).
 //    S^T[16 keys x 16 queries] on MFMA (K rows as A, the query tile as B, 6
@@ -30,6 +33,7 @@
 //    accumulators hold, so P^T needs no reshuffle.
 #include <math.h>
 
+#include "decode_common.h"
 #include "device_common.h"
 #include "mla_internal.h"
 
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(512) void materialise_kv_kernel(
 // rows a half-wave reads in distinct bank groups).
 constexpr int kKRowB = 2 * (kDh + kDr) + 16;  // 400
 constexpr int kVRowB = 2 * kDh + 32;          // 288
-constexpr int kAttnWaves = 4;                  // query tiles per workgroup
+constexpr int kAttnWaves = 8;                  // query tiles per workgroup
 
 __device__ __forceinline__ uint64_t lds_tr4(const char* lds, uint32_t off) {
   const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -141,20 +145,27 @@ __device__ __forceinline__ uint64_t lds_tr4(const char* lds, uint32_t off) {
   return __builtin_bit_cast(uint64_t, v);
 }
 
-__global__ __launch_bounds__(64 * kAttnWaves, 2) void prefill_attn_kernel(
-    int H, int q_len, int max_rows, float scale, PrefillTheta theta,
+__global__ __launch_bounds__(64 * kAttnWaves, 1) void prefill_attn_kernel(
+    int H, int batch, int q_len, int max_rows, float scale, PrefillTheta theta,
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const uint16_t* __restrict__ cache, const int32_t* __restrict__ block_table, int max_pages,
     const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, float* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) char ks_lds[kKeyTile * kKRowB];
-  __shared__ __attribute__((aligned(16))) char v_lds[kKeyTile * kVRowB];
-  const int b = blockIdx.z, h = blockIdx.y;
+  // two buffers: the next tile is stored while the waves compute on this one
+  __shared__ __attribute__((aligned(16))) char ks_buf[2][kKeyTile * kKRowB];
+  __shared__ __attribute__((aligned(16))) char v_buf[2][kKeyTile * kVRowB];
+  // block -> (query block, sequence and head): the query blocks of one
+  // (sequence, head) share an XCD (blocks i and i + 8 do) and follow each
+  // other in dispatch order
+  const int n_qblk = (q_len + kAttnWaves * kQWave - 1) / (kAttnWaves * kQWave);
+  int bh, qblk;
+  dec::block_to_item(blockIdx.x, batch * H, n_qblk, bh, qblk);
+  const int b = bh / H, h = bh % H;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int g = lane >> 4, q = lane & 15;
   const int L = seq_lens[b];
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
-  const int t0 = (blockIdx.x * kAttnWaves + w) * kQWave;   // this wave's first query
+  const int t0 = (qblk * kAttnWaves + w) * kQWave;   // this wave's first query
   // query block qb: tokens t0 + 16qb .. +15; this lane's token (B operand column)
   int pos[kQB];
   bool tvalid[kQB];
@@ -166,7 +177,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, 2) void prefill_attn_kernel(
   }
   // last position of this wave's and of the workgroup's queries (-1: none)
   const int p_wave = t0 < q_len ? L - q_len + min(t0 + kQWave, q_len) - 1 : -1;
-  const int tw_end = min((blockIdx.x + 1) * kAttnWaves * kQWave, q_len);
+  const int tw_end = min((qblk + 1) * kAttnWaves * kQWave, q_len);
   const int p_wg = L - q_len + tw_end - 1;
 
   // Query tiles as the B operand: dimensions 32ks + 8g .. +8 of the lane's token
@@ -207,38 +218,40 @@ __global__ __launch_bounds__(64 * kAttnWaves, 2) void prefill_attn_kernel(
     l_run[qb] = 0.f;
   }
 
-  // Tile staging, software-pipelined: the 256 threads load the next tile into
-  // registers (K^C and V: keys i/16 and 16 + i/16, chunk i%16; k^R: key i/8,
-  // chunk i%8) while the waves compute on the one in LDS.
-  static_assert(kKeyTile * 16 == 2 * 64 * kAttnWaves && kKeyTile * 8 == 64 * kAttnWaves, "staging split");
-  bf16x8 rk[2], rv[2], rr;
+  // Tile staging, software-pipelined over two LDS buffers: the 512 threads
+  // hold the next tile in registers (K^C and V: key i/16, chunk i%16; k^R,
+  // threads < 256: key i/8, chunk i%8), store it into the free buffer at the
+  // top of an iteration and load the one after it, then the waves compute on
+  // the buffer stored there.  One barrier per tile: a buffer is stored again
+  // two iterations after it was read, with a barrier in between.
+  static_assert(kKeyTile * 16 == 64 * kAttnWaves && kKeyTile * 8 == 32 * kAttnWaves, "staging split");
+  bf16x8 rk, rv, rr;
+  const bool rope_thread = threadIdx.x < kKeyTile * 8;
   auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = threadIdx.x + u * 64 * kAttnWaves;
-      const int key = min(k0 + (i >> 4), L - 1);
-      rk[u] = *reinterpret_cast<const bf16x8*>(kh + static_cast<int64_t>(key) * kDh + 8 * (i & 15));
-      rv[u] = *reinterpret_cast<const bf16x8*>(vh + static_cast<int64_t>(key) * kDh + 8 * (i & 15));
+    const int i = threadIdx.x;
+    const int key = min(k0 + (i >> 4), L - 1);
+    rk = *reinterpret_cast<const bf16x8*>(kh + static_cast<int64_t>(key) * kDh + 8 * (i & 15));
+    rv = *reinterpret_cast<const bf16x8*>(vh + static_cast<int64_t>(key) * kDh + 8 * (i & 15));
+    if (rope_thread) {
+      const int kr = min(k0 + (i >> 3), L - 1);
+      rr = *reinterpret_cast<const bf16x8*>(cache_row(cache, bt, kr) + kDc + 8 * (i & 7));
     }
-    const int key = min(k0 + (threadIdx.x >> 3), L - 1);
-    rr = *reinterpret_cast<const bf16x8*>(cache_row(cache, bt, key) + kDc + 8 * (threadIdx.x & 7));
   };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = threadIdx.x + u * 64 * kAttnWaves;
-      *reinterpret_cast<bf16x8*>(ks_lds + (i >> 4) * kKRowB + 16 * (i & 15)) = rk[u];
-      *reinterpret_cast<bf16x8*>(v_lds + (i >> 4) * kVRowB + 16 * (i & 15)) = rv[u];
-    }
-    *reinterpret_cast<bf16x8*>(ks_lds + (threadIdx.x >> 3) * kKRowB + 2 * kDh + 16 * (threadIdx.x & 7)) = rr;
+  auto store_tile = [&](int buf) {
+    const int i = threadIdx.x;
+    *reinterpret_cast<bf16x8*>(ks_buf[buf] + (i >> 4) * kKRowB + 16 * (i & 15)) = rk;
+    *reinterpret_cast<bf16x8*>(v_buf[buf] + (i >> 4) * kVRowB + 16 * (i & 15)) = rv;
+    if (rope_thread)
+      *reinterpret_cast<bf16x8*>(ks_buf[buf] + (i >> 3) * kKRowB + 2 * kDh + 16 * (i & 7)) = rr;
   };
   load_tile(0);
-  for (int k0 = 0; k0 <= p_wg; k0 += kKeyTile) {
-    __syncthreads();  // the previous tile is no longer read
-    store_tile();
+  for (int k0 = 0, it = 0; k0 <= p_wg; k0 += kKeyTile, ++it) {
+    store_tile(it & 1);
     if (k0 + kKeyTile <= p_wg) load_tile(k0 + kKeyTile);
     __syncthreads();
     if (k0 > p_wave) continue;  // every key of the tile lies after this wave's queries
+    const char* ks_lds = ks_buf[it & 1];
+    const char* v_lds = v_buf[it & 1];
 
     // S^T for keys k0 + 16kb + row, queries of block qb: lane holds keys
     // 16kb + 4g + i.  Each row fragment read from LDS feeds one MFMA per
@@ -371,9 +384,10 @@ hipError_t prefill_naive(const mla_dims& d, int batch, int q_len, const void* q_
   PrefillTheta theta;
   for (int k = 0; k < kDr / 2; ++k) theta.t[k] = pow(d.rope_base, -2.0 * k / kDr);
   const int wg_tokens = kAttnWaves * kQWave;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3((q_len + wg_tokens - 1) / wg_tokens, d.n_heads, batch),
-                     dim3(64 * kAttnWaves), 0,
-                     stream, d.n_heads, q_len, max_rows, d.softmax_scale, theta,
+  const int64_t blocks = static_cast<int64_t>((q_len + wg_tokens - 1) / wg_tokens) * d.n_heads * batch;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(64 * kAttnWaves), 0,
+                     stream, d.n_heads, batch, q_len, max_rows, d.softmax_scale, theta,
                      static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_pe),
                      static_cast<const uint16_t*>(kv_cache), block_table, max_pages, seq_lens, kc, vc, out,
                      lse);

@@ -57,7 +57,7 @@ def test_prefill_against_oracle(gpu_lib, name, cfg, lens, T, heads):
     assert_lse(lse[:, :, h], ref["lse"])
 
 
-# The sizes the bench times: a workgroup takes 128 query tokens (four waves of
+# The sizes the bench times: a workgroup takes 256 query tokens (eight waves of
 # 32), so these fill every wave, several workgroups and a ragged last one.
 # The oracle forms each head's keys and values once (causal_prefill_workload).
 LARGE = [
@@ -68,6 +68,7 @@ LARGE = [
     ("h128_T256", small(V2, "pfL3", 1, permute_pages=True), [8192], 256, [10, 100]),
     ("h16_T512", small(LITE, "pfL4", 1, permute_pages=True), [4096], 512, None),
     ("h128_T2048", small(V2, "pfL5", 1, permute_pages=True), [8192], 2048, [0, 127]),
+    ("h128_T300_two_workgroups", small(V2, "pfL6", 2, permute_pages=True), [300, 5000], 300, [1, 90]),
 ]
 
 
