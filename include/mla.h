@@ -12,8 +12,6 @@
  *   mla_decode_splitkv  per work item: scores against [c^KV | k^R], online
  *                       softmax, latent-space weighted sum, partial LSE
  *   mla_decode_splitkv_ordered  the same, items started in a given order
- *   mla_decode_splitkv_balanced the same, the two items of a sequence splitting
- *                       their joint range at run time
  *   mla_combine         log-sum-exp merge of the work items of a sequence
  *   mla_decode_merged   the two above in one launch
  *   mla_decode_splitkv_multi, mla_combine_multi
@@ -210,37 +208,6 @@ mla_status mla_decode_splitkv_ordered(const mla_dims* dims, int32_t batch, const
                                       const int32_t* seq_lens, const int32_t* items,
                                       int32_t num_items, const int32_t* order, float* o_part,
                                       float* lse_part, void* stream);
-
-/* mla_decode_splitkv in which items 2j and 2j+1 of each sequence (in split
- * order, i.e. split_offsets[b] + 2j and + 2j + 1) divide their joint token
- * range between them at run time: the first takes 32-token slices from the
- * front, the second from the back, each starting with 12 slices and claiming
- * the rest 4 at a time from a counter the two share, so the pair ends
- * together however fast each workgroup runs.  A sequence's last item when it
- * has an odd number of them, and pairs whose joint range is shorter than 28
- * slices, keep their planned ranges.  Same split-KV arithmetic (page
- * "DeepSeek-V2/V3：大模型的两张账" section "第一张账"; page "DeepSeek V2 技术解析"
- * 2.1.1); item w's partial then covers the tokens it actually took, so the
- * merged result equals mla_decode_splitkv's up to float32 rounding but is not
- * bit-reproducible from run to run (the split point depends on timing).
- * Arguments as for mla_decode_splitkv_ordered, with order optional (null:
- * slot s takes item s), plus:
- *   split_offsets [batch + 1] int32 (device): the items' CSR offsets from the
- *               planner (items of sequence b at split_offsets[b] .. [b+1]-1,
- *               consecutive and in token order);
- *   counters    [4 * num_items] int32 (device): zero on entry; the call leaves
- *               them zero.  Calls that overlap on one counters buffer race.
- * Only the 128-head gfx950 fast path balances; on other shapes this is
- * mla_decode_splitkv_ordered (counters untouched).
- * Errors: as for mla_decode_splitkv, plus MLA_ERR_INVALID_ARG for null or
- * misaligned split_offsets or counters. */
-mla_status mla_decode_splitkv_balanced(const mla_dims* dims, int32_t batch, const void* q_abs,
-                                       const void* kv_cache, int32_t num_pages,
-                                       const int32_t* block_table, int32_t max_pages_per_seq,
-                                       const int32_t* seq_lens, const int32_t* items,
-                                       int32_t num_items, const int32_t* order,
-                                       const int32_t* split_offsets, int32_t* counters,
-                                       float* o_part, float* lse_part, void* stream);
 
 /* Split-KV decode with q_len query tokens per sequence (speculative or chunked
  * decode: the newest q_len tokens of each sequence, already in the cache, are

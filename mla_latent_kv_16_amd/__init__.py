@@ -31,7 +31,7 @@ import numpy as np
 __all__ = ["MlaError", "Dims", "load", "lib_path", "absorb_q", "plan_splits", "decode_splitkv",
            "decode_merged", "append_kv", "append_kv_noalloc", "decode_splitkv_multi", "combine_multi", "combine_out_proj",
            "prefill_naive",
-           "combine", "out_proj", "decode_step", "decode_splitkv_balanced", "fast_path", "version", "record_calls", "replay_calls",
+           "combine", "out_proj", "decode_step", "fast_path", "version", "record_calls", "replay_calls",
            "check_paging", "exact_pass_count", "BF16", "F32"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -107,8 +107,6 @@ def load():
         "mla_decode_splitkv_ordered": (i32, [pd, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp,
                                               vp]),
         "mla_decode_splitkv": (i32, [pd, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp]),
-        "mla_decode_splitkv_balanced": (i32, [pd, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp, vp,
-                                               vp, vp, vp]),
         "mla_combine": (i32, [pd, i32, vp, vp, vp, vp, vp, vp]),
         "mla_decode_splitkv_multi": (i32, [pd, i32, i32, vp, vp, i32, vp, i32, vp, vp, i32, vp, vp,
                                             vp]),
@@ -337,35 +335,6 @@ def decode_splitkv(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items,
         _launch("mla_decode_splitkv", *head, *tail)
     else:
         _launch("mla_decode_splitkv_ordered", *head, _ptr(order, torch.int32, (W,), "order"), *tail)
-    return o_part, lse_part
-
-
-def decode_splitkv_balanced(dims: Dims, q_abs, kv_cache, block_table, seq_lens, items, split_offsets,
-                            counters, o_part=None, lse_part=None, stream=None, order=None):
-    """mla_decode_splitkv_balanced: items 2j and 2j+1 of a sequence split their
-    joint range at run time.  split_offsets: device int32 [B + 1] from the
-    planner; counters: device int32 [4 W], zero on entry (left zero)."""
-    torch = _torch()
-    dt = _store_dtype(dims)
-    B, H = q_abs.shape[0], dims.n_heads
-    W = items.shape[0]
-    dev = q_abs.device
-    if o_part is None:
-        o_part = torch.empty((W, H, dims.d_latent), dtype=torch.float32, device=dev)
-    if lse_part is None:
-        lse_part = torch.empty((W, H), dtype=torch.float32, device=dev)
-    num_pages = kv_cache.shape[0]
-    _debug_paging(dims, block_table, seq_lens, num_pages, 1, stream, "mla_decode_splitkv_balanced")
-    _launch("mla_decode_splitkv_balanced",
-        ctypes.byref(dims.c()), B, _ptr(q_abs, dt, (B, H, dims.row), "q_abs"),
-        _ptr(kv_cache, dt, (num_pages, dims.page_size, dims.row), "kv_cache"), num_pages,
-        _ptr(block_table, torch.int32, None, "block_table"), block_table.shape[1],
-        _ptr(seq_lens, torch.int32, (B,), "seq_lens"), _ptr(items, torch.int32, (W, 4), "items"), W,
-        _ptr(order, torch.int32, (W,), "order"),
-        _ptr(split_offsets, torch.int32, (B + 1,), "split_offsets"),
-        _ptr(counters, torch.int32, (4 * W,), "counters"),
-        _ptr(o_part, torch.float32, (W, H, dims.d_latent), "o_part"),
-        _ptr(lse_part, torch.float32, (W, H), "lse_part"), _stream(stream))
     return o_part, lse_part
 
 
@@ -600,26 +569,19 @@ def prefill_naive(dims: Dims, q_nope, q_pe, w_uk, w_uv, kv_cache, block_table, s
 
 
 def decode_step(dims: Dims, q_nope, q_pe, positions, w_uk, w_uv, kv_cache, block_table, seq_lens,
-                items, split_offsets, bufs: Optional[dict] = None, stream=None, order=None,
-                counters=None) -> dict:
+                items, split_offsets, bufs: Optional[dict] = None, stream=None, order=None) -> dict:
     """absorb_q -> decode_splitkv -> combine -> out_proj on one stream.
 
     `items`/`split_offsets` (and `order`, for plan_splits(..., ordered=True))
-    are device copies of plan_splits' output.  With `counters` (device int32
-    [4 W], zero) the decode is decode_splitkv_balanced.  `bufs` may hold
-    preallocated q_abs, o_part, lse_part, o_latent, lse, out tensors.
+    are device copies of plan_splits' output.  `bufs` may hold preallocated
+    q_abs, o_part, lse_part, o_latent, lse, out tensors.
     """
     b = {} if bufs is None else bufs
     B = q_nope.shape[0]
     b["q_abs"] = absorb_q(dims, q_nope, q_pe, positions, w_uk, b.get("q_abs"), stream)
-    if counters is None:
-        b["o_part"], b["lse_part"] = decode_splitkv(dims, b["q_abs"], kv_cache, block_table, seq_lens,
-                                                    items, b.get("o_part"), b.get("lse_part"), stream,
-                                                    order=order)
-    else:
-        b["o_part"], b["lse_part"] = decode_splitkv_balanced(
-            dims, b["q_abs"], kv_cache, block_table, seq_lens, items, split_offsets, counters,
-            b.get("o_part"), b.get("lse_part"), stream, order=order)
+    b["o_part"], b["lse_part"] = decode_splitkv(dims, b["q_abs"], kv_cache, block_table, seq_lens,
+                                                items, b.get("o_part"), b.get("lse_part"), stream,
+                                                order=order)
     b["o_latent"], b["lse"] = combine(dims, split_offsets, b["o_part"], b["lse_part"], B,
                                       b.get("o_latent"), b.get("lse"), stream)
     b["out"] = out_proj(dims, b["o_latent"], w_uv, b.get("out"), stream)

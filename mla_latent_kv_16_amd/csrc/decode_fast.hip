@@ -89,17 +89,6 @@ constexpr float kMoveDefault = 8.0f;       // log2 units: the reference moves pa
 #endif
 constexpr int kMoveWindow = MLA_MOVE_WINDOW;
 constexpr float kSafeJumpDefault = 64.0f;  // log2 units: an item is redone past this
-// Balanced launch (paired items): each workgroup of a pair starts with
-// kBalStatic slices at its own end of the joint range and claims the rest
-// kBalClaim slices at a time, one claim in flight, taking each claim's result
-// kBalClaim iterations after making it.  The slice count goes through LDS two
-// iterations ahead of its use (every wave reads it one iteration early, off
-// the path from the barrier to the next loads), with kBalFinal set once no
-// further claim will succeed; kBalStatic covers that lead and the DMA and
-// prefetch distance.
-constexpr int kBalStatic = 12;
-constexpr int kBalClaim = 4;
-constexpr int kBalFinal = 1 << 30;
 
 // Pipelining depths (steps of LDS reads issued ahead of their MFMAs).
 #ifndef MLA_QK_AHEAD
@@ -151,22 +140,17 @@ constexpr int kHeadBlocksWG = kHeadsWG / 16;        // 4
 constexpr int kPBytesWG = kHeadBlocksWG * 64 * 16;  // 4 KiB of weights per slice
 constexpr int kSWaves = 8;
 static_assert(kStages * kSlotBytes + 2 * kPBytesWG + 256 + kSWaves * 4 + 4 * kHeadsWG * 4 +
-                      2 * kHeadsWG * 4 + 2 * 4 * 4 + 2 * kHeadsWG * 4 + 4 + 4 * 4 <=
+                      2 * kHeadsWG * 4 + 2 * 4 * 4 + 2 * kHeadsWG * 4 + 4 <=
                   163840,
               "LDS budget");
 
-// kBal: the balanced launch (one query token per sequence; counters: two int32
-// per pair and head half at 4 * (first item of the pair) + 2 * half, zero on
-// entry and left zero).
-template <bool kBal>
 __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ items, int num_items, const int32_t* __restrict__ order, int q_len,
     float scale, float move_t, float safe_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
-    int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out,
-    int32_t* __restrict__ counters) {
+    int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
   constexpr int H = 128;
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes + 2 * kPBytesWG];
   __shared__ __attribute__((aligned(16))) char junk[256];
@@ -176,7 +160,6 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
   __shared__ float rsc[2][kHeadsWG];      // per window parity: a head's rescale factor
   __shared__ __attribute__((aligned(16))) int moved[2][kHeadBlocksWG];  // per window parity: slice of the last move
   __shared__ float lsum2[2][kHeadsWG];    // per token half: a head's row sum
-  __shared__ int kpub[4];                 // balanced launch: slice count (| kBalFinal) by iteration % 4
   char* const pbuf = lds + kStages * kSlotBytes;
   const uint32_t lds_base =
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
@@ -220,43 +203,6 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
   const int nsplit = merged ? split_offsets[b + 1] - s0 : 0;
   const bool direct = merged && nsplit == 1;
   const bool merge_tail = merged && nsplit > 1;
-
-  // Balanced launch: items 2j and 2j+1 of a sequence (split order) share their
-  // joint token range [bal_lo, bal_hi), the even one taking its slices from
-  // the front and the odd one from the back, so the two end together however
-  // fast each runs.  Each starts with kBalStatic slices and claims the rest
-  // from the pair's counter.  Unpaired items and joint ranges too short for
-  // that keep their own range.
-  int role = 0;  // 0: own range, 1: front, 2: back
-  int pair_n = 0, bal_lo = 0, bal_hi = 0;
-  int32_t* ctr = nullptr;
-  if constexpr (kBal) {
-    const int s_first = split_offsets[b], s_end = split_offsets[b + 1];
-    const int j = it - s_first;
-    const int mate = (j & 1) ? it - 1 : it + 1;
-    if (mate >= s_first && mate < s_end) {
-      const int a = min(it, mate), z = max(it, mate);
-      const int lo = items[4 * a + 2] * kPage;
-      const int hi = min(items[4 * z + 3] * kPage, L);
-      const int n = (hi - lo + kSliceTok - 1) / kSliceTok;
-      if (n >= 2 * kBalStatic + kBalClaim) {
-        role = (j & 1) ? 2 : 1;
-        pair_n = n;
-        bal_lo = lo;
-        bal_hi = hi;
-        ctr = counters + 4 * a + 2 * hh;
-      }
-    }
-  }
-  const int tend = role ? bal_hi : t_end;
-  auto tok0_of = [&](int k) -> int {  // first token of the workgroup's k-th slice
-    if (role == 1) return bal_lo + k * kSliceTok;
-    if (role == 2) return bal_lo + (pair_n - 1 - k) * kSliceTok;
-    return t_begin + k * kSliceTok;
-  };
-  const int k_start = role ? kBalStatic : n_slices;  // slices the workgroup holds at the start
-  if (kBal && threadIdx.x < 4) kpub[threadIdx.x] = k_start | (role ? 0 : kBalFinal);
-  int k_total = n_slices;  // balanced launch: set when the first pass ends
 
   auto slot_of = [&](int n) -> const char* { return lds + (n % kStages) * kSlotBytes; };
   auto pbuf_of = [&](int n) -> char* { return pbuf + (n & 1) * kPBytesWG; };
@@ -313,7 +259,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       }
     };
     auto lane_max = [&](const float (&s)[4]) { return fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])); };
-    auto nvalid = [&](int n) { return min(kSliceTok, tend - tok0_of(n)); };
+    auto nvalid = [&](int n) { return min(kSliceTok, t_end - (t_begin + n * kSliceTok)); };
     // weights 2^(s - m_ref) of slice k (masked tokens: 2^-inf = 0) into its buffer
     auto publish = [&](int k, const float (&s)[4]) {
       float p[4];
@@ -350,28 +296,6 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       }
     };
 
-    // Balanced launch, S wave 0 in iteration k: every kBalClaim iterations it
-    // takes the result of the claim it made kBalClaim iterations earlier and
-    // makes the next; every iteration it publishes the slice count for
-    // iteration k + 2.  A claim asks for kBalClaim slices of the budget the
-    // pair shares (the joint range less both starting shares); a short grant
-    // is the last.
-    int k_cur = k_start;
-    bool k_fin = role == 0;
-    int claim = 0;  // lane 0: the counter value the pending claim returned
-    auto bal_tick = [&](int k, bool first) {
-      if (first && !k_fin && k % kBalClaim == 0) {
-        if (k > 0) {
-          const int budget = pair_n - 2 * kBalStatic;
-          const int got = min(kBalClaim, max(0, budget - __builtin_amdgcn_readfirstlane(claim)));
-          k_cur += got;
-          k_fin = got < kBalClaim;
-        }
-        if (!k_fin && lane == 0) claim = atomicAdd(ctr, kBalClaim);
-      }
-      if (lane == 0) kpub[(k + 2) & 3] = k_cur | (k_fin ? kBalFinal : 0);
-    };
-
     // Full pass.  With `first`, m_ref starts at the per-head maximum of the
     // first slice (both token halves, exchanged through LDS) and moves up
     // during the pass (move_ref); a weight can thus exceed 1 by the jump of
@@ -383,9 +307,6 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       float m_win = -INFINITY;   // this lane's maximum over the current window
       float s[4];
       __syncthreads();
-      if constexpr (kBal) {
-        if (w == 0) bal_tick(0, first);
-      }
       scores(slot_of(0), nvalid(0), s);
       if (first) {
         const float m = rows_max(lane_max(s));
@@ -394,8 +315,9 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       __syncthreads();
       if (first) m_ref = fmaxf(mx_half[0][0][hidx], mx_half[0][1][hidx]);
       publish(0, s);
-      // slice k (k >= 1) holds nv valid tokens (after the iteration's barrier)
-      auto step_body = [&](int k, int nv) {
+      // slice k (k >= 1) holds nv valid tokens
+      auto step = [&](int k, int nv) {
+        __syncthreads();
         const bool check = first && k % kMoveWindow == 0;
         float mp0 = -INFINITY, mp1 = -INFINITY;
         if (check) {  // the previous window's maxima, read before the MFMAs
@@ -417,36 +339,12 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
         }
         publish(k, s);
       };
-      if constexpr (kBal) {
-        // the count for iteration k, read in iteration k - 1, says whether
-        // slice k is the workgroup's; the barrier of the iteration that ends
-        // the loop is the one after it
-        int kn = k_start;  // the count for iteration 1
-        for (int k = 1;; ++k) {
-          __syncthreads();
-          const int kn_next = kpub[(k + 1) & 3] & (kBalFinal - 1);
-          if (k >= kn) {
-            k_total = kn;
-            break;
-          }
-          if (w == 0) bal_tick(k, first);
-          step_body(k, nvalid(k));
-          kn = kn_next;
-        }
-      } else {
-        // slices 1 .. n-2 are whole (the constant count lets the compiler drop
-        // the mask); only the first and the last can be short
-        for (int k = 1; k < n_slices - 1; ++k) {
-          __syncthreads();
-          step_body(k, kSliceTok);
-        }
-        if (n_slices > 1) {
-          __syncthreads();
-          step_body(n_slices - 1, nvalid(n_slices - 1));
-        }
-        __syncthreads();
-      }
+      // slices 1 .. n-2 are whole (the constant count lets the compiler drop
+      // the mask); only the first and the last can be short
+      for (int k = 1; k < n_slices - 1; ++k) step(k, kSliceTok);
+      if (n_slices > 1) step(n_slices - 1, nvalid(n_slices - 1));
       e_lane = fmaxf(e_lane, m_win - m_ref);  // a last, partial window
+      __syncthreads();
       // vote: did a weight of any S wave pass 2^safe_jump?
       const bool mine = __any(first && e_lane > safe_jump);
       if (lane == 0) votes[w] = mine ? 1 : 0;
@@ -464,7 +362,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       // (every weight <= 1, no moves).
       if (threadIdx.x == 0) atomicAdd(&g_exact_passes, 1ull);
       float m_lane = -INFINITY;
-      for (int k = 0; k < k_total; ++k) {
+      for (int k = 0; k < n_slices; ++k) {
         __syncthreads();
         float s[4];
         scores(slot_of(k), nvalid(k), s);
@@ -488,14 +386,6 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
         if (lse_out) lse_out[static_cast<int64_t>(b) * H + head0 + hidx] = lse_v;
       } else {
         lse_part[prow0 + head0 + hidx] = lse_v;
-      }
-    }
-    if constexpr (kBal) {
-      // the second workgroup of the pair to get here resets its counters (both
-      // have made their last claim by now)
-      if (role && w == 0 && lane == 0 && atomicAdd(ctr + 1, 1) == 1) {
-        atomicExch(ctr, 0);
-        atomicExch(ctr + 1, 0);
       }
     }
     if (merge_tail) {  // same barriers as the V waves' merge tail
@@ -524,14 +414,14 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     const uint32_t dma_lane =
         static_cast<uint32_t>(drow * kRowBytes + ((lane & 7) ^ swz(lane >> 3)) * 16);
     auto issue = [&](int n) {
-      const int tok0 = tok0_of(n);
+      const int tok0 = t_begin + n * kSliceTok;
       const int page = bt[tok0 >> 6];
       const char* src = cache + static_cast<int64_t>(page) * (kPage * kRowBytes) +
                         (tok0 & (kPage - 1)) * kRowBytes;
       const uint32_t dst = lds_base + (n % kStages) * kSlotBytes + kLoadsPerWave * u * 1024;
       // tail slice: rows of tokens >= nv are filled from token 0 of the slice
       // (finite data, weight 0), so empty cache slots are never read.
-      const int nv = tend - tok0;
+      const int nv = t_end - tok0;
       const uint32_t voff = drow < nv ? dma_lane : dma_lane - drow * kRowBytes;
 #pragma unroll
       for (int j = 0; j < kLoadsPerWave; ++j) dma16(src + 128 * j, voff, dst + 1024 * j);
@@ -541,25 +431,19 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     // the L2), one 4-byte load per line from the V waves without DMA
     const uint32_t junk_lds = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)junk));
-    auto prefetch = [&](int n, int n_have) {  // n_have: slices known to be the workgroup's
-      if (MLA_PREFETCH_D <= 0 || dma || n >= n_have) return;
-      const int tok0 = tok0_of(n);
+    auto prefetch = [&](int n) {
+      if (MLA_PREFETCH_D <= 0 || dma || n >= n_slices) return;
+      const int tok0 = t_begin + n * kSliceTok;
       const int page = bt[tok0 >> 6];
       const char* src = cache + static_cast<int64_t>(page) * (kPage * kRowBytes) +
                         (tok0 & (kPage - 1)) * kRowBytes;
-      const int nv = tend - tok0;
+      const int nv = t_end - tok0;
       const int li = 2 * ((u - kDmaWaves) * 64 + lane) + hh;  // line of the slice
       if (li < 288 && li / 9 < nv) touch4(src, static_cast<uint32_t>(li * 128), junk_lds);
     };
-    // wait for this wave's part of slice k (slice k+1 stays in flight if it
-    // was issued; n_iss slices have been issued)
-    int n_iss = 0;
-    auto issue_n = [&](int n) {
-      issue(n);
-      n_iss = n + 1;
-    };
+    // wait for this wave's part of slice k (slice k+1 may stay in flight)
     auto wait_slice = [&](int k) {
-      if (k + 1 < n_iss)
+      if (k + 1 < n_slices)
         __builtin_amdgcn_s_waitcnt(MLA_VMCNT(kLoadsPerWave));
       else
         __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
@@ -632,40 +516,21 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       }
     };
     auto full_pass = [&](bool first) -> bool {
-      const int n0 = kBal ? k_start : n_slices;
       if (dma) {
-        issue_n(0);
-        if (n0 > 1) issue_n(1);
+        issue(0);
+        if (n_slices > 1) issue(1);
         wait_slice(0);
       }
       __syncthreads();
-      if (dma && 2 < n0) issue_n(2);
+      if (dma && 2 < n_slices) issue(2);
       __syncthreads();  // the S waves' first-slice maximum exchange
-      for (int n = 2; n <= MLA_PREFETCH_D; ++n) prefetch(n, n0);
-      if constexpr (kBal) {
-        // the same counts as the S waves, read after the same barriers
-        int kn = k_start;
-        for (int k = 1;; ++k) {
-          if (dma) wait_slice(k);
-          __syncthreads();
-          const int kn_next = kpub[(k + 1) & 3] & (kBalFinal - 1);
-          if (dma && k + 2 < kn) issue_n(k + 2);
-          prefetch(k + MLA_PREFETCH_D, kn);
-          accumulate(k - 1, first);
-          if (k >= kn) {
-            k_total = kn;
-            break;
-          }
-          kn = kn_next;
-        }
-      } else {
-        for (int k = 1; k <= n_slices; ++k) {
-          if (dma && k < n_slices) wait_slice(k);
-          __syncthreads();
-          if (dma && k + 2 < n_slices) issue_n(k + 2);
-          prefetch(k + MLA_PREFETCH_D, n_slices);
-          accumulate(k - 1, first);
-        }
+      for (int n = 2; n <= MLA_PREFETCH_D; ++n) prefetch(n);
+      for (int k = 1; k <= n_slices; ++k) {
+        if (dma && k < n_slices) wait_slice(k);
+        __syncthreads();
+        if (dma && k + 2 < n_slices) issue(k + 2);
+        prefetch(k + MLA_PREFETCH_D);
+        accumulate(k - 1, first);
       }
       // vote (written by the S waves)
       __syncthreads();
@@ -680,13 +545,13 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     if (!full_pass(true)) {
       // exact-maximum pass of the S waves: stream the slices again
       if (dma) {
-        issue_n(0);
-        if (k_total > 1) issue_n(1);
+        issue(0);
+        if (n_slices > 1) issue(1);
       }
-      for (int k = 0; k < k_total; ++k) {
+      for (int k = 0; k < n_slices; ++k) {
         if (dma) wait_slice(k);
         __syncthreads();
-        if (dma && k + 2 < k_total) issue_n(k + 2);
+        if (dma && k + 2 < n_slices) issue(k + 2);
       }
       __syncthreads();
       __syncthreads();  // the S waves' maximum exchange
@@ -1095,24 +960,15 @@ hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const vo
                        const int32_t* items, int num_items, const int32_t* order, float* o_part,
                        float* lse_part,
                        const int32_t* split_offsets, int32_t* tickets, float* o_latent,
-                       float* lse_out, int32_t* counters, hipStream_t stream) {
+                       float* lse_out, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(num_items) * q_len * (d.n_heads == 128 ? 2 : 1);
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   if (d.n_heads == 128) {
-    if (counters) {  // balanced launch: one query token, split offsets, no merge
-      if (q_len != 1 || !split_offsets || tickets) return hipErrorInvalidValue;
-      hipLaunchKernelGGL(decode_h128_kernel<true>, dim3(static_cast<uint32_t>(blocks)), dim3(1024), 0, stream,
-                         static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
-                         block_table, max_pages, seq_lens, items, num_items, order, q_len, d.softmax_scale,
-                         move_threshold(), safe_jump(), o_part, lse_part, split_offsets, tickets, o_latent,
-                         lse_out, counters);
-      return hipGetLastError();
-    }
-    hipLaunchKernelGGL(decode_h128_kernel<false>, dim3(static_cast<uint32_t>(blocks)), dim3(1024), 0, stream,
+    hipLaunchKernelGGL(decode_h128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(1024), 0, stream,
                        static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
                        block_table, max_pages, seq_lens, items, num_items, order, q_len, d.softmax_scale,
                        move_threshold(), safe_jump(), o_part, lse_part, split_offsets, tickets, o_latent,
-                       lse_out, nullptr);
+                       lse_out);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(decode_h16_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,

@@ -141,7 +141,7 @@ mla_status decode_splitkv_impl(const mla_dims* dims, int32_t batch, int32_t q_le
   if (is_fast_shape(*dims))
     return launched(decode_fast(*dims, q_len, q_abs, kv_cache, block_table, max_pages_per_seq,
                                 seq_lens, items, num_items, order, o_part, lse_part, nullptr,
-                                nullptr, nullptr, nullptr, nullptr, st));
+                                nullptr, nullptr, nullptr, st));
   return launched(decode_generic(*dims, q_len, q_abs, kv_cache, block_table, max_pages_per_seq,
                                  seq_lens, items, num_items, o_part, lse_part, st));
 }
@@ -191,36 +191,6 @@ mla_status mla_decode_splitkv_ordered(const mla_dims* dims, int32_t batch, const
                              stream);
 }
 
-mla_status mla_decode_splitkv_balanced(const mla_dims* dims, int32_t batch, const void* q_abs,
-                                       const void* kv_cache, int32_t num_pages,
-                                       const int32_t* block_table, int32_t max_pages_per_seq,
-                                       const int32_t* seq_lens, const int32_t* items,
-                                       int32_t num_items, const int32_t* order,
-                                       const int32_t* split_offsets, int32_t* counters,
-                                       float* o_part, float* lse_part, void* stream) {
-  mla_status s = check_dims(dims);
-  if (s != MLA_OK) return s;
-  if (!split_offsets || !counters || !al4(split_offsets) || !al4(counters)) return MLA_ERR_INVALID_ARG;
-  if (!is_fast_shape(*dims) || dims->n_heads != 128)  // the fixed split on other shapes
-    return decode_splitkv_impl(dims, batch, 1, q_abs, kv_cache, num_pages, block_table,
-                               max_pages_per_seq, seq_lens, items, num_items, order, o_part,
-                               lse_part, stream);
-  if (batch < 1 || num_pages < 1 || max_pages_per_seq < 1 || num_items < 1) return MLA_ERR_INVALID_ARG;
-  if (!q_abs || !kv_cache || !block_table || !seq_lens || !items || !o_part || !lse_part)
-    return MLA_ERR_INVALID_ARG;
-  if (!al16(q_abs) || !al16(kv_cache) || !al16(o_part) || !al4(lse_part) || !al4(block_table) ||
-      !al4(seq_lens) || !al4(items) || (order && !al4(order)))
-    return MLA_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(num_items) * 4 > INT32_MAX ||
-      static_cast<int64_t>(batch) * dims->n_heads > (int64_t{1} << 31))
-    return MLA_ERR_UNSUPPORTED;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
-  return launched(decode_fast(*dims, 1, q_abs, kv_cache, block_table, max_pages_per_seq, seq_lens,
-                              items, num_items, order, o_part, lse_part, split_offsets, nullptr,
-                              nullptr, nullptr, counters, st));
-}
-
 mla_status mla_decode_splitkv_multi(const mla_dims* dims, int32_t batch, int32_t q_len,
                                     const void* q_abs, const void* kv_cache, int32_t num_pages,
                                     const int32_t* block_table, int32_t max_pages_per_seq,
@@ -257,7 +227,7 @@ mla_status mla_decode_merged(const mla_dims* dims, int32_t batch, const void* q_
   if (is_fast_shape(*dims))
     return launched(decode_fast(*dims, 1, q_abs, kv_cache, block_table, max_pages_per_seq,
                                 seq_lens, items, num_items, nullptr, o_part, lse_part, split_offsets,
-                                tickets, o_latent, lse, nullptr, st));
+                                tickets, o_latent, lse, st));
   mla_status r = launched(decode_generic(*dims, 1, q_abs, kv_cache, block_table, max_pages_per_seq,
                                          seq_lens, items, num_items, o_part, lse_part, st));
   if (r != MLA_OK) return r;

@@ -48,15 +48,12 @@ hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const v
 // device since the last reset (synchronous copies of a device counter).
 hipError_t exact_pass_count(uint64_t* count, bool reset);
 // order: null, or the item each dispatch slot takes (a permutation of the items).
-// counters: null, or (128 heads, q_len 1, split_offsets set, no tickets) the
-// balanced launch's pair counters, int32 [4 * num_items], zero on entry and on
-// return.
 hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const void* kv_cache,
                        const int32_t* block_table, int max_pages, const int32_t* seq_lens,
                        const int32_t* items, int num_items, const int32_t* order, float* o_part,
                        float* lse_part,
                        const int32_t* split_offsets, int32_t* tickets, float* o_latent,
-                       float* lse_out, int32_t* counters, hipStream_t stream);
+                       float* lse_out, hipStream_t stream);
 hipError_t combine_fast(const mla_dims& d, int batch, int q_len, const int32_t* split_offsets,
                         const float* o_part, const float* lse_part, float* o_latent, float* lse,
                         hipStream_t stream);

@@ -47,11 +47,9 @@ def num_slots() -> int:
     return int(torch.cuda.get_device_properties(0).multi_processor_count)
 
 
-def run(wl, dev=None, slots=None, items=None, offs=None, ordered=False, balanced=False) -> dict:
+def run(wl, dev=None, slots=None, items=None, offs=None, ordered=False) -> dict:
     """Run the four device steps; return numpy copies of every output.
-    `ordered`: the longest-first plan and dispatch (as the bench runs them);
-    `balanced`: the decode through mla_decode_splitkv_balanced (the counters it
-    leaves are returned under "counters")."""
+    `ordered`: the longest-first plan and dispatch (as the bench runs them)."""
     import torch
     dims = dims_of(wl.cfg)
     dev = upload(wl) if dev is None else dev
@@ -64,14 +62,11 @@ def run(wl, dev=None, slots=None, items=None, offs=None, ordered=False, balanced
     it_d = torch.from_numpy(items).cuda()
     of_d = torch.from_numpy(offs).cuda()
     or_d = None if order is None else torch.from_numpy(order).cuda()
-    ctr = torch.zeros(4 * len(items), dtype=torch.int32, device="cuda") if balanced else None
     b = mla.decode_step(dims, dev["q_nope"], dev["q_pe"], dev["positions"], dev["w_uk"],
                         dev["w_uv"], dev["cache"], dev["block_table"], dev["seq_lens"], it_d, of_d,
-                        order=or_d, counters=ctr)
+                        order=or_d)
     torch.cuda.synchronize()
     out = {}
-    if balanced:
-        out["counters"] = ctr.cpu().numpy()
     for k in ("q_abs", "o_latent", "lse", "out", "o_part", "lse_part"):
         t = b[k]
         out[k] = t.float().cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()

@@ -98,28 +98,6 @@ def test_decode_rejects_bad_arguments(lib):
     assert f(_d(), 2, *args) == INVALID
 
 
-def test_decode_balanced_rejects_bad_arguments(lib):
-    f = lib.mla_decode_splitkv_balanced
-    # q_abs kv_cache num_pages bt max_pages seq_lens items num_items order offs counters o_part lse_part stream
-    good = [A, A, 10, A, 4, A, A, 3, None, A, A, A, A, None]
-    assert f(_d(), 0, *good) == INVALID
-    for i in (0, 1, 3, 5, 6, 9, 10, 11, 12):       # each required pointer set to NULL
-        args = list(good)
-        args[i] = None
-        assert f(_d(), 2, *args) == INVALID, i
-    for i, bad in ((2, 0), (4, 0), (7, 0)):        # num_pages, max_pages, num_items < 1
-        args = list(good)
-        args[i] = bad
-        assert f(_d(), 2, *args) == INVALID, i
-    for i, bad in ((1, MIS), (8, A + 2), (9, A + 2), (10, A + 2), (11, A + 4)):
-        args = list(good)                          # misaligned cache, order, offsets, counters, o_part
-        args[i] = bad
-        assert f(_d(), 2, *args) == INVALID, i
-    args = list(good)
-    args[10] = None                                # counters required on every shape
-    assert f(_d(mla.Dims(16, 128, 512, 64)), 2, *args) == INVALID
-
-
 def test_decode_multi_rejects_bad_arguments(lib):
     f = lib.mla_decode_splitkv_multi
     # q_abs kv_cache num_pages bt max_pages seq_lens items num_items o_part lse_part stream
