@@ -14,19 +14,14 @@
 // read from HBM once per 64 sequences.  MFMA v_mfma_f32_16x16x32_bf16.
 #include <math.h>
 
+#include "decode_common.h"
 #include "device_common.h"
 #include "mla_internal.h"
 
 namespace mla {
 namespace {
 
-
-__device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_addr)
-               : "memory");
-}
-
-#define MLA_VMCNT0 ((7 << 4) | (15 << 8))
+static_assert(sizeof(RopeTheta::t) / sizeof(double) == kDr / 2, "one angle per RoPE pair");
 
 // XCD-aware workgroup numbering: workgroup i runs on XCD i % 8.  Give the
 // `per` consecutive blocks of one head the same XCD so they share its L2.
@@ -45,23 +40,6 @@ __device__ __forceinline__ void xcd_split(int i, int per, int& head, int& sub) {
 // adjacent chunks, 16 distinct 16-byte bank groups.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int tsw(int row) { return ((row & 3) << 1) | (((row >> 3) & 1) << 3); }
-
-// theta_k = rope_base^(-2k / d_h^R), k < 32, computed on the host in float64
-struct RopeTheta {
-  double t[kDr / 2];
-};
-
-// sin and cos of the float64 angle x: x reduced to [-pi, pi] in float64 (two-term
-// Cody-Waite with fused multiply-adds, error ~1e-15 for |x| < 2^20), then sin/cos
-// of the reduced angle in float32 (about 1 float32 ulp from the float64 result
-// rounded to float32)
-__device__ __forceinline__ void sincos_reduced(double x, float& sn, float& cs) {
-  constexpr double kTwoPiHi = 6.283185307179586, kTwoPiLo = 2.4492935982947064e-16;
-  const double n = rint(x * (1.0 / kTwoPiHi));
-  double r = fma(-n, kTwoPiHi, x);
-  r = fma(-n, kTwoPiLo, r);
-  sincosf(static_cast<float>(r), &sn, &cs);
-}
 
 __global__ __launch_bounds__(256) void absorb_kernel(
     int batch, int H, RopeTheta theta_k, const uint16_t* __restrict__ q_nope,
@@ -95,7 +73,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(
     for (int i = 0; i < 16; ++i) {
       const int p = (16 * w + i) * 64 + lane;
       const int row = p >> 4, pc = p & 15;
-      dma16(wh, row * (kDc * 2) + 16 * (pc ^ tsw(row)), lds_base + (16 * w + i) * 1024);
+      dec::dma16(wh, row * (kDc * 2) + 16 * (pc ^ tsw(row)), lds_base + (16 * w + i) * 1024);
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qn[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
@@ -137,7 +115,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(
     }
   }
 
-  __builtin_amdgcn_s_waitcnt(MLA_VMCNT0);
+  __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
   __syncthreads();
   if (16 * w >= nb) return;  // no sequence for this wave (no barrier follows)
 

@@ -46,4 +46,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// theta_k = rope_base^(-2k / d_h^R) for the 32 rotation pairs of the 64-wide
+// RoPE part, computed on the host in float64 and passed by value
+struct RopeTheta {
+  double t[32];
+};
+
+// sin and cos of a float64 angle x: x reduced to [-pi, pi] in float64 (two-term
+// Cody-Waite with fused multiply-adds, error ~1e-15 for |x| < 2^20), then sin/cos
+// of the reduced angle in float32 (about 1 float32 ulp from the float64 result
+// rounded to float32)
+__device__ __forceinline__ void sincos_reduced(double x, float& sn, float& cs) {
+  constexpr double kTwoPiHi = 6.283185307179586, kTwoPiLo = 2.4492935982947064e-16;
+  const double n = rint(x * (1.0 / kTwoPiHi));
+  double r = fma(-n, kTwoPiHi, x);
+  r = fma(-n, kTwoPiLo, r);
+  sincosf(static_cast<float>(r), &sn, &cs);
+}
+
 }  // namespace mla

@@ -40,26 +40,14 @@
 namespace mla {
 namespace {
 
+static_assert(sizeof(RopeTheta::t) / sizeof(double) == kDr / 2, "one angle per RoPE pair");
+
 constexpr float kRefSlack = 8.f;   // log2 units the softmax reference may trail the running maximum
 constexpr int kQB = 2;             // 16-query blocks per attention wave
 constexpr int kQWave = 16 * kQB;   // query tokens per attention wave
 constexpr int kKeyTile = 32;   // keys per attention iteration
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr float kLn2F = 0.6931471805599453f;
-
-struct PrefillTheta {
-  double t[kDr / 2];  // theta_k = rope_base^(-2k / d_h^R), from the host in float64
-};
-
-// sin and cos of a float64 angle: reduced to [-pi, pi] in float64 (two-term
-// Cody-Waite with fused multiply-adds), then sin/cos in float32
-__device__ __forceinline__ void sincos_reduced(double x, float& sn, float& cs) {
-  constexpr double kTwoPiHi = 6.283185307179586, kTwoPiLo = 2.4492935982947064e-16;
-  const double n = rint(x * (1.0 / kTwoPiHi));
-  double r = fma(-n, kTwoPiHi, x);
-  r = fma(-n, kTwoPiLo, r);
-  sincosf(static_cast<float>(r), &sn, &cs);
-}
 
 // Maximum / sum over the four lanes q, q+16, q+32, q+48 of a wave.
 __device__ __forceinline__ float rows4_max(float x) {
@@ -146,7 +134,7 @@ __device__ __forceinline__ uint64_t lds_tr4(const char* lds, uint32_t off) {
 }
 
 __global__ __launch_bounds__(64 * kAttnWaves, 1) void prefill_attn_kernel(
-    int H, int batch, int q_len, int max_rows, float scale, PrefillTheta theta,
+    int H, int batch, int q_len, int max_rows, float scale, RopeTheta theta,
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe,
     const uint16_t* __restrict__ cache, const int32_t* __restrict__ block_table, int max_pages,
     const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ kc,
@@ -381,7 +369,7 @@ hipError_t prefill_naive(const mla_dims& d, int batch, int q_len, const void* q_
                      static_cast<const uint16_t*>(w_uv), kc, vc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  PrefillTheta theta;
+  RopeTheta theta;
   for (int k = 0; k < kDr / 2; ++k) theta.t[k] = pow(d.rope_base, -2.0 * k / kDr);
   const int wg_tokens = kAttnWaves * kQWave;
   const int64_t blocks = static_cast<int64_t>((q_len + wg_tokens - 1) / wg_tokens) * d.n_heads * batch;
