@@ -28,8 +28,8 @@ def _latents(wl, b):
     return rows[:, :wl.cfg.d_latent]
 
 
-@pytest.mark.parametrize("base,heads,slots", [("v2_b64_l8192", 128, 256), ("v2_b64_l8192", 128, 4096),
-                                              ("v2lite_b32_l4096", 16, 256)])
+@pytest.mark.parametrize("base,heads,slots", [("v2_b64_l8192", 128, 8), ("v2_b64_l8192", 128, 4096),
+                                              ("v2lite_b32_l4096", 16, 8)])
 def test_zero_query_gives_the_mean(mla, base, heads, slots):
     cfg = small(CONFIGS[base], "zq", len(LENS), permute_pages=True)
     wl = generate(cfg, lens=np.array(LENS, np.int32))
@@ -66,3 +66,34 @@ def test_identical_rows_give_that_row(mla, base, heads):
         got = out["o_latent"][b].astype(np.float64)
         err = np.abs(got - c[None, :]).max() / np.abs(c).max()
         assert err <= 2e-6, f"sequence {b} (L {L}): o~ differs from the row by {err:.2e}"
+
+
+@pytest.mark.parametrize("base,heads,T", [("v2_b64_l8192", 128, 4), ("v2lite_b32_l4096", 16, 5)])
+def test_zero_query_multi_token_gives_prefix_means(mla, base, heads, T):
+    """q_len tokens with zero queries: token t sees rows 0 .. L - T + t, each
+    with weight 1, so its o~ is the mean of that prefix (causal mask exact)."""
+    import torch
+
+    from gpu_util import dims_of, to_dev, upload
+    lens = [T, 65, 777, 3000]
+    cfg = small(CONFIGS[base], "zqm", len(lens), permute_pages=True)
+    wl = generate(cfg, lens=np.array(lens, np.int32))
+    dims = dims_of(cfg)
+    B, H = cfg.batch, cfg.n_heads
+    dev = upload(wl)
+    q_abs = torch.zeros((B, T, H, dims.row), dtype=torch.bfloat16, device="cuda")
+    items, offs = mla.plan_splits(dims, wl.seq_lens, 4096)
+    o_part, lse_part = mla.decode_splitkv_multi(dims, q_abs, dev["cache"], dev["block_table"],
+                                                dev["seq_lens"], torch.from_numpy(items).cuda())
+    o_lat, lse = mla.combine_multi(dims, torch.from_numpy(offs).cuda(), o_part, lse_part, B)
+    torch.cuda.synchronize()
+    o_lat, lse = o_lat.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+    say(f"[zero query, q_len {T}, H={heads}] {len(items)} items")
+    for b, L in enumerate(lens):
+        c = _latents(wl, b)
+        for t in range(T):
+            n = L - T + t + 1
+            mean = c[:n].mean(axis=0)
+            err = np.abs(o_lat[b, t] - mean[None, :]).max() / np.abs(mean).max()
+            assert err <= 2e-6, f"sequence {b} token {t} (prefix {n}): {err:.2e}"
+            assert np.abs(lse[b, t] - np.log(n)).max() <= 2e-6 * max(1.0, np.log(n))
