@@ -310,7 +310,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path does not shard across GPUs in this build)", file=sys.stderr)
+              "(the decode path runs on one GPU; sharding is described, not built)", file=sys.stderr)
         sys.exit(2)
     T = args.q_len
     if T < 1 or (T > 1 and args.merged) or (args.merged and args.unfused):
