@@ -80,10 +80,12 @@
  *   starts at the work item's first-slice score maximum and moves up to a later
  *   slice's maximum when that passes it by more than 2^8 (the accumulators are
  *   rescaled then); MLA_DECODE_MAX_JUMP (log2 units, in (0, 30]) sets that
- *   threshold.  At 128 heads the two halves of a slice's tokens agree on a move
- *   one slice later, so a single slice can push weights past the reference; if
- *   one passes 2^64 the item is recomputed against exact maxima (read the count
- *   with mla_decode_exact_pass_count; MLA_DECODE_SAFE_JUMP, in (0, 100], lowers
+ *   threshold.  At 128 heads the two halves of a slice's tokens are scored by
+ *   different waves, which agree on moves once per window of 8 slices (256
+ *   tokens), from that window's maxima, so within a window the weights can
+ *   pass the reference by the window's rise; if one passes 2^64 the item is
+ *   recomputed against exact maxima (read the count with
+ *   mla_decode_exact_pass_count; MLA_DECODE_SAFE_JUMP, in (0, 100], lowers
  *   that bound).  The result is the same softmax either way.
  *
  * Supported shapes: the gfx950 fast path needs dtype MLA_BF16, d_latent 512,
@@ -410,10 +412,10 @@ mla_status mla_check_paging(const mla_dims* dims, int32_t batch, int32_t min_len
 
 /* Number of workgroups of the 128-head fast decode (each takes one half of a
  * work item's heads for one query token) that recomputed their item against
- * exact score maxima (a single 32-token slice pushed a weight past 2^64 of its
- * reference) on the current device since the count was last reset; with
- * reset != 0 the
- * count goes back to zero after it is read.  For monitoring and tests: the
+ * exact score maxima (the scores rose past the reference by more than 64
+ * log2 units within one window of 8 slices) on the current device since the
+ * count was last reset; with reset != 0 the count goes back to zero after it
+ * is read.  For monitoring and tests: the
  * call copies a device counter synchronously.  Pages as for mla_decode_splitkv
  * (the softmax of one head over the item's tokens).
  * Errors: MLA_ERR_INVALID_ARG for a null count_host; MLA_ERR_HIP if the copy fails. */
