@@ -323,7 +323,7 @@ mla_status mla_out_proj(const mla_dims* dims, int32_t batch, const float* o_late
  * (the combine's arithmetic and order, so o_latent is bit-identical to
  * mla_combine's) and feeds the merged rows to the W^UV product without writing
  * them out first.  Cites as mla_combine and mla_out_proj.  A workgroup takes
- * 32, 16 or 8 query rows of one head (fewer when 32 would leave CUs idle); the
+ * 32, 16, 8 or 4 query rows of one head (fewer when 32 would leave CUs idle); the
  * result does not depend on that choice.
  *   split_offsets, o_part, lse_part  as for mla_combine_multi (q_len = 1: as for
  *             mla_combine)

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(
 
 // ---------------------------------------------------------------------------
 // out_proj: o^T[128 x r] = W^UV_h[128 x 512] . o~^T[512 x r], one workgroup of
-// eight waves per (head, kOutRows = 32, 16 or 8 query rows).  Blocks (h, group)
+// eight waves per (head, kOutRows = 32, 16, 8 or 4 query rows).  Blocks (h, group)
 // and (h, group') run on one XCD (grid x = heads, a multiple of 8), so W^UV_h
 // comes from HBM once and from that XCD's L2 for the other groups.  The
 // float32 o~ of the rows is staged once in LDS as bf16 hi + lo (lo = bf16(x - hi)), rows of
@@ -194,7 +194,8 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
   // one bf16 copy of the staged o~; at 8 rows the MFMA's 16-row block also
   // reads rows 8..15, whose outputs are dropped
   constexpr int kOutHalfBytes = 16 * kRowBlocks * kDc * 2;
-  constexpr int kOutF4 = kOutRows * (kDc / 4) / kOutThreads;  // float4 per thread: 8, 4 or 2
+  constexpr int kOutF4 = kOutRows * (kDc / 4) / kOutThreads;  // float4 per thread: 8, 4, 2 or 1
+  static_assert(kOutF4 >= 1, "a thread stages whole float4s of at least one row");
   __shared__ __attribute__((aligned(16))) char lds[2 * kOutHalfBytes];  // [hi | lo][r][512]
   const int h = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -230,8 +231,8 @@ __global__ __launch_bounds__(kOutThreads) void out_proj_kernel(int rows, int H, 
     // last, reads the row's last item and the value is then replaced), so no
     // branch separates them; the planner gives every sequence at least one
     // item.
-    constexpr int kPair = 16 / kOutF4;   // items per load round of partials: 2, 4 or 8
-    constexpr int kChunk = 64 / kOutF4;  // items per lse load: 8, 16 or 32
+    constexpr int kPair = 16 / kOutF4;   // items per load round of partials: 2, 4, 8 or 16
+    constexpr int kChunk = 64 / kOutF4;  // items per lse load: 8, 16, 32 or 64
     // (a row's sequence: one query token per sequence is the common case, and
     // it needs no division)
     const bool one = q_len == 1;
@@ -395,12 +396,13 @@ int64_t out_proj_fast_groups(int64_t rows) { return (rows + 31) / 32; }
 
 int combine_out_proj_rows_per_group(int n_heads, int64_t rows) {
   // Query rows per workgroup: the largest of 32, 16, 8 that still gives
-  // 256 workgroups (one per CU), else 8.  A workgroup pulls every item's
-  // partial of its rows through one CU, so few large workgroups are slow: at
-  // 16 heads x 32 rows, 16 workgroups of 32 rows took 26 us.
-  for (int cand : {32, 16})
+  // 256 workgroups (one per CU), else 4.  A workgroup pulls every item's
+  // partial of its rows and all of W^UV_h through one CU, so few large
+  // workgroups are slow: at 16 heads x 32 rows, 16 workgroups of 32 rows
+  // took 26 us.
+  for (int cand : {32, 16, 8})
     if (n_heads * ((rows + cand - 1) / cand) >= 256) return cand;
-  return 8;
+  return 4;
 }
 
 hipError_t absorb_fast(const mla_dims& d, int batch, const void* q_nope, const void* q_pe,
@@ -445,8 +447,11 @@ hipError_t combine_out_proj_fast(const mla_dims& d, int batch, int q_len, const 
   else if (R == 16)
     hipLaunchKernelGGL((out_proj_kernel<true, 16>), grid, dim3(kOutThreads), 0, stream, nrows, d.n_heads, q_len,
                        split_offsets, o_part, lse_part, o_latent, lse, w, out);
-  else
+  else if (R == 8)
     hipLaunchKernelGGL((out_proj_kernel<true, 8>), grid, dim3(kOutThreads), 0, stream, nrows, d.n_heads, q_len,
+                       split_offsets, o_part, lse_part, o_latent, lse, w, out);
+  else
+    hipLaunchKernelGGL((out_proj_kernel<true, 4>), grid, dim3(kOutThreads), 0, stream, nrows, d.n_heads, q_len,
                        split_offsets, o_part, lse_part, o_latent, lse, w, out);
   return hipGetLastError();
 }

@@ -47,6 +47,8 @@ def partials(wl, dev, slots, T):
     ("h128_many_rows", small(V2, "f128b", 70, lens=(1, 3000), permute_pages=True), None, 2048, 1),
     ("h128_T3", small(V2, "f128c", 4, permute_pages=True), [3, 100, 4097, 9000], 2048, 3),
     ("h128_rows20", small(V2, "f128d", 20, lens=(1, 2000), permute_pages=True), None, 512, 1),
+    ("h128_rows12", small(V2, "f128e", 12, lens=(1, 3000), permute_pages=True), None, 512, 1),   # 8-row groups
+    ("h128_rows5", small(V2, "f128f", 5, lens=(1, 9000), permute_pages=True), None, 2048, 1),    # 4-row groups
     ("h16", small(LITE, "f16", 5, permute_pages=True), [1, 100, 4096, 4097, 700], 2048, 1),
     ("h16_T2_many_rows", small(LITE, "f16b", 40, lens=(2, 2000), permute_pages=True), None, 512, 2),
     ("h16_ragged_rows", small(LITE, "f16c", 21, lens=(1, 3000), permute_pages=True), None, 512, 1),
