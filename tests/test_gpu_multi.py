@@ -145,3 +145,38 @@ def test_multi_q_len_one_is_single_token(gpu_lib):
         assert np.array_equal(l1.cpu().numpy(), res["lse_part"][:, 0])
         assert np.array_equal(ol.cpu().numpy(), res["o_latent"][:, 0])
         assert np.array_equal(ll.cpu().numpy(), res["lse"][:, 0])
+
+
+def test_multi_token_full_size_sampled(gpu_lib):
+    """The headline batch (B 64, L 8192, 128 heads) at q_len 4, in the launch
+    configuration the bench times (its plan for slots // q_len, the fused merge
+    and W^UV), against the oracle on sampled sequences and heads."""
+    import torch
+    from oracle import multi_decode_workload
+    cfg = V2
+    T = 4
+    wl = generate(cfg)
+    B, H = cfg.batch, cfg.n_heads
+    say(f"[multi full size] q_len {T}")
+    dev = upload(wl)
+    dims = dims_of(cfg)
+    qn, qp = queries(wl, T)
+    pos = (wl.seq_lens[:, None].astype(np.int64) - T + np.arange(T)[None, :]).astype(np.int32)
+    q_abs = mla.absorb_q(dims, to_dev(qn.reshape(B * T, H, cfg.d_head), True),
+                         to_dev(qp.reshape(B * T, H, cfg.d_rope), True), to_dev(pos.reshape(-1), False),
+                         dev["w_uk"]).view(B, T, H, dims.row)
+    slots = int(torch.cuda.get_device_properties(0).multi_processor_count)
+    items, offs = mla.plan_splits(dims, wl.seq_lens, max(1, slots // T))
+    o_part, lse_part = mla.decode_splitkv_multi(dims, q_abs, dev["cache"], dev["block_table"],
+                                                dev["seq_lens"], torch.from_numpy(items).cuda())
+    o_lat = torch.empty((B, T, H, cfg.d_latent), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, T, H), dtype=torch.float32, device="cuda")
+    out = mla.combine_out_proj(dims, torch.from_numpy(offs).cuda(), o_part, lse_part, dev["w_uv"], B,
+                               o_latent=o_lat, lse=lse)
+    torch.cuda.synchronize()
+    seqs, heads = [0, 37, 63], [0, 45, 127]
+    ref = multi_decode_workload(wl, qn, qp, seqs=seqs, heads=heads)
+    sel = lambda a: a.cpu().numpy()[seqs][:, :, heads]  # noqa: E731
+    assert_close(sel(o_lat), ref["o_latent"], "o_latent")
+    assert_close(sel(out), ref["o"], "out")
+    assert_lse(sel(lse), ref["lse"])
