@@ -43,6 +43,7 @@ def merged(wl, ref, dev):
     ("h16_ragged", small(LITE, "m16", 5, permute_pages=True), [1, 100, 4096, 4097, 700], None),
     ("h16_many", small(LITE, "m16b", 2, permute_pages=True), [6000, 70], 2048),
     ("tiny_f32", CONFIGS["tiny_f32"], None, None),
+    ("h128_full_size", V2, None, None),   # the headline batch (bench.py --merged)
 ])
 def test_merged_matches_separate_calls(gpu_lib, name, cfg, lens, slots):
     wl = generate(cfg, lens=None if lens is None else np.array(lens, np.int32))
