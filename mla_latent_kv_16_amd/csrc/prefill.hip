@@ -13,11 +13,12 @@
 //
 // Two launches:
 //  * materialise: K^C and V^C of every cached row, [b][i][j][128] bf16 each, in
-//    the caller's workspace.  One workgroup of eight waves per (head, K or V,
-//    sequence) holds W_i (128 KiB) in LDS and walks the sequence's rows, 16 per
-//    wave at a time: D^T[128 x 16 rows] = W_i[128 x 512] . c^T[512 x 16 rows]
-//    with v_mfma_f32_16x16x32_bf16, the latent rows read straight from the
-//    paged cache, float32 accumulation rounded to bf16.
+//    the caller's workspace.  One workgroup of eight waves per (head,
+//    sequence) holds W^UK_i and W^UV_i in registers (32 rows per wave) and
+//    streams the sequence's latent rows through an LDS ring by DMA:
+//    D^T[32 x 32 rows] = W[32 x 512] . c^T[512 x 32 rows] per wave and tile
+//    with v_mfma_f32_32x32x16_bf16, float32 accumulation rounded to bf16 and
+//    staged in LDS so that whole rows are stored.
 //  * attention: one workgroup of eight waves per (256 query tokens, head,
 //    sequence), numbered so that all query blocks of one (sequence, head)
 //    run on one XCD at about the same time (they stream the same keys and
@@ -68,54 +69,144 @@ __device__ __forceinline__ const uint16_t* cache_row(const uint16_t* cache, cons
   return cache + (static_cast<int64_t>(bt[j >> 6]) * kPage + (j & (kPage - 1))) * kDq;
 }
 
-__global__ __launch_bounds__(512) void materialise_kv_kernel(
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float float16_t;
+
+// Materialisation, one workgroup per (head h, sequence b): K^C_h = c^KV W^UK_h^T
+// and V^C_h = c^KV W^UV_h^T from one pass over the sequence's latent rows.
+// Every workgroup of a sequence reads all its latent rows, so the L2-to-CU
+// traffic is (latent bytes) x H x (workgroups per head); producing K and V
+// together halves it against one workgroup per matrix.  Wave w keeps 32 rows
+// of one matrix (rows 32 (w % 4) .. +31 of W^UK_h for w < 4, of W^UV_h
+// otherwise) in registers as the A operand of v_mfma_f32_32x32x16_bf16 (32
+// k-steps x 8 values = 128 VGPRs); the latent rows stream through a ring of
+// kMatSlots LDS tiles of 32 rows, filled by DMA and read as the B operand.
+// The products of a tile go through LDS as well, so that each store writes
+// four whole 256-byte rows: written straight from the MFMA layout, every store
+// would scatter 16-byte pieces over 32 rows, and those partial-line writes
+// cost more than the whole latent stream.
+constexpr int kMatTile = 32;                       // latent rows per LDS tile
+constexpr int kMatSlots = 4;                       // tiles in the ring
+constexpr int kMatDma = kMatTile / 8;              // DMA rows per wave per tile
+constexpr int kMatStores = 2;                      // global stores per wave per tile
+constexpr int kMatRowB = kDc * 2;                  // 1024: latent bytes of a row
+constexpr int kMatOutB = 2 * kMatTile * kDh * 2;   // 16 KiB: K and V rows of a tile
+
+// s_waitcnt vmcnt(n') for the largest even n' <= n (n <= 2 kMax)
+template <int kMax>
+__device__ __forceinline__ void wait_vmcnt_even(int n) {
+  if constexpr (kMax == 0) {
+    __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+  } else {
+    if (n >= 2 * kMax)
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(2 * kMax));
+    else
+      wait_vmcnt_even<kMax - 1>(n);
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void materialise_kv_kernel(
     int H, int max_rows, const uint16_t* __restrict__ cache, const int32_t* __restrict__ block_table,
     int max_pages, const int32_t* __restrict__ seq_lens, const uint16_t* __restrict__ w_uk,
     const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc) {
-  // W_h (128 rows x 512, 128 KiB) in LDS, row r's 16-byte chunk c at position
-  // c ^ (r % 16): the A-operand reads (16 rows x one chunk per quarter-wave)
-  // then touch 16 distinct bank groups
-  __shared__ __attribute__((aligned(16))) char wl[kDh * kDc * 2];
-  const int h = blockIdx.x, which = blockIdx.y, b = blockIdx.z;
+  // ring: tile row r's 16-byte chunk c sits at position c ^ (r % 16), so that
+  // a ds_read_b128 cycle (16 lanes of a half-wave: rows n with equal parity of
+  // bits 2..4, one chunk) covers all 16 bank groups.  out: two buffers of
+  // [matrix][tile row][128 values], chunk c of row r at position c ^ (r % 16).
+  __shared__ __attribute__((aligned(1024))) char ring[kMatSlots * kMatTile * kMatRowB];
+  __shared__ __attribute__((aligned(1024))) char out[2 * kMatOutB];
+  const int h = blockIdx.x, b = blockIdx.y;
   const int L = seq_lens[b];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int g = lane >> 4, q = lane & 15;
-  const uint16_t* wh = (which ? w_uv : w_uk) + static_cast<int64_t>(h) * kDh * kDc;
-  for (int idx = threadIdx.x; idx < kDh * (kDc / 8); idx += blockDim.x) {
-    const int r = idx >> 6, c = idx & 63;
-    *reinterpret_cast<bf16x8*>(wl + r * (kDc * 2) + 16 * (c ^ (r & 15))) =
-        *reinterpret_cast<const bf16x8*>(wh + r * kDc + 8 * c);
-  }
-  __syncthreads();
+  if (L <= 0) return;  // uniform over the workgroup, before any barrier
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int n = lane & 31, g2 = lane >> 5;
+  const int mat = w >> 2, mb = w & 3;
+  // A operand: W row 32 mb + n, latent values 16ks + 8 g2 .. +8
+  const uint16_t* wsrc = (mat ? w_uv : w_uk) + (static_cast<int64_t>(h) * kDh + 32 * mb + n) * kDc + 8 * g2;
+  bf16x8 a[kDc / 16];
+#pragma unroll
+  for (int ks = 0; ks < kDc / 16; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(wsrc + 16 * ks);
+
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
-  uint16_t* dst0 = (which ? vc : kc) + (static_cast<int64_t>(b) * H + h) * max_rows * kDh;
-  // wave w takes rows j0 + 16w .. +15 of every 128-row tile
-  for (int j0 = 0; j0 < L; j0 += 8 * 16) {
-    const int jb = j0 + 16 * w;
-    if (jb >= L) continue;  // no barrier follows
-    const int j = jb + q;   // this lane's row (B operand column)
-    const bool jvalid = j < L;
-    const uint16_t* crow = cache_row(cache, bt, jvalid ? j : jb) + 8 * g;
-    bf16x8 cf[kDc / 32];
+  const int ntiles = (L + kMatTile - 1) / kMatTile;
+  // the 16 workgroups of a sequence on one XCD (heads h, h + 8, ...) start 16
+  // consecutive tiles apart and wrap around, rather than all on one tile
+  const int t0 = (h >> 3) % ntiles;
+  auto phys = [&](int t) { return t + t0 < ntiles ? t + t0 : t + t0 - ntiles; };
+  const uint32_t ring_lds = dec::lds_addr_of(ring);
+  // wave w copies rows kMatDma w .. +kMatDma of the tile issued t-th, one 1 KiB
+  // row per instruction (lane p fetches chunk p ^ (r % 16)); a tile lies inside
+  // one 64-row page, and rows past the end repeat row L - 1
+  auto issue = [&](int t, int page) {
+    const int tp = phys(t);
+    const char* pbase = reinterpret_cast<const char*>(cache) + static_cast<int64_t>(page) * kPage * (kDq * 2);
 #pragma unroll
-    for (int ks = 0; ks < kDc / 32; ++ks) cf[ks] = *reinterpret_cast<const bf16x8*>(crow + 32 * ks);
-    uint16_t* dst = dst0 + static_cast<int64_t>(j) * kDh;
+    for (int i = 0; i < kMatDma; ++i) {
+      const int r = kMatDma * w + i;
+      const int j = min(tp * kMatTile + r, L - 1);
+      dec::dma16(pbase + (j & (kPage - 1)) * (kDq * 2), 16u * (lane ^ (r & 15)),
+                 ring_lds + ((t % kMatSlots) * kMatTile + r) * kMatRowB);
+    }
+  };
+  // Vector-memory operations of this wave issued after tile t's DMA, before
+  // the wait for it (they complete in issue order): the DMA of tiles t+1 ..
+  // t+kMatSlots-2, and the stores that iterations t-kMatSlots+1 .. t-1 made
+  // of the tile before each of them.
+  auto wait_tile = [&](int t) {
+    const int dma_after = min(t + kMatSlots - 2, ntiles - 1) - t;
+    const int store_iters = t == 0 ? 0 : t - max(t - kMatSlots + 1, 1);
+    wait_vmcnt_even<(kMatDma * (kMatSlots - 2) + kMatStores * (kMatSlots - 1)) / 2>(
+        kMatDma * dma_after + kMatStores * store_iters);
+  };
+  static_assert(kMatDma % 2 == 0 && kMatStores % 2 == 0, "even wait counts");
+
+  // stores of tile t from out buffer t % 2: wave w writes rows 8 mb + 4s ..
+  // +3 (s < 2) of matrix `mat`, 16 bytes per lane, 1 KiB per instruction; the
+  // whole tile is written (rows from L on hold row L - 1's products and lie
+  // inside the workspace, which has max_pages * 64 rows)
+  uint16_t* dst = (mat ? vc : kc) + (static_cast<int64_t>(b) * H + h) * max_rows * kDh;
+  auto store_tile = [&](int t) {
+    const char* ob = out + (t & 1) * kMatOutB + mat * (kMatTile * kDh * 2);
+    const int c = lane & 15;
 #pragma unroll
-    for (int nb = 0; nb < kDh / 16; ++nb) {
-      // A operand: W_h row 16nb + q, latent values 32ks + 8g .. +8 (chunk 4ks + g)
-      const char* arow = wl + (16 * nb + q) * (kDc * 2);
-      float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s2 = 0; s2 < kMatStores; ++s2) {
+      const int r = 8 * mb + 4 * s2 + (lane >> 4);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(ob + r * (kDh * 2) + 16 * (c ^ (r & 15)));
+      *reinterpret_cast<bf16x8*>(dst + static_cast<int64_t>(phys(t) * kMatTile + r) * kDh + 8 * c) = v;
+    }
+  };
+
+  for (int t = 0; t < kMatSlots - 1 && t < ntiles; ++t) issue(t, bt[phys(t) >> 1]);
+  int next_page = kMatSlots - 1 < ntiles ? bt[phys(kMatSlots - 1) >> 1] : 0;
+  // B operand: tile row n, chunk 2ks + g2, at position 2ks ^ (g2 ^ (n % 16))
+  const int y = g2 ^ (n & 15);
+  for (int t = 0; t < ntiles; ++t) {
+    wait_tile(t);
+    // tile t is in LDS; tile t-1's ring slot is free; tile t-1's products are
+    // in out buffer (t-1) % 2, and buffer t % 2 has been stored
+    __syncthreads();
+    if (t + kMatSlots - 1 < ntiles) {
+      issue(t + kMatSlots - 1, next_page);
+      if (t + kMatSlots < ntiles) next_page = bt[phys(t + kMatSlots) >> 1];
+    }
+    const char* rb = ring + ((t % kMatSlots) * kMatTile + n) * kMatRowB;
+    float16_t acc = {};
 #pragma unroll
-      for (int ks = 0; ks < kDc / 32; ++ks)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            *reinterpret_cast<const bf16x8*>(arow + 16 * ((4 * ks + g) ^ q)), cf[ks], acc, 0, 0, 0);
-      // lane holds D^T[16nb + 4g + i][row j]
-      if (jvalid) {
-        const uint32_t lo = pack_bf16x2(acc[0], acc[1]), hi = pack_bf16x2(acc[2], acc[3]);
-        *reinterpret_cast<uint64_t*>(dst + 16 * nb + 4 * g) = (static_cast<uint64_t>(hi) << 32) | lo;
-      }
+    for (int ks = 0; ks < kDc / 16; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          a[ks], *reinterpret_cast<const bf16x8*>(rb + 16 * ((2 * ks) ^ y)), acc, 0, 0, 0);
+    if (t > 0) store_tile(t - 1);
+    // lane holds values 32 mb + 8i + 4 g2 .. +3 (i < 4) of tile row n: 8 bytes
+    // of chunk 4 mb + i
+    char* orow = out + (t & 1) * kMatOutB + mat * (kMatTile * kDh * 2) + n * (kDh * 2) + 8 * g2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = pack_bf16x2(acc[4 * i], acc[4 * i + 1]), hi = pack_bf16x2(acc[4 * i + 2], acc[4 * i + 3]);
+      *reinterpret_cast<uint64_t*>(orow + 16 * ((4 * mb + i) ^ (n & 15))) = (static_cast<uint64_t>(hi) << 32) | lo;
     }
   }
+  __syncthreads();
+  store_tile(ntiles - 1);
 }
 
 // K tile: 32 keys x 192 dimensions, rows padded to 400 bytes.  V tile: 32 keys
@@ -363,7 +454,7 @@ hipError_t prefill_naive(const mla_dims& d, int batch, int q_len, const void* q_
   const int max_rows = max_pages * kPage;
   uint16_t* kc = static_cast<uint16_t*>(workspace);
   uint16_t* vc = kc + static_cast<int64_t>(batch) * d.n_heads * max_rows * kDh;
-  hipLaunchKernelGGL(materialise_kv_kernel, dim3(d.n_heads, 2, batch), dim3(512), 0, stream,
+  hipLaunchKernelGGL(materialise_kv_kernel, dim3(d.n_heads, batch), dim3(512), 0, stream,
                      d.n_heads, max_rows, static_cast<const uint16_t*>(kv_cache),
                      block_table, max_pages, seq_lens, static_cast<const uint16_t*>(w_uk),
                      static_cast<const uint16_t*>(w_uv), kc, vc);
