@@ -27,7 +27,10 @@
 //    MFMAs); keys in tiles of 32 staged in LDS for all eight waves (two
 //    buffers, K row-major, V transposed), with an online
 //    softmax in base 2 whose reference moves only when the running maximum
-//    gains more than 2^8 (the accumulators are rescaled only then).
+//    gains more than 2^8 (the accumulators are rescaled only then); the
+//    causal mask is applied only on tiles that reach the wave's first query,
+//    the scale is folded into the exponent, and the row sums come from the
+//    MFMA (an all-ones block times P^T).
 //    S^T[16 keys x 16 queries] on MFMA (K rows as A, the query tile as B, 6
 //    steps over the 192 dimensions), then O^T[128 x 16 queries] += V^T . P^T
 //    with the reduction index running over the keys each lane's score
@@ -50,20 +53,13 @@ constexpr int kKeyTile = 32;   // keys per attention iteration
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr float kLn2F = 0.6931471805599453f;
 
-// Maximum / sum over the four lanes q, q+16, q+32, q+48 of a wave.
+// Maximum over the four lanes q, q+16, q+32, q+48 of a wave.
 __device__ __forceinline__ float rows4_max(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-__device__ __forceinline__ float rows4_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 // Row j of sequence b in the paged cache (the caller guarantees j < L_b).
 __device__ __forceinline__ const uint16_t* cache_row(const uint16_t* cache, const int32_t* bt, int j) {
   return cache + (static_cast<int64_t>(bt[j >> 6]) * kPage + (j & (kPage - 1))) * kDq;
@@ -285,16 +281,24 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void prefill_attn_kernel(
   }
 
   const float c2 = scale * kLog2eF;
+  // position of the wave's first query: a tile whose last key is at most this
+  // needs no causal mask (a tile holding keys at or past L never qualifies)
+  const int p_first = L - q_len + min(t0, q_len - 1);
+  // all-ones A operand: O^T's extra block 1 . P^T gives every query's row sum
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = static_cast<__bf16>(1.0f);
   const uint16_t* kh = kc + (static_cast<int64_t>(b) * H + h) * max_rows * kDh;
   const uint16_t* vh = vc + (static_cast<int64_t>(b) * H + h) * max_rows * kDh;
   float4_t o[kQB][kDh / 16];
-  float m_run[kQB], l_run[kQB];
+  float m_run[kQB];
+  float4_t lacc[kQB];  // row sums (every element of a lane: its query's)
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
 #pragma unroll
     for (int db = 0; db < kDh / 16; ++db) o[qb][db] = float4_t{0.f, 0.f, 0.f, 0.f};
     m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
+    lacc[qb] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   // Tile staging, software-pipelined over two LDS buffers: the 512 threads
@@ -335,6 +339,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void prefill_attn_kernel(
     // S^T for keys k0 + 16kb + row, queries of block qb: lane holds keys
     // 16kb + 4g + i.  Each row fragment read from LDS feeds one MFMA per
     // query block.
+    const bool diag = k0 + kKeyTile - 1 > p_first;  // the same for the whole wave
+    // raw scores q . K (not yet scaled); -inf where masked
     float s[kQB][2][4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void prefill_attn_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + 16 * kb + 4 * g + i;
-          s[qb][kb][i] = key <= pos[qb] ? acc[qb][i] * c2 : -INFINITY;
+          s[qb][kb][i] = (!diag || key <= pos[qb]) ? acc[qb][i] : -INFINITY;
         }
       }
     }
@@ -363,13 +369,14 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void prefill_attn_kernel(
     bf16x8 pf[kQB];
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-      const float mx = rows4_max(fmaxf(fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3])),
-                                       fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3]))));
-      // The reference m_run moves only when some query of the wave gains more
-      // than kRefSlack over it (always in the first tile, where m_run = -inf;
-      // mx is finite since key 0 <= pos).  Weights 2^(s - m_run) then stay
-      // below 2^kRefSlack, which bf16 weights and float32 sums carry without
-      // loss, and the accumulators are rescaled only on those tiles.
+      const float mx = c2 * rows4_max(fmaxf(fmaxf(fmaxf(s[qb][0][0], s[qb][0][1]), fmaxf(s[qb][0][2], s[qb][0][3])),
+                                            fmaxf(fmaxf(s[qb][1][0], s[qb][1][1]), fmaxf(s[qb][1][2], s[qb][1][3]))));
+      // The reference m_run (log2 units) moves only when some query of the
+      // wave gains more than kRefSlack over it (always in the first tile,
+      // where m_run = -inf; mx is finite since key 0 <= pos).  Weights
+      // 2^(s - m_run) then stay below 2^kRefSlack, which bf16 weights and
+      // float32 sums carry without loss, and the accumulators are rescaled
+      // only on those tiles.
       alpha[qb] = 1.f;
       if (__any(mx > m_run[qb] + kRefSlack)) {  // the same for the whole wave
         const float m_new = fmaxf(m_run[qb], mx);
@@ -377,15 +384,11 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void prefill_attn_kernel(
         m_run[qb] = m_new;
         rescale = true;
       }
-      float p[2][4], psum = 0.f;
+      float p[2][4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kb][i] = __builtin_amdgcn_exp2f(s[qb][kb][i] - m_run[qb]);
-          psum += p[kb][i];
-        }
-      l_run[qb] = l_run[qb] * alpha[qb] + rows4_sum(psum);
+        for (int i = 0; i < 4; ++i) p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][i], c2, -m_run[qb]));
       // P^T as the B operand: reduction index 8g + jj = key 4g + jj (jj < 4) or 16 + 4g + jj - 4
       const uint32_t pk[4] = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
                               pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
@@ -401,7 +404,17 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void prefill_attn_kernel(
           o[qb][db][2] *= alpha[qb];
           o[qb][db][3] *= alpha[qb];
         }
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        lacc[qb][0] *= alpha[qb];
+        lacc[qb][1] *= alpha[qb];
+        lacc[qb][2] *= alpha[qb];
+        lacc[qb][3] *= alpha[qb];
+      }
     }
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+      lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb], lacc[qb], 0, 0, 0);
 #pragma unroll
     for (int db = 0; db < kDh / 16; ++db) {
       // V^T as the A operand: dimension 16db + q, keys 4g .. 4g+3 and 16 + 4g ..
@@ -420,7 +433,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void prefill_attn_kernel(
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     if (!tvalid[qb]) continue;
-    const float inv = 1.f / l_run[qb];
+    const float l_sum = lacc[qb][0];
+    const float inv = 1.f / l_sum;
     const int64_t row = (static_cast<int64_t>(b) * q_len + t0 + 16 * qb + q) * H + h;
     float* orow = out + row * kDh + 4 * g;
 #pragma unroll
@@ -432,7 +446,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void prefill_attn_kernel(
       v[3] *= inv;
       *reinterpret_cast<float4_t*>(orow + 16 * db) = v;
     }
-    if (lse && g == 0) lse[row] = (m_run[qb] + log2f(l_run[qb])) * kLn2F;
+    if (lse && g == 0) lse[row] = (m_run[qb] + log2f(l_sum)) * kLn2F;
   }
 }
 
