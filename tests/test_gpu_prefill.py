@@ -145,3 +145,56 @@ def test_prefill_matches_absorbed_multi_token(gpu_lib):
     torch.cuda.synchronize()
     assert_close(out, out2.cpu().numpy(), "out vs absorbed")
     assert_lse(lse, lse2.cpu().numpy(), "lse vs absorbed")
+
+
+def test_materialised_kv_rows(gpu_lib):
+    """White-box check of the materialisation inside mla_prefill_naive (the
+    workspace contents are not part of the ABI; the layout read here is the
+    kernel's [K^C | V^C], each [b][h][row][128] bf16 with max_pages * 64 rows).
+
+    Every head and every row below L against the float64 products
+    W^UK_i c_j and W^UV_i c_j rounded once to bf16 (the kernel sums in float32,
+    so it may differ by a rounding step); the rows of the last 32-row tile past
+    L are written (finite) and every row past that tile keeps the NaN sentinel
+    the workspace was filled with, bit for bit.  Lengths end inside a tile, on
+    a tile boundary, and below one tile; the pages are permuted."""
+    import torch
+    from oracle import gather_rows, to_f64
+    from synth import bf16_bits_to_f32, f32_to_bf16_bits
+    cfg = small(V2, "pfmat", 3, permute_pages=True)
+    lens = [300, 64, 20]
+    T = 20
+    wl = generate(cfg, lens=np.array(lens, np.int32))
+    say(f"[prefill materialise rows] lens {lens}")
+    dev = upload(wl)
+    dims = dims_of(cfg)
+    B, H = cfg.batch, cfg.n_heads
+    max_pages = wl.block_table.shape[1]
+    max_rows = max_pages * 64
+    need = gpu_lib.mla_prefill_workspace_bytes(__import__("ctypes").byref(dims.c()), B, max_pages)
+    assert need == 2 * B * H * max_rows * 128 * 2
+    sentinel = 0x7FC1  # a bf16 NaN
+    ws = torch.full((need // 2,), sentinel, dtype=torch.int16, device="cuda")
+    qn, qp = queries(wl, T)
+    mla.prefill_naive(dims, to_dev(qn, True), to_dev(qp, True), dev["w_uk"], dev["w_uv"], dev["cache"],
+                      dev["block_table"], dev["seq_lens"], workspace=ws)
+    torch.cuda.synchronize()
+    got = ws.cpu().numpy().view(np.uint16).reshape(2, B, H, max_rows, 128)
+    w = {"k": to_f64(wl.w_uk, True), "v": to_f64(wl.w_uv, True)}
+    for b, L in enumerate(lens):
+        c = to_f64(gather_rows(wl.cache, wl.block_table[b], L, 64), True)[:, :512]
+        end = 32 * ((L + 31) // 32)
+        for m, name in enumerate(("k", "v")):
+            ref = (c @ w[name].T).reshape(L, H, 128).transpose(1, 0, 2)  # [H, L, 128]
+            mag = (np.abs(c) @ np.abs(w[name]).T).reshape(L, H, 128).transpose(1, 0, 2)
+            ref_bf = bf16_bits_to_f32(f32_to_bf16_bits(ref.astype(np.float32))).astype(np.float64)
+            g = bf16_bits_to_f32(got[m, b, :, :L]).astype(np.float64)
+            # one bf16 rounding step at that size, plus what 512 float32
+            # additions can lose where the sum cancels
+            step = np.abs(ref_bf) * 2.0 ** -7 + 4e-5 * mag
+            bad = np.abs(g - ref_bf) > step
+            assert not bad.any(), (f"{name} seq {b}: {bad.sum()} values off by more than one bf16 step; "
+                                   f"max |diff| {np.abs(g - ref_bf).max():.3e}")
+            tail = bf16_bits_to_f32(got[m, b, :, L:end])
+            assert np.all(np.isfinite(tail)), f"{name} seq {b}: rows {L}..{end} of the last tile not written"
+            assert np.all(got[m, b, :, end:] == sentinel), f"{name} seq {b}: rows past the last tile written"
