@@ -359,7 +359,8 @@ mla_status mla_prefill_naive(const mla_dims* dims, int32_t batch, int32_t q_len,
       !al16(workspace) || !al16(out) || !al4(block_table) || !al4(seq_lens) || (lse && !al4(lse)))
     return MLA_ERR_INVALID_ARG;
   if (!is_prefill_shape(*dims)) return MLA_ERR_UNSUPPORTED;
-  if (2 * static_cast<int64_t>(batch) > 65535 ||
+  // the materialisation grid is (heads, batch); the attention's is 1-D
+  if (batch > 65535 ||
       static_cast<int64_t>(batch) * q_len * dims->n_heads > (int64_t{1} << 31) ||
       static_cast<int64_t>(max_pages_per_seq) * 64 > (int64_t{1} << 24))
     return MLA_ERR_UNSUPPORTED;

@@ -249,6 +249,10 @@ def test_prefill_rejects_bad_arguments(lib):
     args[10] = need - 2                            # short workspace
     assert f(_d(), 2, 3, *args) == WORKSPACE
     assert f(_d(mla.Dims(4, 16, 64, 8, dtype=mla.F32)), 2, 3, *good) == UNSUPPORTED
+    # the materialisation grid holds 65535 sequences along y: one more is
+    # refused before the workspace is looked at, and 65535 gets that far
+    assert f(_d(), 65536, 3, *good) == UNSUPPORTED
+    assert f(_d(), 65535, 3, *good) == WORKSPACE
 
 
 def test_plan_rejects_bad_arguments(lib):
