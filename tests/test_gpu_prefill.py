@@ -147,7 +147,17 @@ def test_prefill_matches_absorbed_multi_token(gpu_lib):
     assert_lse(lse, lse2.cpu().numpy(), "lse vs absorbed")
 
 
-def test_materialised_kv_rows(gpu_lib):
+MAT_CASES = [
+    # name, lengths: ends inside a tile, on a tile boundary, below one tile;
+    # then one sequence of the benchmarked length (256 tiles: the ring's
+    # steady state and every head's start offset, wrapping around)
+    ("short", [300, 64, 20]),
+    ("full_length", [8192]),
+]
+
+
+@pytest.mark.parametrize("name,lens", MAT_CASES, ids=[c[0] for c in MAT_CASES])
+def test_materialised_kv_rows(gpu_lib, name, lens):
     """White-box check of the materialisation inside mla_prefill_naive (the
     workspace contents are not part of the ABI; the layout read here is the
     kernel's [K^C | V^C], each [b][h][row][128] bf16 with max_pages * 64 rows).
@@ -156,16 +166,14 @@ def test_materialised_kv_rows(gpu_lib):
     W^UK_i c_j and W^UV_i c_j rounded once to bf16 (the kernel sums in float32,
     so it may differ by a rounding step); the rows of the last 32-row tile past
     L are written (finite) and every row past that tile keeps the NaN sentinel
-    the workspace was filled with, bit for bit.  Lengths end inside a tile, on
-    a tile boundary, and below one tile; the pages are permuted."""
+    the workspace was filled with, bit for bit.  The pages are permuted."""
     import torch
     from oracle import gather_rows, to_f64
     from synth import bf16_bits_to_f32, f32_to_bf16_bits
-    cfg = small(V2, "pfmat", 3, permute_pages=True)
-    lens = [300, 64, 20]
-    T = 20
+    cfg = small(V2, "pfmat_" + name, len(lens), permute_pages=True)
+    T = min(lens)
     wl = generate(cfg, lens=np.array(lens, np.int32))
-    say(f"[prefill materialise rows] lens {lens}")
+    say(f"[prefill materialise rows {name}] lens {lens}")
     dev = upload(wl)
     dims = dims_of(cfg)
     B, H = cfg.batch, cfg.n_heads
@@ -181,20 +189,23 @@ def test_materialised_kv_rows(gpu_lib):
     torch.cuda.synchronize()
     got = ws.cpu().numpy().view(np.uint16).reshape(2, B, H, max_rows, 128)
     w = {"k": to_f64(wl.w_uk, True), "v": to_f64(wl.w_uv, True)}
+    hc = 16  # heads per reference block (bounds the float64 temporaries)
     for b, L in enumerate(lens):
         c = to_f64(gather_rows(wl.cache, wl.block_table[b], L, 64), True)[:, :512]
         end = 32 * ((L + 31) // 32)
-        for m, name in enumerate(("k", "v")):
-            ref = (c @ w[name].T).reshape(L, H, 128).transpose(1, 0, 2)  # [H, L, 128]
-            mag = (np.abs(c) @ np.abs(w[name]).T).reshape(L, H, 128).transpose(1, 0, 2)
-            ref_bf = bf16_bits_to_f32(f32_to_bf16_bits(ref.astype(np.float32))).astype(np.float64)
-            g = bf16_bits_to_f32(got[m, b, :, :L]).astype(np.float64)
-            # one bf16 rounding step at that size, plus what 512 float32
-            # additions can lose where the sum cancels
-            step = np.abs(ref_bf) * 2.0 ** -7 + 4e-5 * mag
-            bad = np.abs(g - ref_bf) > step
-            assert not bad.any(), (f"{name} seq {b}: {bad.sum()} values off by more than one bf16 step; "
-                                   f"max |diff| {np.abs(g - ref_bf).max():.3e}")
+        for m, name_m in enumerate(("k", "v")):
+            for h0 in range(0, H, hc):
+                wh = w[name_m][128 * h0:128 * (h0 + hc)]
+                ref = (c @ wh.T).reshape(L, hc, 128).transpose(1, 0, 2)  # [hc, L, 128]
+                mag = (np.abs(c) @ np.abs(wh).T).reshape(L, hc, 128).transpose(1, 0, 2)
+                ref_bf = bf16_bits_to_f32(f32_to_bf16_bits(ref.astype(np.float32))).astype(np.float64)
+                g = bf16_bits_to_f32(got[m, b, h0:h0 + hc, :L]).astype(np.float64)
+                # one bf16 rounding step at that size, plus what 512 float32
+                # additions can lose where the sum cancels
+                step = np.abs(ref_bf) * 2.0 ** -7 + 4e-5 * mag
+                bad = np.abs(g - ref_bf) > step
+                assert not bad.any(), (f"{name_m} seq {b} heads {h0}..{h0 + hc - 1}: {bad.sum()} values off by "
+                                       f"more than one bf16 step; max |diff| {np.abs(g - ref_bf).max():.3e}")
             tail = bf16_bits_to_f32(got[m, b, :, L:end])
-            assert np.all(np.isfinite(tail)), f"{name} seq {b}: rows {L}..{end} of the last tile not written"
-            assert np.all(got[m, b, :, end:] == sentinel), f"{name} seq {b}: rows past the last tile written"
+            assert np.all(np.isfinite(tail)), f"{name_m} seq {b}: rows {L}..{end} of the last tile not written"
+            assert np.all(got[m, b, :, end:] == sentinel), f"{name_m} seq {b}: rows past the last tile written"
