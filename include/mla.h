@@ -80,8 +80,8 @@
  *   starts at the work item's first-slice score maximum and moves up to a later
  *   slice's maximum when that passes it by more than 2^8 (the accumulators are
  *   rescaled then); MLA_DECODE_MAX_JUMP (log2 units, in (0, 30]) sets that
- *   threshold.  At 128 heads the two halves of a slice's tokens are scored by
- *   different waves, which agree on moves once per window of 8 slices (256
+ *   threshold.  With 64 heads per workgroup (head counts that are multiples
+ *   of 64) the two halves of a slice's tokens are scored by different waves, which agree on moves once per window of 8 slices (256
  *   tokens), from that window's maxima, so within a window the weights can
  *   pass the reference by the window's rise; if one passes 2^64 the item is
  *   recomputed against exact maxima (read the count with
@@ -89,7 +89,9 @@
  *   that bound).  The result is the same softmax either way.
  *
  * Supported shapes: the gfx950 fast path needs dtype MLA_BF16, d_latent 512,
- * d_rope 64, d_head 128, page_size 64 and n_heads 16 or 128; any other shape
+ * d_rope 64, d_head 128, page_size 64 and n_heads a multiple of 16 (the
+ * decode gives a work item n_heads / 64 workgroups of 64 heads when n_heads
+ * is a multiple of 64, else n_heads / 16 workgroups of 16); any other shape
  * with d_latent <= 1024, d_rope even and <= 128, d_head <= 256, page_size in
  * [1, 1024] and n_heads <= 1024 runs on straightforward kernels; larger ones
  * return MLA_ERR_UNSUPPORTED.
@@ -142,8 +144,9 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, const void* q_nope,
  * non-empty page ranges; every page of every sequence lands in exactly one item.
  * The item size is chosen so that about `num_slots` workgroups (CUs times
  * workgroups resident per CU) stay busy with even loads; on the gfx950 fast
- * path with 128 heads each item is decoded by two workgroups (one per half of
- * the heads), so about num_slots / 2 items are made.
+ * path each item is decoded by n_heads / 64 workgroups when n_heads is a
+ * multiple of 64 (two at 128 heads, one per half of the heads), else by
+ * n_heads / 16, so about num_slots divided by that many items are made.
  * items_host [max_items][4] receives (b, split, page_begin, page_end) for items
  * 0 .. *num_items-1, grouped by sequence in order; split_offsets_host [batch + 1]
  * receives the CSR offsets.  Both are plain host memory owned by the caller.
@@ -289,12 +292,13 @@ int64_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t
 /* Split-KV decode with the log-sum-exp merge fused in: the o_latent and lse of
  * mla_combine from one launch (same items and split_offsets as the two calls).
  * Pages as for mla_decode_splitkv; the merge is the combine's exact algebra.
- * On the gfx950 fast path every workgroup writes its partial to o_part /
- * lse_part, releases it, and takes a ticket; the last workgroup of a sequence
- * (of a half of its heads, at 128 heads) merges the partials in item order
- * and resets the ticket.  A sequence with a single item writes o_latent and
- * lse directly.  On other shapes this is mla_decode_splitkv followed by
- * mla_combine on the same stream.
+ * On the gfx950 fast path with 16 or 128 heads every workgroup writes its
+ * partial to o_part / lse_part, releases it, and takes a ticket; the last
+ * workgroup of a sequence (of a half of its heads, at 128 heads) merges the
+ * partials in item order and resets the ticket.  A sequence with a single
+ * item writes o_latent and lse directly.  With other head counts, and on
+ * other shapes, this is mla_decode_splitkv followed by mla_combine on the
+ * same stream (`tickets` is not touched).
  *   tickets   int32 [2 * batch] device memory, all zero on entry; every call
  *             leaves it zero (a call that fails before launching writes nothing)
  *   o_part, lse_part  scratch of the sizes mla_decode_splitkv needs; their

@@ -147,11 +147,11 @@ static_assert(kStages * kSlotBytes + 2 * kPBytesWG + 256 + kSWaves * 4 + 4 * kHe
 __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ items, int num_items, const int32_t* __restrict__ order, int q_len,
+    const int32_t* __restrict__ items, int num_items, const int32_t* __restrict__ order, int q_len, int H,
     float scale, float move_t, float safe_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
-  constexpr int H = 128;
+  const int G = H / kHeadsWG;  // workgroups per item and query token, 64 heads each
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes + 2 * kPBytesWG];
   __shared__ __attribute__((aligned(16))) char junk[256];
   __shared__ int ticket_lds;
@@ -169,12 +169,13 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
   const int g = lane >> 4;   // lane group (k block of the MFMA operands)
   const int q = lane & 15;   // row/column within a 16-block
 
-  // block -> (item, part): an item has 2 q_len workgroups, all on one XCD and
-  // dispatched together (block_to_item); part r = query token r / 2, half r % 2.
+  // block -> (item, part): an item has G q_len workgroups, all on one XCD and
+  // dispatched together (block_to_item); part r = query token r / G, head
+  // group r % G.
   int it, part;
-  block_to_item(blockIdx.x, num_items, 2 * q_len, it, part);
+  block_to_item(blockIdx.x, num_items, G * q_len, it, part);
   if (order) it = order[it];  // dispatch slot -> item
-  const int hh = part & 1, tq = part >> 1;
+  const int hh = part % G, tq = part / G;
   const int b = items[4 * it];
   const int p0 = items[4 * it + 2];
   const int p1 = items[4 * it + 3];
@@ -395,7 +396,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
         // release every wave's partial to the other XCDs (one L2 write-back),
         // then take the ticket
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        ticket_lds = atomicAdd(&tickets[2 * b + hh], 1);
+        ticket_lds = atomicAdd(&tickets[G * b + hh], 1);
       }
       __syncthreads();
       if (ticket_lds == nsplit - 1) {
@@ -426,9 +427,10 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
 #pragma unroll
       for (int j = 0; j < kLoadsPerWave; ++j) dma16(src + 128 * j, voff, dst + 1024 * j);
     };
-    // L2 prefetch of slice n: the 288 128-byte lines of its 32 rows, the even
-    // ones by half 0 of the pair and the odd ones by half 1 (the pair shares
-    // the L2), one 4-byte load per line from the V waves without DMA
+    // L2 prefetch of slice n: the 288 128-byte lines of its 32 rows, line i by
+    // head group i mod G (at 128 heads the even lines by one half of the pair
+    // and the odd ones by the other: the item's workgroups share the L2), one
+    // 4-byte load per line from the V waves without DMA
     const uint32_t junk_lds = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)junk));
     auto prefetch = [&](int n) {
@@ -438,8 +440,8 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       const char* src = cache + static_cast<int64_t>(page) * (kPage * kRowBytes) +
                         (tok0 & (kPage - 1)) * kRowBytes;
       const int nv = t_end - tok0;
-      const int li = 2 * ((u - kDmaWaves) * 64 + lane) + hh;  // line of the slice
-      if (li < 288 && li / 9 < nv) touch4(src, static_cast<uint32_t>(li * 128), junk_lds);
+      for (int li = G * ((u - kDmaWaves) * 64 + lane) + hh; li < 288 && li / 9 < nv; li += G * 256)
+        touch4(src, static_cast<uint32_t>(li * 128), junk_lds);  // line li of the slice
     };
     // wait for this wave's part of slice k (slice k+1 may stay in flight)
     auto wait_slice = [&](int k) {
@@ -620,7 +622,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
           }
           if (lse_out && u == 0 && g == 0) lse_out[static_cast<int64_t>(b) * H + head] = M + logf(Z);
         }
-        if (u == 0 && lane == 0) tickets[2 * b + hh] = 0;
+        if (u == 0 && lane == 0) tickets[G * b + hh] = 0;
       }
     }
   }
@@ -639,11 +641,11 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
 __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ items, int num_items, const int32_t* __restrict__ order, int q_len,
+    const int32_t* __restrict__ items, int num_items, const int32_t* __restrict__ order, int q_len, int H,
     float scale, float move_t, float safe_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
-  constexpr int H = 16;
+  const int G = H / 16;  // workgroups per item and query token, 16 heads each
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes];
   __shared__ int ticket_lds;
   const uint32_t lds_base =
@@ -655,8 +657,9 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
   const int q = lane & 15;
 
   // block -> (item, query token), laid out as in the 128-head kernel
-  int it, tq;
-  block_to_item(blockIdx.x, num_items, q_len, it, tq);
+  int it, part;
+  block_to_item(blockIdx.x, num_items, G * q_len, it, part);
+  const int head0 = 16 * (part % G), tq = part / G;
   if (order) it = order[it];  // dispatch slot -> item
   const int b = items[4 * it];
   const int p0 = items[4 * it + 2];
@@ -666,11 +669,11 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
   const int t_end = min(p1 * kPage, L - q_len + tq + 1);
   const int n_slices = (t_end - t_begin + kSliceTok - 1) / kSliceTok;
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
-  const int64_t qrow0 = (static_cast<int64_t>(b) * q_len + tq) * H;
-  const int64_t prow0 = (static_cast<int64_t>(it) * q_len + tq) * H;
-  if (n_slices <= 0) {  // empty partial, as in the 128-head kernel
-    for (int i = threadIdx.x; i < H * kDc; i += blockDim.x) o_part[prow0 * kDc + i] = 0.f;
-    if (threadIdx.x < H) lse_part[prow0 + threadIdx.x] = -INFINITY;
+  const int64_t qrow0 = (static_cast<int64_t>(b) * q_len + tq) * H + head0;  // q_abs row of the first head
+  const int64_t prow0 = (static_cast<int64_t>(it) * q_len + tq) * H + head0;  // its partial row
+  if (n_slices <= 0) {  // empty partial, as in the 64-head kernel
+    for (int i = threadIdx.x; i < 16 * kDc; i += blockDim.x) o_part[prow0 * kDc + i] = 0.f;
+    if (threadIdx.x < 16) lse_part[prow0 + threadIdx.x] = -INFINITY;
     return;
   }
   auto slot_of = [&](int n) -> const char* { return lds + (n % kStages) * kSlotBytes; };
@@ -858,13 +861,13 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
   if (w == 0 && g == 0) {
     const float lse_v = m_ref * kLn2 + logf(l);
     if (direct) {
-      if (lse_out) lse_out[static_cast<int64_t>(b) * H + q] = lse_v;
+      if (lse_out) lse_out[static_cast<int64_t>(b) * H + head0 + q] = lse_v;
     } else {
       lse_part[prow0 + q] = lse_v;
     }
   }
   const float inv = 1.f / l;
-  float* orow = (direct ? o_latent + static_cast<int64_t>(b) * H * kDc
+  float* orow = (direct ? o_latent + (static_cast<int64_t>(b) * H + head0) * kDc
                         : o_part + prow0 * kDc) + q * kDc + 128 * w + 4 * g;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -886,11 +889,11 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
       if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __syncthreads();
       float M = -INFINITY;
-      for (int s = s0; s < s0 + nsplit; ++s) M = fmaxf(M, lse_part[static_cast<int64_t>(s) * H + q]);
+      for (int s = s0; s < s0 + nsplit; ++s) M = fmaxf(M, lse_part[static_cast<int64_t>(s) * H + head0 + q]);
       float Z = 0.f;
       float4_t acc[8] = {};
       for (int s = s0; s < s0 + nsplit; ++s) {
-        const int64_t r = static_cast<int64_t>(s) * H + q;
+        const int64_t r = static_cast<int64_t>(s) * H + head0 + q;
         const float wgt = expf(lse_part[r] - M);
         Z += wgt;
 #pragma unroll
@@ -904,7 +907,7 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
         }
       }
       const float zinv = 1.f / Z;
-      float* lrow = o_latent + (static_cast<int64_t>(b) * H + q) * kDc + 128 * w + 4 * g;
+      float* lrow = o_latent + (static_cast<int64_t>(b) * H + head0 + q) * kDc + 128 * w + 4 * g;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         acc[c][0] *= zinv;
@@ -913,7 +916,7 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
         acc[c][3] *= zinv;
         *reinterpret_cast<float4_t*>(lrow + 16 * c) = acc[c];
       }
-      if (lse_out && w == 0 && g == 0) lse_out[static_cast<int64_t>(b) * H + q] = M + logf(Z);
+      if (lse_out && w == 0 && g == 0) lse_out[static_cast<int64_t>(b) * H + head0 + q] = M + logf(Z);
       if (threadIdx.x == 0) tickets[2 * b] = 0;
     }
   }
@@ -961,21 +964,25 @@ hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const vo
                        float* lse_part,
                        const int32_t* split_offsets, int32_t* tickets, float* o_latent,
                        float* lse_out, hipStream_t stream) {
-  const int64_t blocks = static_cast<int64_t>(num_items) * q_len * (d.n_heads == 128 ? 2 : 1);
+  // head counts that are multiples of 64 take the 64-heads-per-workgroup
+  // kernel, the other multiples of 16 the 16-heads-per-workgroup one
+  const bool wide = d.n_heads % kHeadsWG == 0;
+  const int groups = wide ? d.n_heads / kHeadsWG : d.n_heads / 16;
+  const int64_t blocks = static_cast<int64_t>(num_items) * q_len * groups;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
-  if (d.n_heads == 128) {
+  if (wide) {
     hipLaunchKernelGGL(decode_h128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(1024), 0, stream,
                        static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
-                       block_table, max_pages, seq_lens, items, num_items, order, q_len, d.softmax_scale,
-                       move_threshold(), safe_jump(), o_part, lse_part, split_offsets, tickets, o_latent,
-                       lse_out);
+                       block_table, max_pages, seq_lens, items, num_items, order, q_len, d.n_heads,
+                       d.softmax_scale, move_threshold(), safe_jump(), o_part, lse_part, split_offsets,
+                       tickets, o_latent, lse_out);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(decode_h16_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
-                     block_table, max_pages, seq_lens, items, num_items, order, q_len, d.softmax_scale,
-                     move_threshold(), safe_jump(), o_part, lse_part, split_offsets, tickets, o_latent,
-                       lse_out);
+                     block_table, max_pages, seq_lens, items, num_items, order, q_len, d.n_heads,
+                     d.softmax_scale, move_threshold(), safe_jump(), o_part, lse_part, split_offsets,
+                     tickets, o_latent, lse_out);
   return hipGetLastError();
 }
 

@@ -9,10 +9,18 @@ namespace mla {
 
 bool is_fast_shape(const mla_dims& d) {
   return d.dtype == MLA_BF16 && d.d_latent == kDc && d.d_rope == kDr && d.d_head == kDh &&
-         d.page_size == kPage && (d.n_heads == 16 || d.n_heads == 128);
+         d.page_size == kPage && d.n_heads % 16 == 0;
 }
 
 namespace {
+
+// Workgroups the decode gives one work item and query token: the fast path
+// takes 64 heads per workgroup when the head count is a multiple of 64 and
+// 16 otherwise; the straightforward kernels take a whole item.
+int decode_groups(const mla_dims& d) {
+  if (!is_fast_shape(d)) return 1;
+  return d.n_heads % 64 == 0 ? d.n_heads / 64 : d.n_heads / 16;
+}
 
 mla_status check_dims(const mla_dims* d) {
   if (!d) return MLA_ERR_INVALID_ARG;
@@ -95,9 +103,10 @@ mla_status mla_plan_splits(const mla_dims* dims, int32_t batch, const int32_t* s
                            int32_t* split_offsets_host, int32_t* num_items) {
   mla_status s = check_dims(dims);
   if (s != MLA_OK) return s;
-  // With 128 heads the fast decode gives every item two workgroups (one per half
-  // of the heads), so about num_slots / 2 items fill the machine.
-  const int per_item = (is_fast_shape(*dims) && dims->n_heads == 128) ? 2 : 1;
+  // The fast decode gives every item decode_groups() workgroups (two at 128
+  // heads, one per half of the heads), so about num_slots / that many items
+  // fill the machine.
+  const int per_item = decode_groups(*dims);
   const int slots = num_slots >= per_item ? num_slots / per_item : num_slots;
   return plan_splits(dims->page_size, batch, seq_lens_host, slots, max_items, items_host,
                      split_offsets_host, num_items, dims->n_heads);
@@ -110,7 +119,7 @@ mla_status mla_plan_splits_ordered(const mla_dims* dims, int32_t batch, const in
   mla_status s = check_dims(dims);
   if (s != MLA_OK) return s;
   if (!order_host) return MLA_ERR_INVALID_ARG;
-  const int per_item = (is_fast_shape(*dims) && dims->n_heads == 128) ? 2 : 1;
+  const int per_item = decode_groups(*dims);
   const int slots = num_slots >= per_item ? num_slots / per_item : num_slots;
   return plan_splits(dims->page_size, batch, seq_lens_host, slots, max_items, items_host,
                      split_offsets_host, num_items, dims->n_heads, order_host);
@@ -133,7 +142,7 @@ mla_status decode_splitkv_impl(const mla_dims* dims, int32_t batch, int32_t q_le
       !al4(seq_lens) || !al4(items) || (order && !al4(order)))
     return MLA_ERR_INVALID_ARG;
   // partial rows and workgroup counts stay within 32-bit grid limits
-  if (static_cast<int64_t>(num_items) * q_len * 2 > INT32_MAX ||
+  if (static_cast<int64_t>(num_items) * q_len * decode_groups(*dims) > INT32_MAX ||
       static_cast<int64_t>(batch) * q_len * dims->n_heads > (int64_t{1} << 31))
     return MLA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -219,15 +228,25 @@ mla_status mla_decode_merged(const mla_dims* dims, int32_t batch, const void* q_
       (lse && !al4(lse)))
     return MLA_ERR_INVALID_ARG;
   // partial rows and workgroup counts stay within 32-bit grid limits
-  if (static_cast<int64_t>(num_items) * 2 > INT32_MAX ||
+  if (static_cast<int64_t>(num_items) * decode_groups(*dims) > INT32_MAX ||
       static_cast<int64_t>(batch) * dims->n_heads > (int64_t{1} << 31))
     return MLA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // drop an error left on this thread by an earlier, unrelated call
-  if (is_fast_shape(*dims))
+  if (is_fast_shape(*dims) && (dims->n_heads == 16 || dims->n_heads == 128))
     return launched(decode_fast(*dims, 1, q_abs, kv_cache, block_table, max_pages_per_seq,
                                 seq_lens, items, num_items, nullptr, o_part, lse_part, split_offsets,
                                 tickets, o_latent, lse, st));
+  if (is_fast_shape(*dims)) {
+    // other head counts: the fast decode and the fast merge as two launches
+    // (the ticket array holds two counters per sequence, as many as 128
+    // heads use); `tickets` is left untouched
+    mla_status r = launched(decode_fast(*dims, 1, q_abs, kv_cache, block_table, max_pages_per_seq,
+                                        seq_lens, items, num_items, nullptr, o_part, lse_part,
+                                        nullptr, nullptr, nullptr, nullptr, st));
+    if (r != MLA_OK) return r;
+    return launched(combine_fast(*dims, batch, 1, split_offsets, o_part, lse_part, o_latent, lse, st));
+  }
   mla_status r = launched(decode_generic(*dims, 1, q_abs, kv_cache, block_table, max_pages_per_seq,
                                          seq_lens, items, num_items, o_part, lse_part, st));
   if (r != MLA_OK) return r;

@@ -38,7 +38,9 @@ int main(void) {
   CHECK(mla_fast_path(&v2) == 1);
   {
     mla_dims odd = v2;
-    odd.n_heads = 64;
+    odd.n_heads = 64; /* any multiple of 16 */
+    CHECK(mla_fast_path(&odd) == 1);
+    odd.n_heads = 40;
     CHECK(mla_fast_path(&odd) == 0);
     odd.d_rope = 63; /* must be even */
     CHECK(mla_fast_path(&odd) < 0);

@@ -50,7 +50,10 @@ def test_fast_path_shapes(lib):
     assert mla.fast_path(V2) == 1
     assert mla.fast_path(mla.Dims(16, 128, 512, 64)) == 1
     assert mla.fast_path(mla.Dims(4, 16, 64, 8, dtype=mla.F32)) == 0
-    assert mla.fast_path(mla.Dims(64, 128, 512, 64)) == 0       # straightforward kernels
+    for h in (32, 48, 64, 192, 1024):                             # any multiple of 16
+        assert mla.fast_path(mla.Dims(h, 128, 512, 64)) == 1, h
+    for h in (8, 24, 100):                                        # straightforward kernels
+        assert mla.fast_path(mla.Dims(h, 128, 512, 64)) == 0, h
     assert mla.fast_path(mla.Dims(128, 128, 512, 64, page_size=32)) == 0
     assert mla.fast_path(mla.Dims(4, 16, 64, 7)) == INVALID     # odd RoPE width
     assert mla.fast_path(mla.Dims(4, 16, 2048, 8)) == UNSUPPORTED
@@ -220,7 +223,7 @@ def test_combine_out_proj_rejects_bad_arguments(lib):
         assert f(_d(), 2, 1, *args) == INVALID, i
     assert f(_d(), 2 ** 20, 2 ** 10, *good) == UNSUPPORTED
     # off the fast path the two kernels need o_latent between them
-    assert f(_d(mla.Dims(64, 128, 512, 64)), 2, 1, *good) == UNSUPPORTED
+    assert f(_d(mla.Dims(8, 128, 512, 64)), 2, 1, *good) == UNSUPPORTED
 
 
 def test_prefill_rejects_bad_arguments(lib):

@@ -42,6 +42,9 @@ def merged(wl, ref, dev):
     ("h128_many", small(V2, "m128b", 2, permute_pages=True), [9000, 3000], 2048),
     ("h16_ragged", small(LITE, "m16", 5, permute_pages=True), [1, 100, 4096, 4097, 700], None),
     ("h16_many", small(LITE, "m16b", 2, permute_pages=True), [6000, 70], 2048),
+    # other head counts: the fast decode and the fast merge as two launches
+    ("h64_ragged", small(V2, "m64", 4, n_heads=64, permute_pages=True), [1, 65, 4097, 700], None),
+    ("h32_many", small(V2, "m32", 2, n_heads=32, permute_pages=True), [6000, 70], 2048),
     ("tiny_f32", CONFIGS["tiny_f32"], None, None),
     ("h128_full_size", V2, None, None),   # the headline batch (bench.py --merged)
 ])

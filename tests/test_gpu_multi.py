@@ -106,6 +106,8 @@ CASES = [
     ("h128_T8", small(V2, "q128d", 3, permute_pages=True), [8, 1000, 8200], 8, 2048, [2, 70, 127]),
     ("h16_T2", small(LITE, "q16a", 5, permute_pages=True), [2, 64, 65, 4097, 700], 2, 2048, None),
     ("h16_T5", small(LITE, "q16b", 4, permute_pages=True), [5, 69, 3333, 8000], 5, 2048, None),
+    ("h64_T3", small(V2, "q64", 3, n_heads=64, permute_pages=True), [3, 130, 4097], 3, 2048, None),
+    ("h48_T2", small(V2, "q48", 3, n_heads=48, permute_pages=True), [2, 65, 3000], 2, 2048, None),
     ("tiny_f32_T3", CONFIGS["tiny_f32"], None, 3, 64, None),
 ]
 

@@ -58,15 +58,39 @@ def test_lite_heads16_ragged(mla):
     compare_with_oracle(wl, out, range(4))
 
 
-def test_generic_heads64(mla):
-    # 64 heads is outside the fast path: the straightforward kernels serve it
-    cfg = small(V2, "v2_h64", 2, n_heads=64)
+def test_generic_heads8(mla):
+    # 8 heads (not a multiple of 16) is outside the fast path: the
+    # straightforward kernels serve it, at the V2 row shape
+    cfg = small(V2, "v2_h8", 2, n_heads=8)
     lens = np.array([70, 300], np.int32)
-    say("[generic heads 64]")
+    say("[generic heads 8]")
     wl = generate(cfg, lens=lens)
     assert mla.fast_path(dims_of(cfg)) == 0
     out = run(wl)
     compare_with_oracle(wl, out, range(2))
+
+
+# Other head counts on the fast path: multiples of 64 take the 64-heads-per-
+# workgroup kernel with H / 64 workgroups per item, the other multiples of 16
+# the 16-heads-per-workgroup kernel with H / 16; ragged lengths, permuted pages
+# and many-split plans, every head against the oracle.
+OTHER_HEADS = [
+    # heads, lengths, plan slots
+    (32, [1, 65, 700, 4100], 2048),
+    (48, [64, 129, 3000], 256),
+    (64, [1, 64, 65, 777, 5000], 2048),
+    (192, [33, 2050, 700], 256),
+]
+
+
+@pytest.mark.parametrize("heads,lens,slots", OTHER_HEADS, ids=[f"h{h}" for h, _, _ in OTHER_HEADS])
+def test_fast_path_other_head_counts(mla, heads, lens, slots):
+    cfg = small(V2, f"v2_h{heads}", len(lens), n_heads=heads, permute_pages=True)
+    say(f"[fast path heads {heads}] lens {lens}")
+    wl = generate(cfg, lens=np.array(lens, np.int32))
+    assert mla.fast_path(dims_of(cfg)) == 1
+    out = run(wl, slots=slots)
+    compare_with_oracle(wl, out, range(len(lens)))
 
 
 def _scale_latents(wl, first, factor):
