@@ -80,8 +80,8 @@
  *   starts at the work item's first-slice score maximum and moves up to a later
  *   slice's maximum when that passes it by more than 2^8 (the accumulators are
  *   rescaled then); MLA_DECODE_MAX_JUMP (log2 units, in (0, 30]) sets that
- *   threshold.  With 64 heads per workgroup (head counts that are multiples
- *   of 64) the two halves of a slice's tokens are scored by different waves, which agree on moves once per window of 8 slices (256
+ *   threshold.  With up to 64 heads per workgroup (every head count but 16)
+ *   the two halves of a slice's tokens are scored by different waves, which agree on moves once per window of 8 slices (256
  *   tokens), from that window's maxima, so within a window the weights can
  *   pass the reference by the window's rise; if one passes 2^64 the item is
  *   recomputed against exact maxima (read the count with
@@ -90,8 +90,8 @@
  *
  * Supported shapes: the gfx950 fast path needs dtype MLA_BF16, d_latent 512,
  * d_rope 64, d_head 128, page_size 64 and n_heads a multiple of 16 (the
- * decode gives a work item n_heads / 64 workgroups of 64 heads when n_heads
- * is a multiple of 64, else n_heads / 16 workgroups of 16); any other shape
+ * decode gives a work item one workgroup at 16 heads, else ceil(n_heads / 64)
+ * workgroups of up to 64 heads); any other shape
  * with d_latent <= 1024, d_rope even and <= 128, d_head <= 256, page_size in
  * [1, 1024] and n_heads <= 1024 runs on straightforward kernels; larger ones
  * return MLA_ERR_UNSUPPORTED.
@@ -144,9 +144,9 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, const void* q_nope,
  * non-empty page ranges; every page of every sequence lands in exactly one item.
  * The item size is chosen so that about `num_slots` workgroups (CUs times
  * workgroups resident per CU) stay busy with even loads; on the gfx950 fast
- * path each item is decoded by n_heads / 64 workgroups when n_heads is a
- * multiple of 64 (two at 128 heads, one per half of the heads), else by
- * n_heads / 16, so about num_slots divided by that many items are made.
+ * path each item is decoded by one workgroup at 16 heads and otherwise by
+ * ceil(n_heads / 64) (two at 128 heads, one per half of the heads), so about
+ * num_slots divided by that many items are made.
  * items_host [max_items][4] receives (b, split, page_begin, page_end) for items
  * 0 .. *num_items-1, grouped by sequence in order; split_offsets_host [batch + 1]
  * receives the CSR offsets.  Both are plain host memory owned by the caller.

@@ -151,7 +151,9 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     float scale, float move_t, float safe_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
-  const int G = H / kHeadsWG;  // workgroups per item and query token, 64 heads each
+  // workgroups per item and query token, 64 heads each (the last one fewer
+  // when 64 does not divide H)
+  const int G = (H + kHeadsWG - 1) / kHeadsWG;
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes + 2 * kPBytesWG];
   __shared__ __attribute__((aligned(16))) char junk[256];
   __shared__ int ticket_lds;
@@ -186,14 +188,18 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
   const int n_slices = (t_end - t_begin + kSliceTok - 1) / kSliceTok;
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
   const int head0 = kHeadsWG * hh;
+  // heads of this group: 64, or fewer in the last group when H is not a
+  // multiple of 64 (a multiple of 16); the other head blocks run on zero
+  // queries, so their weights are finite, and nothing of theirs is stored
+  const int nh = min(kHeadsWG, H - head0);
   const int64_t qrow0 = (static_cast<int64_t>(b) * q_len + tq) * H;    // q_abs row of head 0
   const int64_t prow0 = (static_cast<int64_t>(it) * q_len + tq) * H;   // partial row of head 0
   if (n_slices <= 0) {
     // none of the item's tokens is visible to this query token: an empty
     // partial (weight 0 in the merge); uniform over the workgroup, no barrier
-    for (int i = threadIdx.x; i < kHeadsWG * kDc; i += blockDim.x)
+    for (int i = threadIdx.x; i < nh * kDc; i += blockDim.x)
       o_part[(prow0 + head0 + i / kDc) * kDc + i % kDc] = 0.f;
-    if (threadIdx.x < kHeadsWG) lse_part[prow0 + head0 + threadIdx.x] = -INFINITY;
+    if (threadIdx.x < nh) lse_part[prow0 + head0 + threadIdx.x] = -INFINITY;
     return;
   }
   // Merged mode (tickets != null): o~ and lse of the sequence instead of a
@@ -222,10 +228,13 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     __builtin_amdgcn_s_setprio(MLA_S_PRIO);
     const int hb = w & 3, th = w >> 2;
     bf16x8 qf[18];  // B operand: head head0 + 16hb + q, values 32ks + 8g .. +8
-    {
+    if (16 * hb < nh) {
       const uint16_t* qrow = q_abs + (qrow0 + head0 + 16 * hb + q) * kDq + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) qf[ks] = bf16x8{};
     }
     const int sw = swz(q);
     const uint32_t qk_base = th * kRowGroup2 + (q >> 3) * kTileRowGroup + (q & 7) * 128;
@@ -381,7 +390,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     const float l = rows_sum(l_run);
     if (g == 0) lsum2[th][hidx] = l;
     __syncthreads();
-    if (th == 0 && g == 0) {
+    if (th == 0 && g == 0 && hidx < nh) {
       const float lse_v = m_ref * kLn2 + logf(lsum2[0][hidx] + lsum2[1][hidx]);
       if (direct) {
         if (lse_out) lse_out[static_cast<int64_t>(b) * H + head0 + hidx] = lse_v;
@@ -566,6 +575,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     __syncthreads();
 #pragma unroll
     for (int hb = 0; hb < kHeadBlocksWG; ++hb) {
+      if (16 * hb >= nh) continue;  // a head block past H (uniform over the wave)
       const float inv = 1.f / (lsum2[0][16 * hb + q] + lsum2[1][16 * hb + q]);
       const int64_t row = direct ? static_cast<int64_t>(b) * H + head0 + 16 * hb + q
                                  : prow0 + head0 + 16 * hb + q;
@@ -964,10 +974,12 @@ hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const vo
                        float* lse_part,
                        const int32_t* split_offsets, int32_t* tickets, float* o_latent,
                        float* lse_out, hipStream_t stream) {
-  // head counts that are multiples of 64 take the 64-heads-per-workgroup
-  // kernel, the other multiples of 16 the 16-heads-per-workgroup one
-  const bool wide = d.n_heads % kHeadsWG == 0;
-  const int groups = wide ? d.n_heads / kHeadsWG : d.n_heads / 16;
+  // 16 heads take the 16-heads-per-workgroup kernel; every other multiple of
+  // 16 takes ceil(H / 64) workgroups of 64 heads per item (the last one
+  // partly on zero queries when 64 does not divide H): with one workgroup
+  // per 64 heads each row is taken in by as few CUs as possible
+  const bool wide = d.n_heads != 16;
+  const int groups = wide ? (d.n_heads + kHeadsWG - 1) / kHeadsWG : 1;
   const int64_t blocks = static_cast<int64_t>(num_items) * q_len * groups;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   if (wide) {

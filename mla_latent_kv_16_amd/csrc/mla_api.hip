@@ -15,11 +15,11 @@ bool is_fast_shape(const mla_dims& d) {
 namespace {
 
 // Workgroups the decode gives one work item and query token: the fast path
-// takes 64 heads per workgroup when the head count is a multiple of 64 and
-// 16 otherwise; the straightforward kernels take a whole item.
+// takes 16 heads in one workgroup and otherwise up to 64 heads per workgroup
+// (ceil(H / 64)); the straightforward kernels take a whole item.
 int decode_groups(const mla_dims& d) {
-  if (!is_fast_shape(d)) return 1;
-  return d.n_heads % 64 == 0 ? d.n_heads / 64 : d.n_heads / 16;
+  if (!is_fast_shape(d) || d.n_heads == 16) return 1;
+  return (d.n_heads + 63) / 64;
 }
 
 mla_status check_dims(const mla_dims* d) {

@@ -70,15 +70,17 @@ def test_generic_heads8(mla):
     compare_with_oracle(wl, out, range(2))
 
 
-# Other head counts on the fast path: multiples of 64 take the 64-heads-per-
-# workgroup kernel with H / 64 workgroups per item, the other multiples of 16
-# the 16-heads-per-workgroup kernel with H / 16; ragged lengths, permuted pages
-# and many-split plans, every head against the oracle.
+# Other head counts on the fast path: ceil(H / 64) workgroups of 64 heads per
+# item, the last one partly on zero queries when 64 does not divide H (32, 48:
+# one group with 2 or 3 of its 4 head blocks real; 80: a second group with
+# one); ragged lengths, permuted pages and many-split plans, every head
+# against the oracle.
 OTHER_HEADS = [
     # heads, lengths, plan slots
     (32, [1, 65, 700, 4100], 2048),
     (48, [64, 129, 3000], 256),
     (64, [1, 64, 65, 777, 5000], 2048),
+    (80, [2, 300, 4097], 2048),
     (192, [33, 2050, 700], 256),
 ]
 
