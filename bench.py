@@ -10,7 +10,7 @@ it.  With --q-len T every sequence decodes its T newest tokens at once (causal
 among them): absorb on B*T rows, mla_decode_splitkv_multi, then the merge and
 W^UV on B*T rows.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--merged | --unfused]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--heads H] [--merged | --unfused]
                     [--q-len T] [--slots N] [--back-to-back] [--prefill T [--prefill-batch B]]
                     [--settle-ms MS] [--graph] [--fenced-events] [--no-cpu-baseline]
                     [--copy-probe]
@@ -276,6 +276,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="v2_b64_l8192")
+    ap.add_argument("--heads", type=int, default=0, metavar="H",
+                    help="run the workload with H heads instead of its own (a multiple of 16 "
+                         "takes the gfx950 kernels; the workload is then named <workload>_h<H>)")
     ap.add_argument("--back-to-back", action="store_true",
                     help="no flush: steps back to back over several layers' inputs, two events")
     ap.add_argument("--merged", action="store_true",
@@ -324,6 +327,9 @@ def main():
     from synth import CONFIGS, generate, query_multi
 
     cfg = CONFIGS[args.workload]
+    if args.heads:
+        from synth import small
+        cfg = small(cfg, f"{cfg.name}_h{args.heads}", cfg.batch, n_heads=args.heads)
     t0 = time.perf_counter()
     wl = generate(cfg)
     log(f"[bench] generated {cfg.name} in {time.perf_counter() - t0:.1f} s "
