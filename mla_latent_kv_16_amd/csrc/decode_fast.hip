@@ -32,8 +32,9 @@
 //    permuted (k -> token sigma(g, k), see below) so that the QK^T
 //    accumulators of a lane already hold the P^T operand of the same lane.
 //
-// Work split, H = 128: two workgroups per work item, one per half of the
-// heads (see decode_h128_kernel), each with sixteen waves in two roles:
+// Work split, every head count but 16 (decode_h128_kernel): ceil(H / 64)
+// workgroups per work item, one per group of up to 64 heads (two at the
+// 128 heads of V2, one per half), each with sixteen waves in two roles:
 //  * eight S waves: scores of 16 heads over one 16-token half of every slice
 //    (Q fragments stay in 72 VGPRs), turned into bf16 weights and put in a
 //    4 KiB LDS exchange buffer;
@@ -41,8 +42,9 @@
 //    (64 accumulators), so each transposed C^T fragment feeds 4 MFMAs; four
 //    of them also run the DMA, the other four the L2 prefetch.
 //  The V waves run one slice behind the S waves; one workgroup barrier per
-//  slice.  H = 16 (decode_h16_kernel): one workgroup of four waves per item,
-//  each scoring all 16 heads itself.
+//  slice.  A last group with fewer than 64 heads runs its other head blocks
+//  on zero queries and stores nothing of them.  H = 16 (decode_h16_kernel):
+//  one workgroup of four waves per item, each scoring all 16 heads itself.
 //
 // Softmax in base 2 against a reference per head that starts at the maximum
 // of the item's first slice and moves up to a later slice's maximum when that
@@ -655,7 +657,7 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
     float scale, float move_t, float safe_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
-  const int G = H / 16;  // workgroups per item and query token, 16 heads each
+  const int G = H / 16;  // workgroups per item and query token (the launch uses this kernel at 16 heads: one)
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kSlotBytes];
   __shared__ int ticket_lds;
   const uint32_t lds_base =
