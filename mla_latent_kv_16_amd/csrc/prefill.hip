@@ -37,6 +37,8 @@
 //    accumulators hold, so P^T needs no reshuffle.
 #include <math.h>
 
+#include <algorithm>
+
 #include "decode_common.h"
 #include "device_common.h"
 #include "mla_internal.h"
@@ -124,11 +126,17 @@ __global__ __launch_bounds__(512, 1) void materialise_kv_kernel(
   for (int ks = 0; ks < kDc / 16; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(wsrc + 16 * ks);
 
   const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
-  const int ntiles = (L + kMatTile - 1) / kMatTile;
+  // split z of gridDim.z takes the tiles z0 .. z0 + ntiles - 1 of the sequence
+  // (more workgroups when heads x batch alone would leave CUs idle)
+  const int all_tiles = (L + kMatTile - 1) / kMatTile;
+  const int per_split = (all_tiles + gridDim.z - 1) / gridDim.z;
+  const int z0 = blockIdx.z * per_split;
+  const int ntiles = min(per_split, all_tiles - z0);
+  if (ntiles <= 0) return;  // uniform over the workgroup, before any barrier
   // the 16 workgroups of a sequence on one XCD (heads h, h + 8, ...) start 16
   // consecutive tiles apart and wrap around, rather than all on one tile
   const int t0 = (h >> 3) % ntiles;
-  auto phys = [&](int t) { return t + t0 < ntiles ? t + t0 : t + t0 - ntiles; };
+  auto phys = [&](int t) { return z0 + (t + t0 < ntiles ? t + t0 : t + t0 - ntiles); };
   const uint32_t ring_lds = dec::lds_addr_of(ring);
   // wave w copies rows kMatDma w .. +kMatDma of the tile issued t-th, one 1 KiB
   // row per instruction (lane p fetches chunk p ^ (r % 16)); a tile lies inside
@@ -468,7 +476,13 @@ hipError_t prefill_naive(const mla_dims& d, int batch, int q_len, const void* q_
   const int max_rows = max_pages * kPage;
   uint16_t* kc = static_cast<uint16_t*>(workspace);
   uint16_t* vc = kc + static_cast<int64_t>(batch) * d.n_heads * max_rows * kDh;
-  hipLaunchKernelGGL(materialise_kv_kernel, dim3(d.n_heads, batch), dim3(512), 0, stream,
+  // one workgroup per (head, sequence), each sequence's rows split further
+  // when that leaves CUs idle, keeping at least 8 tiles per split
+  const int64_t pairs = static_cast<int64_t>(d.n_heads) * batch;
+  const int max_tiles = max_pages * (kPage / kMatTile);
+  const int splits = static_cast<int>(
+      std::max<int64_t>(1, std::min<int64_t>((256 + pairs - 1) / pairs, max_tiles / 8)));
+  hipLaunchKernelGGL(materialise_kv_kernel, dim3(d.n_heads, batch, splits), dim3(512), 0, stream,
                      d.n_heads, max_rows, static_cast<const uint16_t*>(kv_cache),
                      block_table, max_pages, seq_lens, static_cast<const uint16_t*>(w_uk),
                      static_cast<const uint16_t*>(w_uv), kc, vc);

@@ -148,16 +148,19 @@ def test_prefill_matches_absorbed_multi_token(gpu_lib):
 
 
 MAT_CASES = [
-    # name, lengths: ends inside a tile, on a tile boundary, below one tile;
-    # then one sequence of the benchmarked length (256 tiles: the ring's
-    # steady state and every head's start offset, wrapping around)
-    ("short", [300, 64, 20]),
-    ("full_length", [8192]),
+    # name, config, lengths: ends inside a tile, on a tile boundary, below one
+    # tile; one sequence of the benchmarked length (256 tiles in two splits:
+    # the ring's steady state and every head's start offset, wrapping around);
+    # 16 heads, where each sequence's rows are split eight ways and the short
+    # sequence leaves its last splits one tile or none
+    ("short", V2, [300, 64, 20]),
+    ("full_length", V2, [8192]),
+    ("h16_splits", LITE, [4096, 700]),
 ]
 
 
-@pytest.mark.parametrize("name,lens", MAT_CASES, ids=[c[0] for c in MAT_CASES])
-def test_materialised_kv_rows(gpu_lib, name, lens):
+@pytest.mark.parametrize("name,base,lens", MAT_CASES, ids=[c[0] for c in MAT_CASES])
+def test_materialised_kv_rows(gpu_lib, name, base, lens):
     """White-box check of the materialisation inside mla_prefill_naive (the
     workspace contents are not part of the ABI; the layout read here is the
     kernel's [K^C | V^C], each [b][h][row][128] bf16 with max_pages * 64 rows).
@@ -170,7 +173,7 @@ def test_materialised_kv_rows(gpu_lib, name, lens):
     import torch
     from oracle import gather_rows, to_f64
     from synth import bf16_bits_to_f32, f32_to_bf16_bits
-    cfg = small(V2, "pfmat_" + name, len(lens), permute_pages=True)
+    cfg = small(base, "pfmat_" + name, len(lens), permute_pages=True)
     T = min(lens)
     wl = generate(cfg, lens=np.array(lens, np.int32))
     say(f"[prefill materialise rows {name}] lens {lens}")
@@ -189,7 +192,7 @@ def test_materialised_kv_rows(gpu_lib, name, lens):
     torch.cuda.synchronize()
     got = ws.cpu().numpy().view(np.uint16).reshape(2, B, H, max_rows, 128)
     w = {"k": to_f64(wl.w_uk, True), "v": to_f64(wl.w_uv, True)}
-    hc = 16  # heads per reference block (bounds the float64 temporaries)
+    hc = min(16, H)  # heads per reference block (bounds the float64 temporaries)
     for b, L in enumerate(lens):
         c = to_f64(gather_rows(wl.cache, wl.block_table[b], L, 64), True)[:, :512]
         end = 32 * ((L + 31) // 32)
