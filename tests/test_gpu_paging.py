@@ -16,7 +16,7 @@ V2 = CONFIGS["v2_b64_l8192"]
 LENS = np.array([1, 63, 64, 65, 1000, 3333], np.int32)
 
 
-@pytest.mark.parametrize("heads", [128, 16])
+@pytest.mark.parametrize("heads", [128, 16, 64, 48])
 def test_permuted_pages_bit_identical(mla, heads):
     base = small(V2, "pg", len(LENS), n_heads=heads)
     contiguous = generate(small(base, "pg", len(LENS), permute_pages=False), lens=LENS)
@@ -29,7 +29,7 @@ def test_permuted_pages_bit_identical(mla, heads):
         assert np.array_equal(a[k], b[k]), k
 
 
-@pytest.mark.parametrize("heads", [128, 16])
+@pytest.mark.parametrize("heads", [128, 16, 64, 48])
 def test_poisoned_empty_slots(mla, heads):
     cfg = small(V2, "poison", len(LENS), n_heads=heads, permute_pages=True)
     clean = generate(cfg, lens=LENS)
@@ -65,7 +65,7 @@ def test_plan_changes_only_rounding(mla):
     assert_lse(many["lse"], one["lse"], "lse many vs one", 1e-3)
 
 
-@pytest.mark.parametrize("heads", [128, 16])
+@pytest.mark.parametrize("heads", [128, 16, 64, 48])
 def test_ordered_dispatch_bit_identical(mla, heads):
     """Dispatching the items longest first (or in any other order) changes
     only when each item runs: partials and outputs are bit-identical to the
