@@ -114,5 +114,33 @@ __device__ __forceinline__ void block_to_item(int blk, int num_items, int per, i
   }
 }
 
+// The work item of dispatch slot `slot`: with a dispatch order the record of
+// item `slot` is read together with order[slot] (longest-first orders are
+// mostly the identity), and only a slot that holds another item reads that
+// item's record after the order arrives.  On return `slot` is the item.
+__device__ __forceinline__ void load_item(const int32_t* items, const int32_t* order, int& slot,
+                                          int& b, int& p0, int& p1) {
+  b = items[4 * slot];
+  p0 = items[4 * slot + 2];
+  p1 = items[4 * slot + 3];
+  if (order) {
+    const int o = order[slot];
+    if (o != slot) {
+      slot = o;
+      b = items[4 * o];
+      p0 = items[4 * o + 2];
+      p1 = items[4 * o + 3];
+    }
+  }
+}
+
+// Table entry of the item's first page, read as soon as the item is known:
+// an ordered (relaxed) load stays where it is written, so it is in flight
+// together with the sequence length instead of after the checks that need
+// the length.
+__device__ __forceinline__ int first_page(const int32_t* bt, int p0) {
+  return __hip_atomic_load(bt + p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 }  // namespace dec
 }  // namespace mla

@@ -147,10 +147,10 @@ static_assert(kStages * kSlotBytes + 2 * kPBytesWG + 256 + kSWaves * 4 + 4 * kHe
               "LDS budget");
 
 __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
-    const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
-    const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ items, int num_items, const int32_t* __restrict__ order, int q_len, int H,
-    float scale, float move_t, float safe_jump,
+    const int32_t* __restrict__ items, const int32_t* __restrict__ order, int num_items, int q_len,
+    int H, int max_pages, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ block_table, const char* __restrict__ cache,
+    const uint16_t* __restrict__ q_abs, float scale, float move_t, float safe_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
   // workgroups per item and query token, 64 heads each (the last one fewer
@@ -178,17 +178,16 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
   // group r % G.
   int it, part;
   block_to_item(blockIdx.x, num_items, G * q_len, it, part);
-  if (order) it = order[it];  // dispatch slot -> item
   const int hh = part % G, tq = part / G;
-  const int b = items[4 * it];
-  const int p0 = items[4 * it + 2];
-  const int p1 = items[4 * it + 3];
+  int b, p0, p1;
+  load_item(items, order, it, b, p0, p1);  // dispatch slot -> item
+  const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
+  const int page0 = first_page(bt, p0);  // slices 0 and 1 lie in page p0
   const int L = seq_lens[b];
   const int t_begin = p0 * kPage;
   // query token tq sits at position L - q_len + tq and sees tokens up to it
   const int t_end = min(p1 * kPage, L - q_len + tq + 1);
   const int n_slices = (t_end - t_begin + kSliceTok - 1) / kSliceTok;
-  const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
   const int head0 = kHeadsWG * hh;
   // heads of this group: 64, or fewer in the last group when H is not a
   // multiple of 64 (a multiple of 16); the other head blocks run on zero
@@ -427,7 +426,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
         static_cast<uint32_t>(drow * kRowBytes + ((lane & 7) ^ swz(lane >> 3)) * 16);
     auto issue = [&](int n) {
       const int tok0 = t_begin + n * kSliceTok;
-      const int page = bt[tok0 >> 6];
+      const int page = n < 2 ? page0 : bt[tok0 >> 6];
       const char* src = cache + static_cast<int64_t>(page) * (kPage * kRowBytes) +
                         (tok0 & (kPage - 1)) * kRowBytes;
       const uint32_t dst = lds_base + (n % kStages) * kSlotBytes + kLoadsPerWave * u * 1024;
@@ -651,10 +650,10 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
 // item's Q rows arrive through the fourth slot before the first slices.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
-    const uint16_t* __restrict__ q_abs, const char* __restrict__ cache,
-    const int32_t* __restrict__ block_table, int max_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ items, int num_items, const int32_t* __restrict__ order, int q_len, int H,
-    float scale, float move_t, float safe_jump,
+    const int32_t* __restrict__ items, const int32_t* __restrict__ order, int num_items, int q_len,
+    int H, int max_pages, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ block_table, const char* __restrict__ cache,
+    const uint16_t* __restrict__ q_abs, float scale, float move_t, float safe_jump,
     float* __restrict__ o_part, float* __restrict__ lse_part, const int32_t* __restrict__ split_offsets,
     int32_t* __restrict__ tickets, float* __restrict__ o_latent, float* __restrict__ lse_out) {
   const int G = H / 16;  // workgroups per item and query token (the launch uses this kernel at 16 heads: one)
@@ -672,15 +671,14 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
   int it, part;
   block_to_item(blockIdx.x, num_items, G * q_len, it, part);
   const int head0 = 16 * (part % G), tq = part / G;
-  if (order) it = order[it];  // dispatch slot -> item
-  const int b = items[4 * it];
-  const int p0 = items[4 * it + 2];
-  const int p1 = items[4 * it + 3];
+  int b, p0, p1;
+  load_item(items, order, it, b, p0, p1);  // dispatch slot -> item
+  const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
+  const int page0 = first_page(bt, p0);  // slices 0 and 1 lie in page p0
   const int L = seq_lens[b];
   const int t_begin = p0 * kPage;
   const int t_end = min(p1 * kPage, L - q_len + tq + 1);
   const int n_slices = (t_end - t_begin + kSliceTok - 1) / kSliceTok;
-  const int32_t* bt = block_table + static_cast<int64_t>(b) * max_pages;
   const int64_t qrow0 = (static_cast<int64_t>(b) * q_len + tq) * H + head0;  // q_abs row of the first head
   const int64_t prow0 = (static_cast<int64_t>(it) * q_len + tq) * H + head0;  // its partial row
   if (n_slices <= 0) {  // empty partial, as in the 64-head kernel
@@ -706,7 +704,7 @@ __global__ __launch_bounds__(256, 1) void decode_h16_kernel(
       static_cast<uint32_t>(drow * kRowBytes + ((lane & 7) ^ swz(lane >> 3)) * 16);
   auto issue = [&](int n) {
     const int tok0 = t_begin + n * kSliceTok;
-    const int page = bt[tok0 >> 6];
+    const int page = n < 2 ? page0 : bt[tok0 >> 6];
     const char* src = cache + static_cast<int64_t>(page) * (kPage * kRowBytes) +
                       (tok0 & (kPage - 1)) * kRowBytes;
     const uint32_t dst = lds_base + (n % kStages) * kSlotBytes + kLoadsPerWave * w * 1024;
@@ -986,15 +984,15 @@ hipError_t decode_fast(const mla_dims& d, int q_len, const void* q_abs, const vo
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   if (wide) {
     hipLaunchKernelGGL(decode_h128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(1024), 0, stream,
-                       static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
-                       block_table, max_pages, seq_lens, items, num_items, order, q_len, d.n_heads,
+                       items, order, num_items, q_len, d.n_heads, max_pages, seq_lens, block_table,
+                       static_cast<const char*>(kv_cache), static_cast<const uint16_t*>(q_abs),
                        d.softmax_scale, move_threshold(), safe_jump(), o_part, lse_part, split_offsets,
                        tickets, o_latent, lse_out);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(decode_h16_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(q_abs), static_cast<const char*>(kv_cache),
-                     block_table, max_pages, seq_lens, items, num_items, order, q_len, d.n_heads,
+                     items, order, num_items, q_len, d.n_heads, max_pages, seq_lens, block_table,
+                     static_cast<const char*>(kv_cache), static_cast<const uint16_t*>(q_abs),
                      d.softmax_scale, move_threshold(), safe_jump(), o_part, lse_part, split_offsets,
                      tickets, o_latent, lse_out);
   return hipGetLastError();
