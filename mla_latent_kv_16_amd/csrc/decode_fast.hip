@@ -90,6 +90,8 @@ constexpr float kMoveDefault = 8.0f;       // log2 units: the reference moves pa
 #define MLA_MOVE_WINDOW 8
 #endif
 constexpr int kMoveWindow = MLA_MOVE_WINDOW;
+static_assert(kMoveWindow >= 2 && (kMoveWindow & (kMoveWindow - 1)) == 0,
+              "the loops find a window's last slice with a bit mask");
 constexpr float kSafeJumpDefault = 64.0f;  // log2 units: an item is redone past this
 
 // Pipelining depths (steps of LDS reads issued ahead of their MFMAs).
@@ -326,10 +328,14 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       __syncthreads();
       if (first) m_ref = fmaxf(mx_half[0][0][hidx], mx_half[0][1][hidx]);
       publish(0, s);
-      // slice k (k >= 1) holds nv valid tokens
-      auto step = [&](int k, int nv) {
+      // slice k (k >= 1) holds nv valid tokens; with the window work of a
+      // window's first slice (move test) and last slice (its maxima).
+      // edge_c: 1 for a window's first slice, 2 for its last, 0 to test k.
+      auto step = [&](int k, int nv, auto edge_c) {
+        constexpr int edge = decltype(edge_c)::value;
         __syncthreads();
-        const bool check = first && k % kMoveWindow == 0;
+        const bool check = first && (edge == 1 || (edge == 0 && k % kMoveWindow == 0));
+        const bool wend = edge == 2 || (edge == 0 && k % kMoveWindow == kMoveWindow - 1);
         float mp0 = -INFINITY, mp1 = -INFINITY;
         if (check) {  // the previous window's maxima, read before the MFMAs
           const int v = k / kMoveWindow - 1;
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
         if (first) {
           if (check) move_ref(k, fmaxf(mp0, mp1));
           m_win = fmaxf(m_win, lane_max(s));
-          if (k % kMoveWindow == kMoveWindow - 1) {  // window k / kMoveWindow ends
+          if (wend) {  // window k / kMoveWindow ends
             // m_ref is constant within a window: its weights' largest exponent
             e_lane = fmaxf(e_lane, m_win - m_ref);
             const float mh = rows_max(m_win);  // every lane takes part in the row permutes
@@ -350,10 +356,28 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
         }
         publish(k, s);
       };
+      // a whole slice that is neither the first nor the last of its window
+      // (no window work: its branches cost the critical path on every slice)
+      auto step_inner = [&](int k) {
+        __syncthreads();
+        scores(slot_of(k), kSliceTok, s);
+        if (first) m_win = fmaxf(m_win, lane_max(s));
+        publish(k, s);
+      };
       // slices 1 .. n-2 are whole (the constant count lets the compiler drop
-      // the mask); only the first and the last can be short
-      for (int k = 1; k < n_slices - 1; ++k) step(k, kSliceTok);
-      if (n_slices > 1) step(n_slices - 1, nvalid(n_slices - 1));
+      // the mask); only the first and the last can be short.  Per window: its
+      // first slice, the inner slices, its last slice (window 0 starts at 1).
+      using First = std::integral_constant<int, 1>;
+      using Last = std::integral_constant<int, 2>;
+      int k = 1;
+      for (const int e = min(n_slices - 1, kMoveWindow - 1); k < e; ++k) step_inner(k);
+      if (k < n_slices - 1) step(k++, kSliceTok, Last{});
+      while (k < n_slices - 1) {  // k starts a window
+        step(k++, kSliceTok, First{});
+        for (const int e = min(n_slices - 1, k | (kMoveWindow - 1)); k < e; ++k) step_inner(k);
+        if (k < n_slices - 1) step(k++, kSliceTok, Last{});
+      }
+      if (n_slices > 1) step(n_slices - 1, nvalid(n_slices - 1), std::integral_constant<int, 0>{});
       e_lane = fmaxf(e_lane, m_win - m_ref);  // a last, partial window
       __syncthreads();
       // vote: did a weight of any S wave pass 2^safe_jump?
@@ -479,13 +503,16 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     };
     // O^T[64 columns x 64 heads] += C^T . P^T for slice k; with `moves`, first
     // the rescale of the head blocks whose reference moved at slice k
-    auto accumulate = [&](int k, bool moves) {
+    // (may_move_c: std::true_type for a slice that can start a window, else
+    // std::false_type, which leaves out the move test altogether)
+    auto accumulate = [&](int k, bool moves, auto may_move_c) {
+      constexpr bool may_move = decltype(may_move_c)::value;
       const char* slot = slot_of(k);
       const char* pb = pbuf_of(k);
       // the slice indices of the last moves first (at window starts), then
       // every operand read of the slice; the scheduling barrier keeps that
       // order, so the move test waits only for its own read
-      moves = moves && k > 0 && k % kMoveWindow == 0;  // moves happen at window starts only
+      moves = may_move && moves && k > 0 && k % kMoveWindow == 0;  // moves happen at window starts only
       int4 mv = {-1, -1, -1, -1};
       if (moves) mv = *reinterpret_cast<const int4*>(&moved[(k / kMoveWindow) & 1][0]);
       bf16x8 pf[kHeadBlocksWG];
@@ -498,7 +525,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
         f0[c] = lds_read_tr(slot, pv_off(4 * u + c));
         f1[c] = lds_read_tr(slot, pv_off(4 * u + c) + kRowGroup2);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      if (may_move) __builtin_amdgcn_sched_barrier(0);
       if (moves) {
         const int hit = (__builtin_amdgcn_readfirstlane(mv.x) == k ? 1 : 0) |
                         (__builtin_amdgcn_readfirstlane(mv.y) == k ? 2 : 0) |
@@ -537,12 +564,19 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       if (dma && 2 < n_slices) issue(2);
       __syncthreads();  // the S waves' first-slice maximum exchange
       for (int n = 2; n <= MLA_PREFETCH_D; ++n) prefetch(n);
-      for (int k = 1; k <= n_slices; ++k) {
+      // iteration k adds slice k - 1; only a slice that starts a window
+      // (k - 1 a multiple of kMoveWindow) carries the move test
+      auto vstep = [&](int k, auto may_move_c) {
         if (dma && k < n_slices) wait_slice(k);
         __syncthreads();
         if (dma && k + 2 < n_slices) issue(k + 2);
         prefetch(k + MLA_PREFETCH_D);
-        accumulate(k - 1, first);
+        accumulate(k - 1, first, may_move_c);
+      };
+      for (int k = 1; k <= n_slices;) {
+        vstep(k++, std::true_type{});
+        const int next = (k - 1 + kMoveWindow - 1) / kMoveWindow * kMoveWindow + 1;  // next window start
+        for (const int e = min(n_slices + 1, next); k < e; ++k) vstep(k, std::false_type{});
       }
       // vote (written by the S waves)
       __syncthreads();
