@@ -505,9 +505,24 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     // the rescale of the head blocks whose reference moved at slice k
     // (may_move_c: std::true_type for a slice that can start a window, else
     // std::false_type, which leaves out the move test altogether)
-    auto accumulate = [&](int k, bool moves, auto may_move_c) {
-      constexpr bool may_move = decltype(may_move_c)::value;
+    // C^T fragments of the slice to accumulate next, read at the end of the
+    // iteration before (slice k is in the LDS from barrier k on, and its slot
+    // is refilled two iterations later), so that after a barrier the V waves
+    // read only the weights before their MFMAs
+    bf16x4 fc0[4], fc1[4];
+    auto read_ct = [&](int k) {
       const char* slot = slot_of(k);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        fc0[c] = lds_read_tr(slot, pv_off(4 * u + c));
+        fc1[c] = lds_read_tr(slot, pv_off(4 * u + c) + kRowGroup2);
+      }
+    };
+    // slice k with the C^T fragments in fc0/fc1; then the next slice's
+    // fragments when `next` (in flight across the barrier, used next
+    // iteration)
+    auto accumulate = [&](int k, bool moves, auto may_move_c, bool next) {
+      constexpr bool may_move = decltype(may_move_c)::value;
       const char* pb = pbuf_of(k);
       // the slice indices of the last moves first (at window starts), then
       // every operand read of the slice; the scheduling barrier keeps that
@@ -519,12 +534,6 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
 #pragma unroll
       for (int hb = 0; hb < kHeadBlocksWG; ++hb)
         pf[hb] = *reinterpret_cast<const bf16x8*>(pb + (hb * 64 + lane) * 16);
-      bf16x4 f0[4], f1[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        f0[c] = lds_read_tr(slot, pv_off(4 * u + c));
-        f1[c] = lds_read_tr(slot, pv_off(4 * u + c) + kRowGroup2);
-      }
       if (may_move) __builtin_amdgcn_sched_barrier(0);
       if (moves) {
         const int hit = (__builtin_amdgcn_readfirstlane(mv.x) == k ? 1 : 0) |
@@ -548,11 +557,12 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 a = __builtin_shufflevector(f0[c], f1[c], 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 a = __builtin_shufflevector(fc0[c], fc1[c], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int hb = 0; hb < kHeadBlocksWG; ++hb)
           oacc[c][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[hb], oacc[c][hb], 0, 0, 0);
       }
+      if (next) read_ct(k + 1);
     };
     auto full_pass = [&](bool first) -> bool {
       if (dma) {
@@ -562,6 +572,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       }
       __syncthreads();
       if (dma && 2 < n_slices) issue(2);
+      read_ct(0);
       __syncthreads();  // the S waves' first-slice maximum exchange
       for (int n = 2; n <= MLA_PREFETCH_D; ++n) prefetch(n);
       // iteration k adds slice k - 1; only a slice that starts a window
@@ -571,7 +582,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
         __syncthreads();
         if (dma && k + 2 < n_slices) issue(k + 2);
         prefetch(k + MLA_PREFETCH_D);
-        accumulate(k - 1, first, may_move_c);
+        accumulate(k - 1, first, may_move_c, k < n_slices);
       };
       for (int k = 1; k <= n_slices;) {
         vstep(k++, std::true_type{});
