@@ -1,6 +1,7 @@
-// Device helpers shared by the gfx950 decode kernels (decode_fast.hip and
-// decode_wide.hip): the cache-row slot layout in LDS, the DMA and L2-touch
-// loads, the LDS operand reads and the cross-lane reductions.
+// Device helpers shared by the gfx950 decode kernels (decode_fast.hip), and
+// in part by the dense and prefill kernels: the cache-row slot layout in LDS,
+// the DMA and L2-touch loads, the LDS operand reads and the cross-lane
+// reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>

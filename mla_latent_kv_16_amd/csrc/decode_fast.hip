@@ -143,6 +143,10 @@ constexpr int kHeadsWG = 64;
 constexpr int kHeadBlocksWG = kHeadsWG / 16;        // 4
 constexpr int kPBytesWG = kHeadBlocksWG * 64 * 16;  // 4 KiB of weights per slice
 constexpr int kSWaves = 8;
+// LDS offset of the staged queries (18 steps x 4 head blocks x 1 KiB, ring
+// slots 2 and 3)
+constexpr uint32_t kQStageOff = 2 * kSlotBytes;
+static_assert(18 * kHeadBlocksWG * 1024 == 2 * kSlotBytes, "the queries fill two ring slots");
 static_assert(kStages * kSlotBytes + 2 * kPBytesWG + 256 + kSWaves * 4 + 4 * kHeadsWG * 4 +
                       2 * kHeadsWG * 4 + 2 * 4 * 4 + 2 * kHeadsWG * 4 + 4 <=
                   163840,
@@ -231,10 +235,26 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
     __builtin_amdgcn_s_setprio(MLA_S_PRIO);
     const int hb = w & 3, th = w >> 2;
     bf16x8 qf[18];  // B operand: head head0 + 16hb + q, values 32ks + 8g .. +8
+    // The queries reach the CU once, by DMA into ring slots 2 and 3 (free
+    // until slice 2 is issued), instead of once per token half: 1 KiB block
+    // (ks, hb) holds at lane position 16g + q the operand of lane 16g + q.
+    // Token half th fetches steps 9th .. 9th + 8 of its head block; after the
+    // barrier both halves read all 18.
+    const uint32_t q_lds = kQStageOff + 1024 * hb;
     if (16 * hb < nh) {
-      const uint16_t* qrow = q_abs + (qrow0 + head0 + 16 * hb + q) * kDq + 8 * g;
+      const char* qsrc = reinterpret_cast<const char*>(q_abs + (qrow0 + head0 + 16 * hb) * kDq);
+      const uint32_t qoff = static_cast<uint32_t>(q * kRowBytes + 16 * g);
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+      for (int j = 0; j < 9; ++j) {
+        const int ks = 9 * th + j;
+        dma16(qsrc + 64 * ks, qoff, lds_base + q_lds + 4096 * ks);
+      }
+      __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
+    }
+    __syncthreads();  // every query block is in the LDS
+    if (16 * hb < nh) {
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) qf[ks] = lds_read128(lds, q_lds + 4096 * ks + 16 * lane);
     } else {
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) qf[ks] = bf16x8{};
@@ -564,10 +584,13 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       }
       if (next) read_ct(k + 1);
     };
-    auto full_pass = [&](bool first) -> bool {
+    // `issued`: slices 0 and 1 are already in flight
+    auto full_pass = [&](bool first, bool issued) -> bool {
       if (dma) {
-        issue(0);
-        if (n_slices > 1) issue(1);
+        if (!issued) {
+          issue(0);
+          if (n_slices > 1) issue(1);
+        }
         wait_slice(0);
       }
       __syncthreads();
@@ -598,8 +621,14 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       return any == 0;
     };
 
+    // the first slices go out beside the S waves' query DMA
+    if (dma) {
+      issue(0);
+      if (n_slices > 1) issue(1);
+    }
+    __syncthreads();  // the queries are in the LDS (the S waves' first barrier)
     zero_acc();
-    if (!full_pass(true)) {
+    if (!full_pass(true, true)) {
       // exact-maximum pass of the S waves: stream the slices again
       if (dma) {
         issue(0);
@@ -613,7 +642,7 @@ __global__ __launch_bounds__(1024, 1) void decode_h128_kernel(
       __syncthreads();
       __syncthreads();  // the S waves' maximum exchange
       zero_acc();
-      full_pass(false);
+      full_pass(false, false);
     }
     // epilogue: normalise by the row sums of the S waves and write the partial
     // (or, for a sequence with one item in merged mode, o~ itself)
