@@ -171,8 +171,10 @@ def measured_traffic(workload: str):
     return float(m.group(1))
 
 
-def cpu_baseline(wl, budget_s: float = 20.0):
-    """The fp64 oracle, untuned, on a bounded sample of the same workload."""
+def cpu_baseline(wl, budget_s: float = 20.0, gpu_out=None):
+    """The fp64 oracle, untuned, on a bounded sample of the same workload.
+    With `gpu_out` ([B, H, d_h], the timed step's output on these inputs) the
+    sampled sequences' outputs are also compared with the oracle's."""
     from oracle import decode_workload
     cfg = wl.cfg
     affinity = len(os.sched_getaffinity(0))
@@ -183,21 +185,33 @@ def cpu_baseline(wl, budget_s: float = 20.0):
         threads = affinity
     order = list(range(cfg.batch))
     done, flop, t_total = [], 0, 0.0
+    ref = []
     for b in order:
         t0 = time.perf_counter()
-        decode_workload(wl, seqs=[b])
+        r = decode_workload(wl, seqs=[b])
         t_total += time.perf_counter() - t0
+        ref.append(r["o"][0])
         done.append(b)
         flop += int(wl.seq_lens[b]) * cfg.n_heads * 2 * (cfg.d_latent + cfg.d_rope + cfg.d_latent)
         if t_total >= budget_s * 0.5 or len(done) == cfg.batch:
             break
     toks = int(sum(int(wl.seq_lens[b]) for b in done))
-    return {"value": flop / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "affinity_cores": int(affinity), "blas_threads": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(done)} of {cfg.batch} sequences ({toks} cached tokens, all "
-                      f"{cfg.n_heads} heads), naive fp64 path, {t_total:.1f} s wall",
-            "seq_per_s": len(done) / t_total}
+    res = {"value": flop / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+           "affinity_cores": int(affinity), "blas_threads": int(threads),
+           "kind": "oracle",
+           "sample": f"{len(done)} of {cfg.batch} sequences ({toks} cached tokens, all "
+                     f"{cfg.n_heads} heads), naive fp64 path, {t_total:.1f} s wall",
+           "seq_per_s": len(done) / t_total}
+    if gpu_out is not None:
+        # the timed step's output against the oracle on the same sequences
+        got = np.asarray(gpu_out[done], np.float64)
+        want = np.stack(ref)
+        res["oracle_check"] = {
+            "sequences": len(done),
+            "out_rel_l2": float(np.linalg.norm(got - want) / np.linalg.norm(want)),
+            "out_max_abs_ratio": float(np.abs(got - want).max() / np.abs(want).max()),
+            "tolerance": {"rel_l2": 5e-3, "max_abs_ratio": 2e-2}}
+    return res
 
 
 def time_prefill(args, cfg, wl, dims, L0, block_table, seq_lens, stream, new_events, evict, slots):
@@ -660,6 +674,12 @@ def main():
         "step_mfma_frac": round(work["step_flop"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "step_algorithmic_bytes": work["step_bytes"],
     }
+    # the step's output on the workload's own inputs (layer 0, before the cache
+    # write below changes a slot), for the check against the oracle
+    gpu_out = None
+    if T == 1 and not args.score_jump and n_layers == 1 and not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        gpu_out = bufs["out"].view(B, H, cfg.d_head).float().cpu().numpy()
     # The cache write of the next token of every sequence (mla_append_kv), timed
     # on its own (per-launch events): it precedes the step in a model and is not
     # part of `value`.
@@ -707,7 +727,7 @@ def main():
         log("[bench] copy probe: 1 GiB device-to-device copy done")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        result["cpu_baseline"] = cpu_baseline(wl)
+        result["cpu_baseline"] = cpu_baseline(wl, gpu_out=gpu_out)
     print(json.dumps(result), flush=True)
 
 
