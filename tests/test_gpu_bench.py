@@ -37,3 +37,22 @@ def test_bench_json_line(gpu_lib):
     rf = b["roofline"]
     assert rf["bound"] == "hbm" and rf["peak"] == 8000.0 and rf["unit"] == "GB/s"
     assert 0 < rf["frac"] < 1 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+
+
+def test_bench_oracle_check(gpu_lib):
+    """With the CPU baseline on, the bench compares the timed step's output
+    with the float64 oracle on the sequences the baseline samples."""
+    from gpu_util import MAX_ABS, REL_L2, say
+    say("[bench.py oracle check]")
+    cmd = [sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "v2lite_b32_l4096", "--steps", "2",
+           "--warmup", "1", "--settle-ms", "10"]
+    r = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, r.stderr[-2000:]
+    b = json.loads([ln for ln in r.stdout.splitlines() if ln.strip()][-1])
+    cb = b["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0
+    oc = cb["oracle_check"]
+    say(f"  {oc['sequences']} sequences: out rel L2 {oc['out_rel_l2']:.3e}, "
+        f"max-abs ratio {oc['out_max_abs_ratio']:.3e}")
+    assert oc["sequences"] >= 1
+    assert oc["out_rel_l2"] <= REL_L2 and oc["out_max_abs_ratio"] <= MAX_ABS
