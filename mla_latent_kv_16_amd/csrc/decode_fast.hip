@@ -24,6 +24,9 @@
 //    the slice MLA_PREFETCH_D ahead (the even lines in one workgroup of the
 //    pair, the odd ones in the other), with a load whose data lands in a junk
 //    LDS line; by the time that slice's DMA is issued its rows are in the L2.
+//  * Queries (128-head kernel): fetched once per workgroup by DMA into the two
+//    ring slots that slices 2 and 3 later fill, then read into registers by
+//    both S waves of a head block, so each CU takes them in once.
 //  * QK^T operands: a lane reads 16 contiguous bytes (8 latent values of one
 //    token) with ds_read_b128.
 //  * PV operands: C^T needs 8 tokens of one latent column per lane; two
